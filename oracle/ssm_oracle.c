@@ -1,0 +1,262 @@
+/*
+ * ssm_oracle.c -- plain fp64 CPU reference for the selective state-space (S6)
+ * scan and its single-token decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The HIP library never
+ * includes, links or calls it, and the two share no code.
+ *
+ * Sources (cited by page title and section):
+ *   [MAMBA]  "Mamba: Linear-Time Sequence Modeling with Selective State
+ *            Spaces" (reading guide to arXiv 2312.00752, xyznot.com):
+ *            - "Method": the continuous SSM h'(t) = A h(t) + B x(t),
+ *              y(t) = C h(t); zero-order-hold discretization with step Delta
+ *              (A-bar = exp(Delta A)); the discrete recurrence
+ *              h_t = A-bar h_{t-1} + B-bar x_t with readout y_t = C h_t taken
+ *              from the state after the step-t update.
+ *            - "The selection mechanism (S6)": Delta, B and C are functions of
+ *              the token at step t; Delta = softplus(parameter + s_Delta(x_t)).
+ *              The exact ZOH form of B-bar is given in "Method" and is kept
+ *              here as an option (zoh != 0).
+ *            - Q&A on generation: decoding keeps one fixed D x N state per
+ *              layer and updates it once per token.
+ *   [CN]     "Mamba选择性状态空间机制：效率提升10倍的核心突破" (soft186.com),
+ *            dynamic-parameterization section: the simplified update adds
+ *            x * dB to the decayed state, with dB = Delta * B.  This is the
+ *            default B-bar here (zoh == 0).
+ *
+ * Readings of points the pages leave open:
+ *   - A is real and diagonal per channel, stored A[d][n]; exp is elementwise.
+ *   - The initial state is h0 when given, else zero.
+ *   - Delta_t drives A-bar_t of its own step.
+ *   - softplus is the exact ln(1 + e^u), evaluated as max(u,0) + log1p(e^-|u|).
+ *   - Skip and gate: y = (C.h + Dskip*x) * silu(z), silu(z) = z / (1 + e^-z);
+ *     a NULL z means no gate, a NULL Dskip or dt_bias means zero.
+ *   - Layouts (row-major, last index fastest): x, dt, z, y [batch][dim][L];
+ *     Bm, Cm [batch][N][L]; A [dim][N]; Dskip, dt_bias [dim];
+ *     h0, hL, state [batch][dim][N]; decode x, dt, z, y [batch][dim];
+ *     decode Bm, Cm [batch][N].
+ *
+ * Build with plain -O2 and no fast-math.  ORACLE_MUTANT=k (k > 0) compiles a
+ * deliberately wrong variant; the test suite uses those to show that each
+ * planted mistake fails at least one pin.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+#include <stdlib.h>
+
+#ifndef ORACLE_MUTANT
+#define ORACLE_MUTANT 0
+#endif
+
+/* [MAMBA] S6 section: Delta = softplus(.), written without cancellation. */
+static double softplus(double u)
+{
+#if ORACLE_MUTANT == 12
+    return log1p(exp(-fabs(u))); /* planted: drops the max(u, 0) branch */
+#else
+    return fmax(u, 0.0) + log1p(exp(-fabs(u)));
+#endif
+}
+
+/* Gate multiplier silu(z) = z * sigmoid(z). */
+static double silu(double z)
+{
+#if ORACLE_MUTANT == 3
+    return 1.0 / (1.0 + exp(-z)); /* planted: sigmoid instead of silu */
+#else
+    return z / (1.0 + exp(-z));
+#endif
+}
+
+typedef struct {
+    int batch, dim, seqlen, dstate, zoh;
+    const double *x, *dt, *dt_bias, *A, *Bm, *Cm, *Dskip, *z, *h0;
+    double *y, *hL;
+} scan_args;
+
+/*
+ * One (b, d) row, strictly sequential in t.  h has dstate entries.
+ * [MAMBA] Method: A-bar = exp(Delta A); h_t = A-bar h_{t-1} + B-bar x_t;
+ * y_t = C_t h_t read after the update.
+ */
+static void scan_row(const scan_args *a, int b, int d, double *h)
+{
+    const int L = a->seqlen, N = a->dstate;
+    const size_t row = ((size_t)b * a->dim + d) * (size_t)L;
+    const double *x = a->x + row, *dt = a->dt + row;
+    const double *z = a->z ? a->z + row : NULL;
+    const double *Bm = a->Bm + (size_t)b * N * L;
+    const double *Cm = a->Cm + (size_t)b * N * L;
+    const double *Arow = a->A + (size_t)d * N;
+    double bias = a->dt_bias ? a->dt_bias[d] : 0.0;
+    double skip = a->Dskip ? a->Dskip[d] : 0.0;
+#if ORACLE_MUTANT == 6
+    bias = 0.0; /* planted: dt_bias ignored */
+#endif
+#if ORACLE_MUTANT == 2
+    skip = 0.0; /* planted: skip term dropped */
+#endif
+
+    for (int n = 0; n < N; ++n) {
+        double init = a->h0 ? a->h0[((size_t)b * a->dim + d) * N + n] : 0.0;
+#if ORACLE_MUTANT == 9
+        init = 0.0; /* planted: initial state ignored */
+#endif
+        h[n] = init;
+    }
+
+    for (int t = 0; t < L; ++t) {
+        double dtv = dt[t];
+#if ORACLE_MUTANT == 7
+        /* planted: Delta taken from the neighbouring channel's dt row */
+        dtv = a->dt[((size_t)b * a->dim + (d + 1) % a->dim) * (size_t)L + t];
+#endif
+        const double delta = softplus(dtv + bias);
+#if ORACLE_MUTANT == 1
+        double readout_prev = 0.0;
+        for (int n = 0; n < N; ++n) {
+            readout_prev += Cm[(size_t)n * L + t] * h[n];
+        }
+#endif
+        double s = 0.0;
+        for (int n = 0; n < N; ++n) {
+            double an = Arow[n];
+#if ORACLE_MUTANT == 11
+            an = a->A[(size_t)n * a->dim + d]; /* planted: A read as [N][dim] */
+#endif
+#if ORACLE_MUTANT == 4
+            const double abar = exp(-delta * an); /* planted: sign error */
+#else
+            const double abar = exp(delta * an);
+#endif
+            double bn = Bm[(size_t)n * L + t];
+            double cn = Cm[(size_t)n * L + t];
+#if ORACLE_MUTANT == 5
+            bn = Bm[(size_t)t * N + n]; /* planted: B read as [L][N] */
+#endif
+#if ORACLE_MUTANT == 8
+            { double tmp = bn; bn = cn; cn = tmp; } /* planted: B and C swapped */
+#endif
+            double bbar;
+            if (a->zoh) {
+                /* [MAMBA] Method: B-bar = (Delta A)^-1 (exp(Delta A) - I) Delta B,
+                 * i.e. expm1(Delta A) / A * B for diagonal A, -> Delta B at A = 0. */
+                bbar = (an != 0.0) ? expm1(delta * an) / an * bn : delta * bn;
+#if ORACLE_MUTANT == 13
+                bbar = expm1(delta * an) * bn; /* planted: missing 1/A */
+#endif
+            } else {
+                /* [CN] dynamic parameterization: dB = Delta * B. */
+                bbar = delta * bn;
+#if ORACLE_MUTANT == 10
+                bbar = bn; /* planted: Delta factor dropped */
+#endif
+            }
+            h[n] = abar * h[n] + bbar * x[t];
+            s += cn * h[n];
+        }
+#if ORACLE_MUTANT == 1
+        s = readout_prev; /* planted: readout from the state before the update */
+#endif
+        s += skip * x[t];
+        a->y[row + t] = z ? s * silu(z[t]) : s;
+    }
+    if (a->hL) {
+        for (int n = 0; n < N; ++n) {
+#if ORACLE_MUTANT == 14
+            if (n == N - 1) continue; /* planted: last state entry not returned */
+#endif
+            a->hL[((size_t)b * a->dim + d) * N + n] = h[n];
+        }
+    }
+}
+
+typedef struct {
+    const scan_args *a;
+    long first, last; /* row range [first, last) over batch * dim */
+    int ok;
+} worker;
+
+static void *run_rows(void *p)
+{
+    worker *w = (worker *)p;
+    double *h = (double *)malloc(sizeof(double) * (size_t)w->a->dstate);
+    if (!h) { w->ok = 0; return NULL; }
+    for (long r = w->first; r < w->last; ++r) {
+        scan_row(w->a, (int)(r / w->a->dim), (int)(r % w->a->dim), h);
+    }
+    free(h);
+    w->ok = 1;
+    return NULL;
+}
+
+static int run_threaded(const scan_args *a, int nthreads)
+{
+    const long rows = (long)a->batch * a->dim;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > rows) nthreads = (int)rows;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t tid[256];
+    int created[256];
+    worker w[256];
+    int ok = 1;
+    for (int i = 0; i < nthreads; ++i) {
+        w[i].a = a;
+        w[i].first = rows * i / nthreads;
+        w[i].last = rows * (i + 1) / nthreads;
+        w[i].ok = 0;
+        created[i] = 0;
+        if (i == 0) continue;
+        if (pthread_create(&tid[i], NULL, run_rows, &w[i]) == 0) {
+            created[i] = 1;
+        } else {
+            run_rows(&w[i]); /* no thread available: run on the caller */
+        }
+    }
+    run_rows(&w[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (created[i]) pthread_join(tid[i], NULL);
+    }
+    for (int i = 0; i < nthreads; ++i) ok &= w[i].ok;
+    return ok ? 0 : -2;
+}
+
+/*
+ * Full-sequence scan.  Returns 0 on success, -1 on bad arguments, -2 if a
+ * worker could not allocate its state.  hL may be NULL; h0 may be NULL.
+ */
+int ssm_oracle_scan_f64(int batch, int dim, int seqlen, int dstate, int zoh,
+                        const double *x, const double *dt, const double *dt_bias,
+                        const double *A, const double *Bm, const double *Cm,
+                        const double *Dskip, const double *z, const double *h0,
+                        double *y, double *hL, int nthreads)
+{
+    if (batch < 1 || dim < 1 || seqlen < 1 || dstate < 1) return -1;
+    if (!x || !dt || !A || !Bm || !Cm || !y) return -1;
+    scan_args a = {batch, dim, seqlen, dstate, zoh, x, dt, dt_bias, A,
+                   Bm, Cm, Dskip, z, h0, y, hL};
+    return run_threaded(&a, nthreads);
+}
+
+/*
+ * Decode step: the scan body at L = 1, starting from `state` and writing the
+ * updated state back into it ([MAMBA] Q&A on generation).  Shapes: state
+ * [batch][dim][N]; x, dt, z, y [batch][dim]; Bm, Cm [batch][N].
+ */
+int ssm_oracle_state_update_f64(int batch, int dim, int dstate, int zoh,
+                                double *state, const double *x, const double *dt,
+                                const double *dt_bias, const double *A,
+                                const double *Bm, const double *Cm,
+                                const double *Dskip, const double *z, double *y,
+                                int nthreads)
+{
+    if (!state) return -1;
+    /* With L = 1 the [batch][dim][L] and [batch][N][L] layouts are exactly the
+     * decode layouts, so the scan applies unchanged. */
+    return ssm_oracle_scan_f64(batch, dim, 1, dstate, zoh, x, dt, dt_bias, A, Bm,
+                               Cm, Dskip, z, state, y, state, nthreads);
+}
+
+int ssm_oracle_mutant_id(void) { return ORACLE_MUTANT; }
