@@ -1,0 +1,227 @@
+"""Benchmark: fused selective-scan forward (ssm_scan_fwd) on one MI355X.
+
+One step = one ssm_scan_fwd call over the whole Mamba-2.8B-shaped layer
+(batch 4, d_inner 5120, N 16, L 2048, bf16 x/dt/z/Bm/Cm, fp32 A/Dskip/dt_bias,
+fp32 y and final state), inputs already resident in HBM.  Prints one JSON line:
+
+  value       scan elements (batch*dim*L*N) per second, whole job
+  roofline    the dominant (only) kernel against the VALU issue-rate peak it is
+              bound by; the algorithmic HBM rate is reported beside it
+  cpu_baseline the fp64 CPU oracle on the host cores, same workload
+  decode      the 256-step ssm_state_update loop of the decode workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I]
+       [--no-cpu-baseline] [--no-decode]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# ---------------------------------------------------------------- chip model
+# MI355X: 256 CUs at 2.4 GHz.  fp32 VALU: 128 lanes/clk/CU (157.3 TFLOP/s with
+# FMA = 2 flops) = 78.6 T lane-op issue slots/s.  Transcendentals (exp2, log2,
+# rcp) issue at a quarter of that rate, i.e. 4 slots each.  HBM3E: 8 TB/s.
+CUS, CLOCK_HZ = 256, 2.4e9
+PEAK_SLOTS = CUS * 128 * CLOCK_HZ          # 7.864e13 fp32 lane-op slots / s
+TRANS_SLOTS = 4
+PEAK_HBM = 8.0e12                          # B/s
+
+# Algorithmic work (the method's minimum, no scan overhead):
+#  per (b,d,l,n): Delta*A (1), exp (4), Delta*x*B (1), state fma (1), readout fma (1)
+#  per (b,d,l):   dt + bias (1), softplus = exp + add + log (9), Delta*x (1),
+#                 skip fma (1), silu = exp + add + rcp + mul (10), gate mul (1)
+SLOTS_PER_ELEM = 1 + TRANS_SLOTS + 1 + 1 + 1
+SLOTS_PER_ROW_STEP = 1 + (TRANS_SLOTS + 1 + TRANS_SLOTS) + 1 + 1 + (TRANS_SLOTS + 1 + TRANS_SLOTS + 1) + 1
+
+
+def algorithmic_slots(batch, dim, L, N):
+    return batch * dim * L * (N * SLOTS_PER_ELEM + SLOTS_PER_ROW_STEP)
+
+
+def algorithmic_bytes(batch, dim, L, N, in_bytes, out_bytes, gate=True):
+    per_row_step = (3 if gate else 2) * in_bytes + out_bytes          # x, dt, (z) in; y out
+    bc = 2 * batch * N * L * in_bytes                                 # Bm, Cm
+    params = dim * N * 4 + 2 * dim * 4                                # A, Dskip, dt_bias
+    state = batch * dim * N * 4                                       # hL out
+    return batch * dim * L * per_row_step + bc + params + state
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def to_dev(inp, name):
+    import torch
+    a = getattr(inp, name)
+    if name in inp.stored and inp.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def cpu_baseline(inp, block=512):
+    """The fp64 oracle as it stands, on all host cores, over the whole workload
+    (processed in channel blocks to bound host memory)."""
+    import oracle
+    wl = inp.wl
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    A, Dk, bias = (inp.A.astype(np.float64), inp.Dskip.astype(np.float64),
+                   inp.dt_bias.astype(np.float64))
+    Bm, Cm = inp.values("Bm"), inp.values("Cm")
+    elapsed = 0.0
+    for d0 in range(0, wl.dim, block):
+        d1 = min(wl.dim, d0 + block)
+        x = synth_vals(inp, "x", d0, d1)
+        dt = synth_vals(inp, "dt", d0, d1)
+        z = synth_vals(inp, "z", d0, d1)
+        t0 = time.perf_counter()
+        oracle.scan_fwd(x, dt, A[d0:d1], Bm, Cm, dt_bias=bias[d0:d1], Dskip=Dk[d0:d1], z=z,
+                        threads=threads)
+        elapsed += time.perf_counter() - t0
+    elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
+    return {"value": elems / elapsed, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": "whole workload (%d x %d x %d x %d), fp64 sequential recurrence, %.2f s"
+                      % (wl.batch, wl.dim, wl.seqlen, wl.dstate, elapsed)}
+
+
+def synth_vals(inp, name, d0, d1):
+    from selective_state_space_64_amd import synth
+    a = getattr(inp, name)[:, d0:d1]
+    if inp.dtype == "bf16":
+        return synth.bf16_values(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def bench_decode(torch, ssm, synth, steps_cap=256):
+    wl = synth.WORKLOADS[4]
+    inp = synth.make_inputs(wl)
+    perm = lambda t: t.permute(2, 0, 1).contiguous()
+    xs, dts, zs = perm(to_dev(inp, "x")), perm(to_dev(inp, "dt")), perm(to_dev(inp, "z"))
+    Bs, Cs = perm(to_dev(inp, "Bm")), perm(to_dev(inp, "Cm"))
+    A, Dk, bias = to_dev(inp, "A"), to_dev(inp, "Dskip"), to_dev(inp, "dt_bias")
+    state0 = torch.from_numpy(inp.h0).cuda()
+    state = state0.clone()
+    ys = torch.empty((wl.seqlen, wl.batch, wl.dim), device="cuda")
+    steps = min(steps_cap, wl.seqlen)
+
+    def loop():
+        for s in range(steps):
+            ssm.ssm_state_update(state, xs[s], dts[s], A, Bs[s], Cs[s], dt_bias=bias, Dskip=Dk,
+                                 z=zs[s], y=ys[s])
+
+    loop()
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    loop()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per_call_bytes = (2 * wl.batch * wl.dim * wl.dstate * 4 + 3 * wl.batch * wl.dim * 2
+                      + 2 * wl.batch * wl.dstate * 2 + wl.dim * wl.dstate * 4 + 2 * wl.dim * 4
+                      + wl.batch * wl.dim * 4)
+    elems = wl.batch * wl.dim * wl.dstate
+    return {"workload": wl.name, "calls": steps, "us_per_call": ms * 1e3,
+            "elements_per_s": elems / (ms * 1e-3),
+            "hbm_gbps_algorithmic": per_call_bytes / (ms * 1e-3) / 1e9,
+            "bytes_per_call": per_call_bytes,
+            "note": "one launch per token, state fp32 in place; 21 MB state can stay in the 256 MB MALL"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every box here has one GPU and the scan is "
+              "benchmarked on a single device (--gpus %d is not supported)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import selective_state_space_64_amd as ssm
+    from selective_state_space_64_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = synth.WORKLOADS[args.workload]
+    inp = synth.make_inputs(wl)
+    t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}
+    y = torch.empty((wl.batch, wl.dim, wl.seqlen), device="cuda")
+    hL = torch.empty((wl.batch, wl.dim, wl.dstate), device="cuda")
+
+    def step():
+        ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                         Dskip=t["Dskip"], z=t["z"], y=y, hL=hL)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = wall * 1e3 / args.steps
+    kern_s = float(launch_ms.mean()) * 1e-3
+    elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
+    in_bytes = 2 if wl.dtype == "bf16" else 4
+    slots = algorithmic_slots(wl.batch, wl.dim, wl.seqlen, wl.dstate)
+    nbytes = algorithmic_bytes(wl.batch, wl.dim, wl.seqlen, wl.dstate, in_bytes, 4)
+    achieved = slots / kern_s / 1e12
+    peak = PEAK_SLOTS / 1e12
+    result = {
+        "metric": "selective-scan elems/s (B·D·L·N) fwd + achieved HBM GB/s, 1 MI355X",
+        "value": elems / (ms_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "dim": wl.dim, "dstate": wl.dstate,
+                   "seqlen": wl.seqlen, "input_dtype": wl.dtype, "output_dtype": "f32",
+                   "parallelism": "single GPU"},
+        "kernel_ms": {"mean": float(launch_ms.mean()), "min": float(launch_ms.min()),
+                      "median": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "hbm_gbps_algorithmic": nbytes / kern_s / 1e9,
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
+                     "frac": achieved / peak, "traffic": None,
+                     "model": "fp32 VALU issue slots (transcendental = 4), %.4f slots/element algorithmic"
+                              % (slots / elems),
+                     "hbm": {"achieved": nbytes / kern_s / 1e9, "peak": PEAK_HBM / 1e9,
+                             "unit": "GB/s", "frac": nbytes / kern_s / PEAK_HBM,
+                             "algorithmic_bytes": nbytes}},
+    }
+    if not args.no_decode:
+        result["decode"] = bench_decode(torch, ssm, synth)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,132 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) selective state-space (S6) library.
+ *
+ * Two operations, both from the page "Mamba: Linear-Time Sequence Modeling
+ * with Selective State Spaces" (reading guide to arXiv 2312.00752):
+ *
+ *   ssm_scan_fwd      the fused selective scan over a whole sequence.
+ *                     "Method": A-bar = exp(Delta A) by zero-order hold; the
+ *                     recurrence h_t = A-bar_t h_{t-1} + B-bar_t x_t; the
+ *                     readout y_t = C_t h_t taken after the step-t update.
+ *                     "The selection mechanism (S6)": Delta_t, B_t, C_t
+ *                     depend on the token; Delta_t = softplus(dt + dt_bias).
+ *                     "Hardware-aware state expansion": the expanded
+ *                     (batch, L, dim, N) state is never written to memory;
+ *                     only the contracted output and the final state are.
+ *                     B-bar follows the simplified form dB = Delta * B of the
+ *                     dynamic-parameterization section of the soft186.com page
+ *                     "Mamba选择性状态空间机制：效率提升10倍的核心突破".
+ *                     Output: y = (C . h + Dskip * x) * silu(z), silu(z) =
+ *                     z * sigmoid(z); a NULL z means no gate.
+ *
+ *   ssm_state_update  one decode step: the same arithmetic at L = 1 on a
+ *                     fixed dim x N state per sequence, updated in place
+ *                     (Q&A on generation: constant work per token, no KV cache).
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *     densely packed (last index fastest).  The library allocates nothing,
+ *     keeps no state between calls, and is reentrant.
+ *   - Layouts: x, dt, z, y      [batch][dim][seqlen]
+ *              Bm, Cm           [batch][dstate][seqlen]
+ *              A                [dim][dstate]          (fp32, real, diagonal)
+ *              Dskip, dt_bias   [dim]                  (fp32)
+ *              h0, hL, state    [batch][dim][dstate]   (fp32)
+ *     For ssm_state_update the seqlen index is dropped: x, dt, z, y are
+ *     [batch][dim] and Bm, Cm are [batch][dstate].
+ *   - in_dtype is the storage type of x, dt, z, Bm, Cm; arithmetic is fp32.
+ *   - Every pointer must be aligned to its element size (2 bytes for bf16,
+ *     4 for fp32); the decode `state` must be 16-byte aligned.  The kernels
+ *     use 16-byte vector accesses wherever the addresses allow it.
+ *   - Argument errors are found before anything is launched: the call then
+ *     returns the status and writes nothing.  A failed launch returns
+ *     SSM_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation of `stream`.
+ *   - Calls are asynchronous: they return once the work is enqueued on
+ *     `stream` (a hipStream_t; NULL is the default stream).
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum { SSM_F32 = 0, SSM_BF16 = 1 } ssm_dtype_t;
+
+typedef enum {
+    SSM_OK = 0,
+    SSM_ERR_NULL_ARG = 1,    /* a required pointer is NULL                         */
+    SSM_ERR_BAD_SHAPE = 2,   /* a size < 1 or beyond the supported range (below)    */
+    SSM_ERR_BAD_DTYPE = 3,   /* in_dtype or out_dtype is not a value of ssm_dtype_t */
+    SSM_ERR_MISALIGNED = 4,  /* a pointer below its element alignment (state: 16 B) */
+    SSM_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap    */
+    SSM_ERR_UNSUPPORTED = 6, /* dstate not in {1,2,4,8,16}, or an unknown flag bit */
+    SSM_ERR_WORKSPACE = 7,   /* workspace smaller than ssm_scan_fwd_workspace_bytes */
+    SSM_ERR_HIP = 8          /* the HIP runtime rejected the launch                */
+} ssm_status_t;
+
+/* Reserved: exact zero-order-hold B-bar = (Delta A)^-1 (exp(Delta A) - 1) Delta B
+ * from the "Method" section.  This version rejects it with SSM_ERR_UNSUPPORTED. */
+#define SSM_FLAG_ZOH_B 0x1u
+
+/* SSM_ABI_VERSION of the loaded library. */
+int ssm_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *ssm_status_string(ssm_status_t status);
+
+/* Device workspace ssm_scan_fwd needs for these sizes, in bytes (0: none;
+ * the workspace argument may then be NULL). */
+size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
+
+/*
+ * Selective scan over the whole sequence.
+ *   x        [batch][dim][seqlen]   in_dtype  input
+ *   dt       [batch][dim][seqlen]   in_dtype  raw step, before bias and softplus
+ *   dt_bias  [dim]     fp32, or NULL (zero): Delta = softplus(dt + dt_bias)
+ *   A        [dim][dstate]          fp32      diagonal state matrix per channel
+ *   Bm, Cm   [batch][dstate][seqlen] in_dtype input and output matrices,
+ *                                              shared by all channels
+ *   Dskip    [dim]     fp32, or NULL (zero)   skip weight
+ *   z        [batch][dim][seqlen]   in_dtype, or NULL (no gate)
+ *   h0       [batch][dim][dstate]   fp32, or NULL (zero initial state)
+ *   y        [batch][dim][seqlen]   out_dtype output; must not overlap any input
+ *   hL       [batch][dim][dstate]   fp32 final state, or NULL (not returned);
+ *            may be exactly h0 (each channel reads its h0 before writing hL)
+ *            but must not otherwise overlap an input or y
+ *   workspace, workspace_bytes: device scratch of at least
+ *            ssm_scan_fwd_workspace_bytes(...) bytes (NULL allowed when 0)
+ * Supported sizes: batch <= 65535, seqlen <= 2^30, dstate in {1, 2, 4, 8, 16}.
+ */
+ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+                          unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                          const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                          const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                          float *hL, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step (seqlen = 1) on a persistent state.
+ *   state    [batch][dim][dstate]   fp32, read and overwritten in place
+ *   x, dt    [batch][dim]           in_dtype
+ *   dt_bias  [dim] fp32 or NULL;  A [dim][dstate] fp32
+ *   Bm, Cm   [batch][dstate]        in_dtype
+ *   Dskip    [dim] fp32 or NULL;  z [batch][dim] in_dtype or NULL
+ *   y        [batch][dim]           out_dtype; must not overlap any input or state
+ * Supported sizes: batch * dim < 2^31, dstate in {1, 2, 4, 8, 16}.
+ */
+ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
+                              unsigned flags, float *state, const void *x, const void *dt,
+                              const float *dt_bias, const float *A, const void *Bm,
+                              const void *Cm, const float *Dskip, const void *z,
+                              ssm_dtype_t out_dtype, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

@@ -1,0 +1,149 @@
+"""Selective state-space (S6) scan for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/ssm.h`` (``libssm.so``):
+argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``csrc/``; PyTorch only provides device memory and the stream.
+There is no CPU fallback: if the library is missing or no GPU is present the
+calls raise.
+
+    y, hL = ssm_scan_fwd(x, dt, A, Bm, Cm, dt_bias=..., Dskip=..., z=..., h0=...)
+    y = ssm_state_update(state, x, dt, A, Bm, Cm, dt_bias=..., Dskip=..., z=...)
+
+Layouts: x, dt, z, y [batch, dim, L]; Bm, Cm [batch, N, L]; A [dim, N];
+Dskip, dt_bias [dim]; h0, hL, state [batch, dim, N] (decode: drop L).
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssm.so")
+
+SSM_F32, SSM_BF16 = 0, 1
+STATUS = {
+    0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_BAD_DTYPE",
+    4: "SSM_ERR_MISALIGNED", 5: "SSM_ERR_ALIAS", 6: "SSM_ERR_UNSUPPORTED",
+    7: "SSM_ERR_WORKSPACE", 8: "SSM_ERR_HIP",
+}
+EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
+           "ssm_scan_fwd", "ssm_state_update"]
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libssm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libssm.so is not built (run __graft_entry__.build() or "
+                               "python -m selective_state_space_64_amd._build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, u, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+        L.ssm_abi_version.restype = i
+        L.ssm_abi_version.argtypes = []
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_status_string.argtypes = [i]
+        L.ssm_scan_fwd_workspace_bytes.restype = sz
+        L.ssm_scan_fwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.ssm_scan_fwd.restype = i
+        L.ssm_scan_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 9 + [i, vp, vp, vp, sz, vp]
+        L.ssm_state_update.restype = i
+        L.ssm_state_update.argtypes = [i, i, i, i, u] + [vp] * 9 + [i, vp, vp]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise SSMError(status, lib().ssm_status_string(status).decode())
+
+
+def _dtype_code(t):
+    if t == torch.float32:
+        return SSM_F32
+    if t == torch.bfloat16:
+        return SSM_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t)
+
+
+def _ptr(t, name, shape=None, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    return t.data_ptr()
+
+
+def _stream(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return s.cuda_stream
+
+
+def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
+                 out_dtype=torch.float32, return_final_state=True, y=None, hL=None,
+                 stream=None):
+    """Fused selective scan; returns (y, hL) (hL is None unless requested)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    N = A.shape[-1]
+    ind = x.dtype
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=out_dtype, device=x.device)
+    if hL is None and return_final_state:
+        hL = torch.empty((batch, dim, N), dtype=torch.float32, device=x.device)
+    f32 = torch.float32
+    args = [
+        _ptr(x, "x", (batch, dim, L), ind), _ptr(dt, "dt", (batch, dim, L), ind),
+        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
+        _ptr(Bm, "Bm", (batch, N, L), ind), _ptr(Cm, "Cm", (batch, N, L), ind),
+        _ptr(Dskip, "Dskip", (dim,), f32), _ptr(z, "z", (batch, dim, L), ind),
+        _ptr(h0, "h0", (batch, dim, N), f32),
+    ]
+    yp = _ptr(y, "y", (batch, dim, L), out_dtype)
+    hp = _ptr(hL, "hL", (batch, dim, N), f32)
+    st = lib().ssm_scan_fwd(batch, dim, L, N, _dtype_code(ind), 0, *args, _dtype_code(y.dtype),
+                            yp, hp, None, 0, _stream(stream, x.device))
+    _check(st)
+    return y, hL
+
+
+def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None,
+                     out_dtype=torch.float32, y=None, stream=None):
+    """One decode step; updates `state` in place and returns y [batch, dim]."""
+    batch, dim, N = state.shape
+    ind = x.dtype
+    if y is None:
+        y = torch.empty((batch, dim), dtype=out_dtype, device=x.device)
+    f32 = torch.float32
+    args = [
+        _ptr(state, "state", (batch, dim, N), f32),
+        _ptr(x, "x", (batch, dim), ind), _ptr(dt, "dt", (batch, dim), ind),
+        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
+        _ptr(Bm, "Bm", (batch, N), ind), _ptr(Cm, "Cm", (batch, N), ind),
+        _ptr(Dskip, "Dskip", (dim,), f32), _ptr(z, "z", (batch, dim), ind),
+    ]
+    yp = _ptr(y, "y", (batch, dim), out_dtype)
+    st = lib().ssm_state_update(batch, dim, N, _dtype_code(ind), 0, *args, _dtype_code(y.dtype),
+                                yp, _stream(stream, x.device))
+    _check(st)
+    return y
+
+
+scan_fwd = ssm_scan_fwd
+state_update = ssm_state_update

@@ -1,0 +1,176 @@
+// ssm_api.hip -- the C ABI declared in include/ssm.h: argument validation
+// and dispatch to the gfx950 kernels.  Every argument error is detected here,
+// before anything is enqueued, so a failing call has no side effects.
+#include "ssm.h"
+
+#include <stdint.h>
+
+#include "ssm_launch.hpp"
+
+namespace {
+
+// True when p is not a multiple of `align` bytes (NULL is never misaligned).
+bool misaligned(const void *p, uintptr_t align)
+{
+    return p && (reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0;
+}
+
+struct Span {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Span span(const void *p, size_t bytes)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return {a, a + bytes};
+}
+
+bool overlaps(const void *p, size_t pb, const void *q, size_t qb)
+{
+    if (!p || !q || pb == 0 || qb == 0) return false;
+    const Span a = span(p, pb), b = span(q, qb);
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool valid_dtype(int t) { return t == SSM_F32 || t == SSM_BF16; }
+size_t dsize(int t) { return t == SSM_BF16 ? 2 : 4; }
+bool valid_dstate(int n) { return n == 1 || n == 2 || n == 4 || n == 8 || n == 16; }
+
+// Product of positive ints as size_t, or 0 on overflow past 2^62.
+size_t mul3(long long a, long long b, long long c)
+{
+    const unsigned __int128 r = (unsigned __int128)a * (unsigned __int128)b * (unsigned __int128)c;
+    if (r > ((unsigned __int128)1 << 62)) return 0;
+    return size_t(r);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char *ssm_status_string(ssm_status_t s)
+{
+    switch (s) {
+    case SSM_OK: return "ok";
+    case SSM_ERR_NULL_ARG: return "a required pointer argument is NULL";
+    case SSM_ERR_BAD_SHAPE: return "batch, dim and seqlen must be >= 1 and within the supported range";
+    case SSM_ERR_BAD_DTYPE: return "in_dtype/out_dtype must be SSM_F32 or SSM_BF16";
+    case SSM_ERR_MISALIGNED: return "a pointer is not aligned to its element size (state: 16 bytes)";
+    case SSM_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
+    case SSM_ERR_UNSUPPORTED: return "unsupported dstate (use 1, 2, 4, 8 or 16) or flag bit";
+    case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_fwd_workspace_bytes";
+    case SSM_ERR_HIP: return "the HIP runtime rejected the kernel launch";
+    }
+    return "unknown status";
+}
+
+size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    (void)batch; (void)dim; (void)seqlen; (void)dstate;
+    return 0;
+}
+
+ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+                          unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                          const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                          const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                          float *hL, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
+        return SSM_ERR_BAD_SHAPE;
+    if (!valid_dstate(dstate) || flags != 0) return SSM_ERR_UNSUPPORTED;
+
+    const size_t seq_elems = mul3(batch, dim, seqlen);
+    const size_t bc_elems = mul3(batch, dstate, seqlen);
+    const size_t st_elems = mul3(batch, dim, dstate);
+    if (!seq_elems || !bc_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+
+    const size_t in = dsize(in_dtype);
+    for (const void *p : {x, dt, Bm, Cm, z})
+        if (misaligned(p, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)dt_bias, (const void *)A, (const void *)Dskip,
+                          (const void *)h0, (const void *)hL})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+
+    const size_t ybytes = seq_elems * dsize(out_dtype);
+    const size_t hbytes = st_elems * sizeof(float);
+    struct In {
+        const void *p;
+        size_t bytes;
+    } inputs[] = {{x, seq_elems * in},  {dt, seq_elems * in},       {dt_bias, dim * sizeof(float)},
+                  {A, size_t(dim) * dstate * sizeof(float)},
+                  {Bm, bc_elems * in},  {Cm, bc_elems * in},        {Dskip, dim * sizeof(float)},
+                  {z, seq_elems * in},  {h0, hbytes}};
+    for (const In &i : inputs) {
+        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        // hL may be exactly h0 (read before written per channel), nothing else
+        if (hL && !(i.p == h0 && hL == h0) && overlaps(hL, hbytes, i.p, i.bytes))
+            return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, ybytes, hL, hbytes)) return SSM_ERR_ALIAS;
+
+    if (workspace_bytes < ssm_scan_fwd_workspace_bytes(batch, dim, seqlen, dstate))
+        return SSM_ERR_WORKSPACE;
+    (void)workspace;
+
+    ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                    x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL};
+    const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
+                              unsigned flags, float *state, const void *x, const void *dt,
+                              const float *dt_bias, const float *A, const void *Bm,
+                              const void *Cm, const float *Dskip, const void *z,
+                              ssm_dtype_t out_dtype, void *y, void *stream)
+{
+    if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1) return SSM_ERR_BAD_SHAPE;
+    if (!valid_dstate(dstate) || flags != 0) return SSM_ERR_UNSUPPORTED;
+
+    const size_t rows = mul3(batch, dim, 1);
+    if (rows > ssm::kMaxDecodeRows) return SSM_ERR_BAD_SHAPE;
+    const size_t st_elems = mul3(batch, dim, dstate);
+    if (!rows || !st_elems) return SSM_ERR_BAD_SHAPE;
+
+    const size_t in = dsize(in_dtype);
+    if (misaligned(state, 16)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {x, dt, Bm, Cm, z})
+        if (misaligned(p, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)dt_bias, (const void *)A, (const void *)Dskip})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+
+    const size_t ybytes = rows * dsize(out_dtype);
+    const size_t sbytes = st_elems * sizeof(float);
+    struct In {
+        const void *p;
+        size_t bytes;
+    } inputs[] = {{x, rows * in},
+                  {dt, rows * in},
+                  {dt_bias, dim * sizeof(float)},
+                  {A, size_t(dim) * dstate * sizeof(float)},
+                  {Bm, size_t(batch) * dstate * in},
+                  {Cm, size_t(batch) * dstate * in},
+                  {Dskip, dim * sizeof(float)},
+                  {z, rows * in}};
+    for (const In &i : inputs) {
+        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        if (overlaps(state, sbytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, ybytes, state, sbytes)) return SSM_ERR_ALIAS;
+
+    ssm::UpdateArgs a{batch, dim, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                      state, x, dt, dt_bias, A, Bm, Cm, Dskip, z, y};
+    const hipError_t e = ssm::launch_state_update(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// ssm_launch.hpp -- internal interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ssm {
+
+struct ScanArgs {
+    int batch, dim, seqlen, dstate;
+    int in_bf16, out_bf16;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *h0;
+    void *y;
+    float *hL;
+};
+
+struct UpdateArgs {
+    int batch, dim, dstate;
+    int in_bf16, out_bf16;
+    float *state;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    void *y;
+};
+
+// Both return hipSuccess or the launch error; arguments are already validated.
+hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t stream);
+hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream);
+
+// Largest batch the scan grid supports (grid y dimension).
+constexpr int kMaxBatch = 65535;
+// Longest sequence: keeps every in-kernel timestep index inside 32 bits.
+constexpr int kMaxSeqlen = 1 << 30;
+// Most (batch, channel) rows one decode launch covers (1-D grid of 256-lane blocks).
+constexpr long long kMaxDecodeRows = (1LL << 31) - 1;
+
+}  // namespace ssm

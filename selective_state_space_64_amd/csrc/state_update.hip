@@ -1,0 +1,141 @@
+// state_update.hip -- single-token decode step for gfx950.
+//
+// One token per sequence against a persistent fp32 state of dim x N per
+// sequence, updated in place (Q&A on generation of the page "Mamba:
+// Linear-Time Sequence Modeling with Selective State Spaces": a fixed-size
+// state and constant work per token).  Same arithmetic as the scan at L = 1:
+//     Delta = softplus(dt + dt_bias[d])
+//     h[n]  = exp(Delta A[d,n]) h[n] + Delta Bm[b,n] x
+//     y     = (sum_n Cm[b,n] h[n] + Dskip[d] x) * silu(z)
+//
+// The step is bound by moving the state (read + write, 2 x 4N bytes per
+// (b, d)).  One lane owns one (b, d): its N states are one contiguous run of
+// 4N bytes, so a wave reads and writes 64 consecutive runs with 16-byte
+// vector accesses (the state is 16-byte aligned).  A, Bm and Cm are shared
+// across lanes and come from cache.
+#include "ssm_device.hpp"
+#include "ssm_launch.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct UpdateParams {
+    int batch, dim;
+    float *state;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    void *y;
+};
+
+template <int N>
+__device__ inline void load_f32(const float *p, float *v)
+{
+    if constexpr (N % 4 == 0) {
+        const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            const f32x4 w = q[i];
+            v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) v[i] = p[i];
+    }
+}
+
+template <typename Tin, typename Tout, int N>
+__global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
+{
+    const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
+    const long long rows = (long long)p.batch * p.dim;
+    if (idx >= rows) return;
+    const int b = int(idx / p.dim);
+    const int d = int(idx - (long long)b * p.dim);
+
+    float h[N], a[N], bm[N], cm[N];
+    float *st = p.state + idx * N;
+    load_f32<N>(st, h);
+#pragma unroll
+    for (int n = 0; n < N; ++n) a[n] = p.A[size_t(d) * N + n];
+    const Tin *Bp = static_cast<const Tin *>(p.Bm) + size_t(b) * N;
+    const Tin *Cp = static_cast<const Tin *>(p.Cm) + size_t(b) * N;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        bm[n] = io<Tin>::load1(Bp + n);
+        cm[n] = io<Tin>::load1(Cp + n);
+    }
+    const float xv = io<Tin>::load1(static_cast<const Tin *>(p.x) + idx);
+    const float dtv = io<Tin>::load1(static_cast<const Tin *>(p.dt) + idx);
+    const float bias = p.dt_bias ? p.dt_bias[d] : 0.0f;
+    const float skip = p.Dskip ? p.Dskip[d] : 0.0f;
+
+    const float delta = softplus(dtv + bias);
+    const float u = delta * xv;
+    float acc = skip * xv;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        const float dA = exp2_hw(delta * (a[n] * kLog2e));
+        h[n] = __builtin_fmaf(dA, h[n], u * bm[n]);
+        acc = __builtin_fmaf(cm[n], h[n], acc);
+    }
+    if (p.z) acc *= silu(io<Tin>::load1(static_cast<const Tin *>(p.z) + idx));
+
+    if constexpr (N % 4 == 0) {
+        f32x4 *q = reinterpret_cast<f32x4 *>(st);
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) {
+            f32x4 w = {h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]};
+            q[i] = w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) st[i] = h[i];
+    }
+    if constexpr (sizeof(Tout) == 4) {
+        static_cast<float *>(p.y)[idx] = acc;
+    } else {
+        static_cast<uint16_t *>(p.y)[idx] = uint16_t(pack_bf16x2(acc, 0.0f) & 0xffffu);
+    }
+}
+
+template <typename Tin, typename Tout, int N>
+hipError_t launch_typed(const UpdateArgs &a, hipStream_t stream)
+{
+    UpdateParams p{a.batch, a.dim, a.state, a.x, a.dt, a.dt_bias, a.A,
+                   a.Bm, a.Cm, a.Dskip, a.z, a.y};
+    const long long rows = (long long)a.batch * a.dim;
+    const unsigned blocks = unsigned((rows + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL((state_update_kernel<Tin, Tout, N>), dim3(blocks), dim3(kThreads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_n(const UpdateArgs &a, hipStream_t stream)
+{
+    switch (a.dstate) {
+    case 1: return launch_typed<Tin, Tout, 1>(a, stream);
+    case 2: return launch_typed<Tin, Tout, 2>(a, stream);
+    case 4: return launch_typed<Tin, Tout, 4>(a, stream);
+    case 8: return launch_typed<Tin, Tout, 8>(a, stream);
+    case 16: return launch_typed<Tin, Tout, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream)
+{
+    if (a.in_bf16) {
+        return a.out_bf16 ? launch_n<bf16_t, bf16_t>(a, stream) : launch_n<bf16_t, float>(a, stream);
+    }
+    return a.out_bf16 ? launch_n<float, bf16_t>(a, stream) : launch_n<float, float>(a, stream);
+}
+
+}  // namespace ssm

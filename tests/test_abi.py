@@ -1,0 +1,206 @@
+"""The C-ABI boundary: exported symbols (CPU), and the documented status for
+every argument error with nothing written (GPU, real device buffers)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import selective_state_space_64_amd as ssm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "ssm.h")) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(ssm.EXPORTS)
+    lib = ctypes.CDLL(ssm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_host_only_entry_points():
+    L = ssm.lib()
+    assert L.ssm_abi_version() == 1
+    for s in range(9):
+        assert L.ssm_status_string(s).decode()
+    assert L.ssm_status_string(99).decode() == "unknown status"
+    assert L.ssm_scan_fwd_workspace_bytes(4, 5120, 2048, 16) == 0
+
+
+# ---------------------------------------------------------------- GPU: errors
+def _bufs(batch=2, dim=8, L=40, N=16, dtype=torch.bfloat16):
+    g = torch.Generator().manual_seed(0)
+    r = lambda *s: torch.randn(*s, generator=g).to(dtype).cuda()
+    f = lambda *s: torch.randn(*s, generator=g).cuda()
+    return dict(batch=batch, dim=dim, L=L, N=N, x=r(batch, dim, L), dt=r(batch, dim, L),
+                z=r(batch, dim, L), Bm=r(batch, N, L), Cm=r(batch, N, L), A=-f(dim, N).abs(),
+                Dskip=f(dim), dt_bias=f(dim), h0=f(batch, dim, N),
+                y=torch.full((batch, dim, L), 7.0, device="cuda"),
+                hL=torch.full((batch, dim, N), 7.0, device="cuda"))
+
+
+def _call(b, **over):
+    a = dict(batch=b["batch"], dim=b["dim"], seqlen=b["L"], dstate=b["N"], in_dtype=1, flags=0,
+             x=b["x"].data_ptr(), dt=b["dt"].data_ptr(), dt_bias=b["dt_bias"].data_ptr(),
+             A=b["A"].data_ptr(), Bm=b["Bm"].data_ptr(), Cm=b["Cm"].data_ptr(),
+             Dskip=b["Dskip"].data_ptr(), z=b["z"].data_ptr(), h0=b["h0"].data_ptr(), out_dtype=0,
+             y=b["y"].data_ptr(), hL=b["hL"].data_ptr(), ws=None, wsb=0, stream=None)
+    a.update(over)
+    return ssm.lib().ssm_scan_fwd(a["batch"], a["dim"], a["seqlen"], a["dstate"], a["in_dtype"],
+                                  a["flags"], a["x"], a["dt"], a["dt_bias"], a["A"], a["Bm"],
+                                  a["Cm"], a["Dskip"], a["z"], a["h0"], a["out_dtype"], a["y"],
+                                  a["hL"], a["ws"], a["wsb"], a["stream"])
+
+
+ERRORS = [
+    ("null_x", dict(x=None), 1), ("null_A", dict(A=None), 1), ("null_y", dict(y=None), 1),
+    ("batch0", dict(batch=0), 2), ("dim_neg", dict(dim=-1), 2), ("L0", dict(seqlen=0), 2),
+    ("batch_huge", dict(batch=70000), 2), ("L_huge", dict(seqlen=(1 << 30) + 1), 2),
+    ("in_dtype", dict(in_dtype=7), 3), ("out_dtype", dict(out_dtype=-1), 3),
+    ("N3", dict(dstate=3), 6), ("N32", dict(dstate=32), 6), ("flag_zoh", dict(flags=1), 6),
+    ("flag_other", dict(flags=0x80), 6),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("name,over,status", ERRORS, ids=[e[0] for e in ERRORS])
+def test_scan_argument_errors_write_nothing(name, over, status):
+    b = _bufs()
+    assert _call(b, **over) == status
+    torch.cuda.synchronize()
+    assert (b["y"] == 7.0).all() and (b["hL"] == 7.0).all()
+
+
+@pytest.mark.gpu
+def test_scan_misaligned_and_alias():
+    b = _bufs()
+    assert _call(b, x=b["x"].data_ptr() + 1) == 4
+    assert _call(b, hL=b["hL"].data_ptr() + 2) == 4
+    assert _call(b, y=b["x"].data_ptr()) == 5                       # y over x (bf16 vs f32 sizes)
+    assert _call(b, hL=b["Dskip"].data_ptr()) == 5                  # hL over a parameter
+    assert _call(b, hL=b["y"].data_ptr()) == 5                      # hL over y
+    big = torch.empty(4096, device="cuda")
+    assert _call(b, y=big.data_ptr(), hL=big.data_ptr() + 64) == 5  # hL inside y
+    torch.cuda.synchronize()
+    assert (b["y"] == 7.0).all() and (b["hL"] == 7.0).all()
+    # hL exactly equal to h0 is allowed
+    assert _call(b, hL=b["h0"].data_ptr()) == 0
+    torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_state_update_argument_errors():
+    b = _bufs()
+    st = b["h0"]
+    keep = st.clone()
+    L = ssm.lib()
+    x1, dt1 = b["x"][:, :, 0].contiguous(), b["dt"][:, :, 0].contiguous()
+    B1, C1 = b["Bm"][:, :, 0].contiguous(), b["Cm"][:, :, 0].contiguous()
+    y = torch.full((2, 8), 7.0, device="cuda")
+
+    def call(**o):
+        a = dict(batch=2, dim=8, N=16, ind=1, flags=0, state=st.data_ptr(), x=x1.data_ptr(),
+                 dt=dt1.data_ptr(), bias=b["dt_bias"].data_ptr(), A=b["A"].data_ptr(),
+                 B=B1.data_ptr(), C=C1.data_ptr(), D=b["Dskip"].data_ptr(), z=None, outd=0,
+                 y=y.data_ptr())
+        a.update(o)
+        return L.ssm_state_update(a["batch"], a["dim"], a["N"], a["ind"], a["flags"], a["state"],
+                                  a["x"], a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"],
+                                  a["z"], a["outd"], a["y"], None)
+
+    assert call(state=None) == 1
+    assert call(batch=0) == 2
+    assert call(ind=5) == 3
+    assert call(x=x1.data_ptr() + 1) == 4
+    assert call(state=st.data_ptr() + 4) == 4
+    assert call(y=st.data_ptr()) == 5
+    assert call(state=b["A"].data_ptr()) == 5
+    assert call(N=5) == 6
+    assert call(flags=1) == 6
+    torch.cuda.synchronize()
+    assert torch.equal(st, keep) and (y == 7.0).all()
+    with pytest.raises(ssm.SSMError):
+        ssm.ssm_scan_fwd(b["x"], b["dt"], b["A"][:, :3].contiguous(), b["Bm"][:, :3].contiguous(),
+                         b["Cm"][:, :3].contiguous())
+
+
+# ---------------------------------------------------------------- CPU: validation
+# Fake, 16-byte-aligned addresses that are never dereferenced: every case below
+# must be rejected before any launch.  Skipped where a GPU is present so that a
+# validation bug could never launch a kernel on them.
+_FAKE = {k: 0x10000000 * (i + 1) for i, k in enumerate(
+    ["x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias", "h0", "y", "hL"])}
+
+
+def _fake_call(**over):
+    a = dict(batch=2, dim=8, seqlen=40, dstate=16, in_dtype=1, flags=0, out_dtype=0,
+             ws=None, wsb=0, **_FAKE)
+    a.update(over)
+    return ssm.lib().ssm_scan_fwd(a["batch"], a["dim"], a["seqlen"], a["dstate"], a["in_dtype"],
+                                  a["flags"], a["x"], a["dt"], a["dt_bias"], a["A"], a["Bm"],
+                                  a["Cm"], a["Dskip"], a["z"], a["h0"], a["out_dtype"], a["y"],
+                                  a["hL"], a["ws"], a["wsb"], None)
+
+
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer checks run only without a GPU")
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", ERRORS, ids=[e[0] for e in ERRORS])
+def test_validation_rejects_before_launch(name, over, status):
+    assert _fake_call(**over) == status
+
+
+@no_gpu
+def test_validation_alignment_and_alias():
+    assert _fake_call(x=_FAKE["x"] + 1) == 4
+    assert _fake_call(z=_FAKE["z"] + 3) == 4
+    assert _fake_call(A=_FAKE["A"] + 2) == 4
+    assert _fake_call(out_dtype=1, y=_FAKE["y"] + 1) == 4
+    assert _fake_call(x=_FAKE["x"] + 2, dt=_FAKE["dt"] + 2) == 8  # bf16 element alignment suffices
+    assert _fake_call(y=_FAKE["x"]) == 5
+    assert _fake_call(y=_FAKE["x"] + 1280 - 16) == 5      # tail of x (2*8*40 bf16 = 1280 B)
+    assert _fake_call(y=_FAKE["x"] + 1280) != 5           # just past x: no overlap with x
+    assert _fake_call(hL=_FAKE["Dskip"]) == 5
+    assert _fake_call(hL=_FAKE["y"] + 2560 - 16) == 5     # last bytes of y (fp32)
+    assert _fake_call(hL=_FAKE["h0"] + 16) == 5           # partial overlap with h0
+    # valid arguments reach the launch, which fails without a device
+    assert _fake_call() == 8
+    assert _fake_call(hL=_FAKE["h0"]) == 8                # hL == h0 exactly is allowed
+    assert _fake_call(z=None, h0=None, hL=None, Dskip=None, dt_bias=None) == 8
+
+
+@no_gpu
+def test_state_update_validation():
+    L = ssm.lib()
+
+    def call(**o):
+        a = dict(batch=2, dim=8, N=16, ind=1, flags=0, state=_FAKE["h0"], x=_FAKE["x"],
+                 dt=_FAKE["dt"], bias=_FAKE["dt_bias"], A=_FAKE["A"], B=_FAKE["Bm"], C=_FAKE["Cm"],
+                 D=_FAKE["Dskip"], z=_FAKE["z"], outd=0, y=_FAKE["y"])
+        a.update(o)
+        return L.ssm_state_update(a["batch"], a["dim"], a["N"], a["ind"], a["flags"], a["state"],
+                                  a["x"], a["dt"], a["bias"], a["A"], a["B"], a["C"], a["D"],
+                                  a["z"], a["outd"], a["y"], None)
+
+    assert call(state=None) == 1
+    assert call(y=None) == 1
+    assert call(batch=0) == 2
+    assert call(ind=5) == 3
+    assert call(outd=2) == 3
+    assert call(x=_FAKE["x"] + 1) == 4
+    assert call(state=_FAKE["h0"] + 4) == 4
+    assert call(x=_FAKE["x"] + 2) == 8
+    assert call(y=_FAKE["h0"]) == 5
+    assert call(state=_FAKE["A"]) == 5
+    assert call(N=5) == 6
+    assert call(flags=1) == 6
+    assert call() == 8

@@ -1,0 +1,89 @@
+"""GPU parity of ssm_state_update (through the C ABI) against the fp64 oracle:
+the 256-step decode workload on a [64, 5120, 16] fp32 state updated in place,
+and small shapes compared in full.  The oracle side runs the same steps as
+one scan from the initial state (the decode recurrence and the scan are the
+same function; the oracle's own pins show it)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_64_amd as ssm
+from selective_state_space_64_amd import synth
+from helpers import TOL_BF16_OUT, rel_err, sample_rows, to_dev, tol_for, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _steps(t):
+    """[batch, X, steps] -> [steps, batch, X] contiguous per-step slices."""
+    return t.permute(2, 0, 1).contiguous()
+
+
+def _run_decode(inp, steps, gate=True, out_dtype=torch.float32):
+    state = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
+    xs, dts, zs = _steps(to_dev(inp, "x")), _steps(to_dev(inp, "dt")), _steps(to_dev(inp, "z"))
+    Bs, Cs = _steps(to_dev(inp, "Bm")), _steps(to_dev(inp, "Cm"))
+    A, Dk, bias = to_dev(inp, "A"), to_dev(inp, "Dskip"), to_dev(inp, "dt_bias")
+    ys = torch.empty((steps,) + tuple(state.shape[:2]), dtype=out_dtype, device="cuda")
+    for s in range(steps):
+        ssm.ssm_state_update(state, xs[s], dts[s], A, Bs[s], Cs[s], dt_bias=bias, Dskip=Dk,
+                             z=zs[s] if gate else None, y=ys[s], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return ys, state
+
+
+def _oracle_decode(inp, rows, gate=True):
+    ys, hs = [], []
+    for b, d in rows:
+        y, hL = oracle.scan_fwd(
+            inp.values("x")[b:b + 1, d:d + 1], inp.values("dt")[b:b + 1, d:d + 1],
+            inp.A[d:d + 1].astype(np.float64), inp.values("Bm")[b:b + 1], inp.values("Cm")[b:b + 1],
+            dt_bias=inp.dt_bias[d:d + 1].astype(np.float64),
+            Dskip=inp.Dskip[d:d + 1].astype(np.float64),
+            z=inp.values("z")[b:b + 1, d:d + 1] if gate else None,
+            h0=inp.h0[b:b + 1, d:d + 1].astype(np.float64))
+        ys.append(y[0, 0])
+        hs.append(hL[0, 0])
+    return np.stack(ys), np.stack(hs)
+
+
+def test_decode_workload_sampled():
+    wl = synth.WORKLOADS[4]
+    print("workload", wl.name, flush=True)
+    inp = synth.make_inputs(wl)
+    ys, state = _run_decode(inp, wl.seqlen)
+    rows = sample_rows(wl.batch, wl.dim, per_batch=4, seed=4)[::3]
+    bi = torch.tensor([r[0] for r in rows], device="cuda")
+    di = torch.tensor([r[1] for r in rows], device="cuda")
+    gy = ys[:, bi, di].T.cpu().numpy()
+    gh = state[bi, di].cpu().numpy()
+    ry, rh = _oracle_decode(inp, rows)
+    ey, eh = rel_err(gy, ry), rel_err(gh, rh)
+    print("  %d rows x %d steps: err y %.3e state %.3e" % (len(rows), wl.seqlen, ey, eh), flush=True)
+    assert ey <= tol_for("bf16") and eh <= tol_for("bf16")
+
+
+@pytest.mark.parametrize("shape", [(3, 7, 16, 5, "f32"), (2, 70, 4, 9, "bf16"), (1, 1, 1, 3, "f32"),
+                                   (4, 33, 2, 4, "bf16"), (2, 64, 8, 6, "f32")],
+                         ids=lambda s: "b%d_d%d_N%d_steps%d_%s" % s)
+def test_decode_small_full(shape):
+    batch, dim, N, steps, dt = shape
+    inp = synth.make_inputs(workload("dec", batch, dim, N, steps, dt), with_h0=True)
+    for gate in (True, False):
+        ys, state = _run_decode(inp, steps, gate)
+        rows = [(b, d) for b in range(batch) for d in range(dim)]
+        ry, rh = _oracle_decode(inp, rows, gate)
+        gy = ys.permute(1, 2, 0).reshape(batch * dim, steps).cpu().numpy()
+        gh = state.reshape(batch * dim, N).cpu().numpy()
+        tol = tol_for(dt)
+        assert rel_err(gy, ry) <= tol and rel_err(gh, rh) <= tol, (shape, gate)
+
+
+def test_decode_bf16_output():
+    inp = synth.make_inputs(workload("dec16", 2, 40, 16, 4, "bf16"), with_h0=True)
+    ys, state = _run_decode(inp, 4, out_dtype=torch.bfloat16)
+    rows = [(b, d) for b in range(2) for d in range(40)]
+    ry, rh = _oracle_decode(inp, rows)
+    gy = ys.float().permute(1, 2, 0).reshape(80, 4).cpu().numpy()
+    assert rel_err(gy, ry) <= TOL_BF16_OUT

@@ -1,0 +1,139 @@
+"""Invariants of the HIP path that need no oracle: resume from a saved state,
+decode = scan, exact (bitwise) layout and causality probes, guard bands
+around the outputs, determinism, and in-place h0 -> hL."""
+import numpy as np
+import pytest
+import torch
+
+import selective_state_space_64_amd as ssm
+from selective_state_space_64_amd import synth
+from helpers import rel_err, to_dev, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_all(inp):
+    return {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}
+
+
+def _scan(t, **kw):
+    return ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                            Dskip=t["Dskip"], z=t.get("z"), **kw)
+
+
+def test_split_and_resume():
+    inp = synth.make_inputs(workload("split", 2, 32, 16, 1500, "f32"), with_h0=True)
+    t = _dev_all(inp)
+    y, hL = _scan(t)
+    for cut in (1, 256, 700, 1499):
+        a = {k: (v[..., :cut].contiguous() if k in ("x", "dt", "z", "Bm", "Cm") else v)
+             for k, v in t.items()}
+        b = {k: (v[..., cut:].contiguous() if k in ("x", "dt", "z", "Bm", "Cm") else v)
+             for k, v in t.items()}
+        y1, h1 = _scan(a)
+        y2, h2 = _scan(b, h0=h1)
+        torch.cuda.synchronize()
+        yy = torch.cat([y1, y2], dim=2)
+        assert rel_err(yy.cpu().numpy(), y.cpu().numpy()) <= 1e-5, cut
+        assert rel_err(h2.cpu().numpy(), hL.cpu().numpy()) <= 1e-5, cut
+
+
+def test_decode_chain_equals_scan():
+    inp = synth.make_inputs(workload("chain", 3, 40, 16, 37, "bf16"), with_h0=True)
+    t = _dev_all(inp)
+    h0 = torch.from_numpy(inp.h0).cuda()
+    y, hL = _scan(t, h0=h0)
+    state = h0.clone()
+    ys = []
+    for s in range(37):
+        ys.append(ssm.ssm_state_update(state, t["x"][..., s].contiguous(), t["dt"][..., s].contiguous(),
+                                       t["A"], t["Bm"][..., s].contiguous(), t["Cm"][..., s].contiguous(),
+                                       dt_bias=t["dt_bias"], Dskip=t["Dskip"],
+                                       z=t["z"][..., s].contiguous()))
+    torch.cuda.synchronize()
+    yd = torch.stack(ys, dim=2)
+    assert rel_err(yd.cpu().numpy(), y.cpu().numpy()) <= 1e-5
+    assert rel_err(state.cpu().numpy(), hL.cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layout_probe_bitexact(dtype):
+    """With Cm = 0 and no gate, y = fl32(Dskip[d] * x[b, d, l]) bit for bit."""
+    inp = synth.make_inputs(workload("probe", 3, 37, 16, 999, dtype), with_h0=True)
+    t = _dev_all(inp)
+    t["Cm"] = torch.zeros_like(t["Cm"])
+    t["z"] = None
+    y, _ = _scan(t, h0=torch.from_numpy(inp.h0).cuda())
+    torch.cuda.synchronize()
+    xv = inp.values("x").astype(np.float32)
+    ref = inp.Dskip[None, :, None].astype(np.float32) * xv
+    assert np.array_equal(y.cpu().numpy(), ref)
+
+
+def test_impulse_zero_pattern():
+    """x non-zero only at (b0, d0, l0) and Bm non-zero only in state n0: y is
+    non-zero exactly on (b0, d0, l >= l0) and hL exactly at (b0, d0, n0)."""
+    batch, dim, N, L = 2, 20, 16, 700
+    b0, d0, l0, n0 = 1, 17, 300, 5
+    x = torch.zeros(batch, dim, L, device="cuda")
+    x[b0, d0, l0] = 1.5
+    dt = torch.full((batch, dim, L), -3.0, device="cuda")
+    A = torch.full((dim, N), -0.01, device="cuda")
+    Bm = torch.zeros(batch, N, L, device="cuda")
+    Bm[:, n0, :] = 1.0
+    g = torch.Generator().manual_seed(3)
+    Cm = (torch.rand(batch, N, L, generator=g) + 0.5).cuda()
+    z = (torch.rand(batch, dim, L, generator=g) + 0.5).cuda()
+    Dk = torch.ones(dim, device="cuda")
+    y, hL = ssm.ssm_scan_fwd(x, dt, A, Bm, Cm, Dskip=Dk, z=z)
+    torch.cuda.synchronize()
+    nz = (y != 0).cpu().numpy()
+    expect = np.zeros_like(nz)
+    expect[b0, d0, l0:] = True
+    assert np.array_equal(nz, expect)
+    hz = (hL != 0).cpu().numpy()
+    he = np.zeros_like(hz)
+    he[b0, d0, n0] = True
+    assert np.array_equal(hz, he)
+
+
+def test_zero_decay_keeps_state_bitexact():
+    """A = 0 and x = 0: exp(0) = 1 and the input term is 0, so hL == h0 exactly."""
+    inp = synth.make_inputs(workload("keep", 2, 18, 16, 777, "f32"), with_h0=True)
+    t = _dev_all(inp)
+    t["A"] = torch.zeros_like(t["A"])
+    t["x"] = torch.zeros_like(t["x"])
+    h0 = torch.from_numpy(inp.h0).cuda()
+    _, hL = _scan(t, h0=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(hL, h0)
+
+
+def test_guard_bands_untouched():
+    inp = synth.make_inputs(workload("guard", 2, 21, 16, 301, "bf16"))
+    t = _dev_all(inp)
+    G = 64
+    nan_bits = torch.tensor([0x7FC0DEAD], dtype=torch.int32).view(torch.float32).item()
+    ybig = torch.full((2 * 21 * 301 + 2 * G,), nan_bits, device="cuda")
+    hbig = torch.full((2 * 21 * 16 + 2 * G,), nan_bits, device="cuda")
+    y = ybig[G:G + 2 * 21 * 301].view(2, 21, 301)
+    hL = hbig[G:G + 2 * 21 * 16].view(2, 21, 16)
+    _scan(t, y=y, hL=hL)
+    torch.cuda.synchronize()
+    for big, n in ((ybig, 2 * 21 * 301), (hbig, 2 * 21 * 16)):
+        bits = big.view(torch.int32).cpu().numpy()
+        assert (bits[:G] == 0x7FC0DEAD).all() and (bits[G + n:] == 0x7FC0DEAD).all()
+    assert torch.isfinite(y).all() and torch.isfinite(hL).all()
+
+
+def test_deterministic_and_inplace_state():
+    inp = synth.make_inputs(workload("det", 2, 40, 16, 1200, "bf16"), with_h0=True)
+    t = _dev_all(inp)
+    h0 = torch.from_numpy(inp.h0).cuda()
+    y1, h1 = _scan(t, h0=h0)
+    y2, h2 = _scan(t, h0=h0)
+    hin = h0.clone()
+    y3, h3 = _scan(t, h0=hin, hL=hin)  # final state written over the initial one
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    assert torch.equal(y1, y3) and torch.equal(h1, hin) and h3 is hin
