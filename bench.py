@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
+                         "used to scale the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -156,6 +159,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 3}), flush=True)
+        return
     wl = synth.WORKLOADS[args.workload]
     inp = synth.make_inputs(wl)
     t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}

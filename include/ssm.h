@@ -101,7 +101,7 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
  *            but must not otherwise overlap an input or y
  *   workspace, workspace_bytes: device scratch of at least
  *            ssm_scan_fwd_workspace_bytes(...) bytes (NULL allowed when 0)
- * Supported sizes: batch <= 65535, seqlen <= 2^30, dstate in {1, 2, 4, 8, 16}.
+ * Supported sizes: batch <= 65535, seqlen <= 2^28 - 4096, dstate in {1, 2, 4, 8, 16}.
  */
 ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
                           unsigned flags, const void *x, const void *dt, const float *dt_bias,

@@ -9,9 +9,13 @@
 // with the state expansion kept on chip ("Hardware-aware state expansion"):
 // only y and the final state are written to HBM.
 //
-// Work split.  A workgroup of 4 waves owns one batch row and 16 channels.
-// Each 16-lane DPP row of a wave owns one channel; lane j of the row owns the
-// K consecutive timesteps [l0 + jK, l0 + jK + K) of a chunk of 16K timesteps.
+// Work split.  A workgroup of kWaves waves owns one batch row and 4 kWaves
+// channels.  Each 16-lane DPP row of a wave owns one channel; lane j of the
+// row owns the K consecutive timesteps [l0 + jK, l0 + jK + K) of a chunk of
+// 16K timesteps.  K = 8 keeps the kernel at <= 128 VGPRs and ~36 KB of LDS
+// per 4-wave workgroup, i.e. four waves per SIMD; a single wave issues VALU
+// work far below the SIMD's rate, so the scan needs the occupancy more than
+// it needs longer per-lane runs.
 // The workgroup walks the sequence chunk by chunk.  For each state n:
 //   1. each lane folds its K steps into one affine map h -> a h + b
 //      (a = exp2(A' sum Delta), b by a K-step fma chain),
@@ -30,10 +34,29 @@
 namespace ssm {
 namespace {
 
+// Tuning constants (overridable at build time for sweeps).
+#ifndef SSM_SCAN_WAVES
+#define SSM_SCAN_WAVES 4
+#endif
+#ifndef SSM_SCAN_K
+#define SSM_SCAN_K 8
+#endif
+#ifndef SSM_SCAN_MINW_BF16
+#define SSM_SCAN_MINW_BF16 4
+#endif
+#ifndef SSM_SCAN_MINW_F32
+#define SSM_SCAN_MINW_F32 4
+#endif
 constexpr int kRow = 16;                    // lanes per channel (one DPP row)
-constexpr int kWaves = 4;                   // waves per workgroup
+constexpr int kWaves = SSM_SCAN_WAVES;      // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChannels = kThreads / kRow;  // channels per workgroup
+constexpr int kK = SSM_SCAN_K;              // consecutive timesteps per lane
+// Occupancy target (waves per SIMD): 4, which is also what the ~36 KB of LDS
+// per 4-wave workgroup allows (4 workgroups per CU).  More resident waves
+// were measured not to help: the state loop runs near the VALU issue limit.
+template <typename Tin>
+constexpr int kMinWavesPerSimd = sizeof(Tin) == 2 ? SSM_SCAN_MINW_BF16 : SSM_SCAN_MINW_F32;
 
 struct ScanParams {
     int dim, seqlen;
@@ -52,19 +75,30 @@ __device__ inline bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() would also wait
+// for every outstanding global load and store of the wave (s_waitcnt vmcnt),
+// which here would cut the prefetch of the next chunk short at each chunk
+// boundary.  Waves exchange data only through LDS, so LDS ordering suffices.
+__device__ inline void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive scan of affine maps h -> a h + b over the 16 lanes of each DPP
-// row, then the state at the end (hend) and at the start (hin) of every
-// lane's block given the state `carry` entering the chunk.  Level s combines
+// row, then the state at the end (hend) and at the start (h) of every lane's
+// block given the state entering the chunk (passed in h).  Level s combines
 // lane j with lane j - s, whose map covers earlier steps and is applied
 // first: (a, b) <- (a_{j-s} a, b_{j-s} a + b).  Lanes with no partner inside
 // the row are left unwritten (bound_ctrl off), i.e. combined with the
-// identity map.  Lane 0 of each row keeps hin = carry.
+// identity map.  Lane 0 of each row keeps the carry as its start state.
 // Each v_*_dpp reads its DPP source at least two wait states after that
 // register was last written (the GFX9 VALU-write -> DPP-read hazard), hence
 // the s_nop padding.  All 64 lanes must be active.
-__device__ inline void row_scan(float &a, float &b, float carry, float &hend, float &hin)
+__device__ inline void row_scan(float &a, float &b, float &hend, float &h)
 {
-    hin = carry;
+    // on entry h holds the carry; v_fma reads it before v_mov_dpp overwrites it
     asm volatile(
         "s_nop 1\n\t"
         "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
@@ -78,11 +112,10 @@ __device__ inline void row_scan(float &a, float &b, float carry, float &hend, fl
         "s_nop 0\n\t"
         "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
         "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fma_f32 %2, %0, %4, %1\n\t"
+        "v_fma_f32 %2, %0, %3, %1\n\t"
         "s_nop 1\n\t"
         "v_mov_b32_dpp %3, %2 row_shr:1 row_mask:0xf bank_mask:0xf"
-        : "+v"(a), "+v"(b), "=&v"(hend), "+v"(hin)
-        : "v"(carry));
+        : "+v"(a), "+v"(b), "=&v"(hend), "+v"(h));
 }
 
 template <typename Tout, int K>
@@ -94,7 +127,7 @@ __device__ inline void store_y(Tout *dst, bool vec, int count, const float *v)
 #pragma unroll
             for (int i = 0; i < K / 4; ++i) {
                 f32x4 w = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
-                __builtin_nontemporal_store(w, q + i);
+                q[i] = w;
             }
         } else {
 #pragma unroll
@@ -111,7 +144,7 @@ __device__ inline void store_y(Tout *dst, bool vec, int count, const float *v)
                 w.y = pack_bf16x2(v[8 * i + 2], v[8 * i + 3]);
                 w.z = pack_bf16x2(v[8 * i + 4], v[8 * i + 5]);
                 w.w = pack_bf16x2(v[8 * i + 6], v[8 * i + 7]);
-                __builtin_nontemporal_store(w, q + i);
+                q[i] = w;
             }
         } else {
             uint16_t *s = reinterpret_cast<uint16_t *>(dst);
@@ -122,24 +155,42 @@ __device__ inline void store_y(Tout *dst, bool vec, int count, const float *v)
     }
 }
 
+// Global access through a wave-uniform base and a 32-bit per-lane byte
+// offset, so that only one VGPR per access stream is spent on addressing.
+template <typename T>
+__device__ inline const T *at(const T *base, uint32_t byte_off)
+{
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+template <typename T>
+__device__ inline T *at(T *base, uint32_t byte_off)
+{
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + byte_off);
+}
+
 template <typename Tin, typename Tout, int N, int K>
-__global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p)
+__global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kernel(ScanParams p)
 {
     static_assert(K % 8 == 0, "K must be a multiple of 8");
     static_assert(N * kRow <= kThreads, "one staging slot per thread");
     constexpr int T = kRow * K;  // timesteps per chunk
     constexpr int Q = K / 4;     // float4 per lane per state
+    constexpr int NP = N + 1;    // per-channel stride of sA / sCarry (one pad entry)
 
     // Bm/Cm chunk in LDS, fp32, layout [n][q][lane j] of float4 so that the
     // 16 lanes of a row read 256 contiguous bytes per ds_read_b128.
-    __shared__ float4 sB[2][N * Q * kRow];
+    // sB has one spare state so the look-ahead load of the last state stays
+    // inside the array.
+    __shared__ float4 sB[2][(N + 1) * Q * kRow];
     __shared__ float4 sC[2][N * Q * kRow];
-    __shared__ float sA[kChannels * N];      // A * log2(e)
-    __shared__ float sCarry[kChannels * N];  // state entering the current chunk
+    // Per channel: NP entries of A * log2(e), then NP entries of the state
+    // entering the current chunk.
+    __shared__ float sAC[kChannels * 2 * NP];
 
     const int tid = threadIdx.x;
     const int j = tid & (kRow - 1);
-    const int c = tid / kRow;
+    const int c = tid / kRow;                 // channel within the workgroup
+    const int cw = c & 3;                     // channel within the wave
     const int b = blockIdx.y;
     const int dim = p.dim;
     const int L = p.seqlen;
@@ -147,111 +198,151 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p)
     const bool live = d < dim;
     const int dc = live ? d : dim - 1;
 
-    const size_t row = (size_t(b) * dim + dc) * size_t(L);
-    const Tin *xr = static_cast<const Tin *>(p.x) + row;
-    const Tin *dtr = static_cast<const Tin *>(p.dt) + row;
-    const Tin *zr = p.z ? static_cast<const Tin *>(p.z) + row : nullptr;
+    // Wave-uniform row base (its first channel, clamped) and per-lane offset.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int d0 = min(int(blockIdx.x) * kChannels + wave * 4, dim - 1);
+    const size_t row0 = (size_t(b) * dim + d0) * size_t(L);
+    const Tin *xw = static_cast<const Tin *>(p.x) + row0;
+    const Tin *dtw = static_cast<const Tin *>(p.dt) + row0;
+    const Tin *zw = p.z ? static_cast<const Tin *>(p.z) + row0 : nullptr;
+    Tout *yw = static_cast<Tout *>(p.y) + row0;
+    const uint32_t lane_row = uint32_t(dc - d0) * uint32_t(L);  // elements
     const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * N * L;
     const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * N * L;
+    // Wave-uniform: every row of every streamed tensor starts on a 16-byte
+    // boundary, so all runs of a chunk that lies inside the sequence can use
+    // unguarded 16-byte vector accesses.
+    const bool rows_vec = aligned16(p.x) && aligned16(p.dt) && (!p.z || aligned16(p.z)) &&
+                          aligned16(p.y) && aligned16(p.Bm) && aligned16(p.Cm) &&
+                          (size_t(L) * sizeof(Tin)) % 16 == 0 && (size_t(L) * sizeof(Tout)) % 16 == 0;
+    auto chunk_full = [&](int chunk) { return rows_vec && (chunk + 1) * T <= L; };
 
-    for (int s = tid; s < kChannels * N; s += kThreads) {
-        const int cc = s / N, n = s % N;
+    for (int s = tid; s < kChannels * NP; s += kThreads) {
+        const int cc = s / NP, n = s % NP;
         const int dd = min(int(blockIdx.x) * kChannels + cc, dim - 1);
-        sA[s] = p.A[size_t(dd) * N + n] * kLog2e;
+        sAC[cc * 2 * NP + n] = (n < N) ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
     }
     if (j == 0) {
 #pragma unroll
         for (int n = 0; n < N; ++n)
-            sCarry[c * N + n] = p.h0 ? p.h0[(size_t(b) * dim + dc) * N + n] : 0.0f;
+            sAC[c * 2 * NP + NP + n] = p.h0 ? p.h0[(size_t(b) * dim + dc) * N + n] : 0.0f;
+        sAC[c * 2 * NP + NP + N] = 0.0f;
     }
-    const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
-    const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
 
-    // staging slot of this thread: state sn, lane block sj
+    // Staging slot of this thread: state sn, lane block sj (threads < N*16).
     const bool stager = tid < N * kRow;
-    const int sn = tid / kRow, sj = tid % kRow;
+    const int sn = stager ? tid / kRow : 0, sj = tid % kRow;
     raw_run<Tin, K> stB, stC;
-    auto stage_load = [&](int chunk) {
+    auto stage_load = [&](const Tin *src, int chunk, raw_run<Tin, K> &st) {
         const int l = chunk * T + sj * K;
-        const int cnt = max(0, min(K, L - l));
-        const Tin *pb = Bb + size_t(sn) * L + l;
-        const Tin *pc = Cb + size_t(sn) * L + l;
-        load_raw<Tin, K>(pb, cnt == K && aligned16(pb), cnt, stB);
-        load_raw<Tin, K>(pc, cnt == K && aligned16(pc), cnt, stC);
-    };
-    auto stage_store = [&](int buf) {
-        float vb[K], vc[K];
-        decode_raw<Tin, K>(stB, vb);
-        decode_raw<Tin, K>(stC, vc);
-#pragma unroll
-        for (int q = 0; q < Q; ++q) {
-            sB[buf][(sn * Q + q) * kRow + sj] =
-                make_float4(vb[4 * q], vb[4 * q + 1], vb[4 * q + 2], vb[4 * q + 3]);
-            sC[buf][(sn * Q + q) * kRow + sj] =
-                make_float4(vc[4 * q], vc[4 * q + 1], vc[4 * q + 2], vc[4 * q + 3]);
+        const Tin *q = src + size_t(sn) * size_t(L) + l;
+        if (chunk_full(chunk)) {
+            load_raw<Tin, K>(q, true, K, st);
+        } else {
+            const int cnt = max(0, min(K, L - l));
+            load_raw<Tin, K>(q, cnt == K && aligned16(q), cnt, st);
         }
+    };
+    auto stage_store = [&](float4 *dst, const raw_run<Tin, K> &st) {
+        float v[K];
+        decode_raw<Tin, K>(st, v);
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            dst[(sn * Q + q) * kRow + sj] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     };
 
     raw_run<Tin, K> rx, rdt, rz;
-    auto xdz_load = [&](int chunk) {
+    auto xd_load = [&](int chunk) {
         const int l = chunk * T + j * K;
-        const int cnt = max(0, min(K, L - l));
-        const bool vec = cnt == K && aligned16(xr + l) && aligned16(dtr + l);
-        load_raw<Tin, K>(xr + l, vec, cnt, rx);
-        load_raw<Tin, K>(dtr + l, vec, cnt, rdt);
-        if (zr) load_raw<Tin, K>(zr + l, cnt == K && aligned16(zr + l), cnt, rz);
+        const uint32_t off = (lane_row + uint32_t(l)) * uint32_t(sizeof(Tin));
+        const Tin *qx = at(xw, off), *qd = at(dtw, off);
+        if (chunk_full(chunk)) {
+            load_raw<Tin, K>(qx, true, K, rx);
+            load_raw<Tin, K>(qd, true, K, rdt);
+        } else {
+            const int cnt = max(0, min(K, L - l));
+            const bool vec = cnt == K && aligned16(qx) && aligned16(qd);
+            load_raw<Tin, K>(qx, vec, cnt, rx);
+            load_raw<Tin, K>(qd, vec, cnt, rdt);
+        }
+    };
+    auto z_load = [&](int chunk, uint32_t off) {
+        const Tin *qz = at(zw, off);
+        if (chunk_full(chunk)) {
+            load_raw<Tin, K>(qz, true, K, rz);
+        } else {
+            const int cnt = max(0, min(K, L - (chunk * T + j * K)));
+            load_raw<Tin, K>(qz, cnt == K && aligned16(qz), cnt, rz);
+        }
     };
 
     const int nchunks = (L + T - 1) / T;
     if (stager) {
-        stage_load(0);
-        stage_store(0);
+        stage_load(Bb, 0, stB);
+        stage_load(Cb, 0, stC);
+        stage_store(sB[0], stB);
+        stage_store(sC[0], stC);
     }
-    xdz_load(0);
-    __syncthreads();
+    xd_load(0);
+    lds_barrier();
+
+    float *aptr = sAC + c * 2 * NP;  // A' at aptr[n], carry at aptr[NP + n]
 
     for (int ch = 0; ch < nchunks; ++ch) {
         const int buf = ch & 1;
         const int l0 = ch * T + j * K;
         const int cnt = max(0, min(K, L - l0));
+        const uint32_t yoff = (lane_row + uint32_t(l0)) * uint32_t(sizeof(Tin));
 
         // Delta, Delta*x and the skip term for this lane's K steps; steps past
         // the end of the sequence get Delta = 0 (identity map: a = 1, b = 0).
+        const bool full = chunk_full(ch);
         float delta[K], u[K], yv[K];
         float sumd = 0.0f;
+        const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+        const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-            const float xv = decode_raw_at<Tin, K>(rx, i);
-            const float dv = softplus(decode_raw_at<Tin, K>(rdt, i) + bias);
-            const bool in = i < cnt;
-            delta[i] = in ? dv : 0.0f;
-            u[i] = in ? dv * xv : 0.0f;
-            yv[i] = skip * xv;
-            sumd += delta[i];
+            for (int i = 0; i < K; ++i) {
+                const float xv = decode_raw_at<Tin, K>(rx, i);
+                delta[i] = softplus(decode_raw_at<Tin, K>(rdt, i) + bias);
+                u[i] = delta[i] * xv;
+                yv[i] = skip * xv;
+                sumd += delta[i];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const float xv = decode_raw_at<Tin, K>(rx, i);
+                const float dv = softplus(decode_raw_at<Tin, K>(rdt, i) + bias);
+                const bool in = i < cnt;
+                delta[i] = in ? dv : 0.0f;
+                u[i] = in ? dv * xv : 0.0f;
+                yv[i] = skip * xv;
+                sumd += delta[i];
+            }
         }
-        raw_run<Tin, K> zc;
-        if (zr) zc = rz;
-        if (ch + 1 < nchunks) {
-            xdz_load(ch + 1);
-            if (stager) stage_load(ch + 1);
-        }
+        const bool more = ch + 1 < nchunks;
 
-        // LDS operands of state n are loaded one iteration ahead.
-        auto load_state = [&](int n, float *v, const float4 *src) {
+        const float4 *bp = sB[buf] + j;
+        const float4 *cp = sC[buf] + j;
+        float bv[K];
+        auto load_b = [&](const float4 *src, float *v) {
 #pragma unroll
             for (int q = 0; q < Q; ++q) {
-                const float4 w = src[(n * Q + q) * kRow + j];
+                const float4 w = src[q * kRow];
                 v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
             }
         };
-        float bv[K];
-        load_state(0, bv, sB[buf]);
-        float ap = sA[c * N];
-        float carry = sCarry[c * N];
-#pragma unroll 1
-        for (int n = 0; n < N; ++n) {
+        load_b(bp, bv);
+        float ap = aptr[0];
+        float carry = aptr[NP];
+
+        // One state: local fold, row scan, carry update and replay.
+        auto state_step = [&](int n) {
             float cv[K];
-            load_state(n, cv, sC[buf]);
+            load_b(cp, cv);
+            cp += Q * kRow;
             float dA[K], bb[K];
 #pragma unroll
             for (int i = 0; i < K; ++i) {
@@ -262,42 +353,82 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(ScanParams p)
 #pragma unroll
             for (int i = 1; i < K; ++i) hl = __builtin_fmaf(dA[i], hl, bb[i]);
             float aa = exp2_hw(sumd * ap);
-            float hend, h;
-            row_scan(aa, hl, carry, hend, h);
-            if (j == kRow - 1) sCarry[c * N + n] = hend;
-            const int nn = (n + 1 < N) ? n + 1 : n;
-            load_state(nn, bv, sB[buf]);
-            ap = sA[c * N + nn];
-            carry = sCarry[c * N + nn];
+            float hend, h = carry;
+            row_scan(aa, hl, hend, h);
+            if (j == kRow - 1) aptr[NP + n] = hend;
+            bp += Q * kRow;
+            load_b(bp, bv);          // next state's B (one past the end on the last state)
+            ap = aptr[n + 1];
+            carry = aptr[NP + n + 1];
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 h = __builtin_fmaf(dA[i], h, bb[i]);
                 yv[i] = __builtin_fmaf(cv[i], h, yv[i]);
             }
+        };
+
+        // The loads in flight are spread over thirds of the states so that
+        // few of them hold registers at once: the next chunk's Bm and Cm are
+        // staged during the first third; this chunk's z and the next chunk's
+        // x and dt are fetched during the last third.
+        if constexpr (N >= 8) {
+            constexpr int N1 = (N + 2) / 3, N2 = N - (N + 2) / 3;
+            if (more && stager) {
+                stage_load(Bb, ch + 1, stB);
+                stage_load(Cb, ch + 1, stC);
+            }
+#pragma unroll 1
+            for (int n = 0; n < N1; ++n) state_step(n);
+            if (more && stager) {
+                stage_store(sB[buf ^ 1], stB);
+                stage_store(sC[buf ^ 1], stC);
+            }
+#pragma unroll 1
+            for (int n = N1; n < N2; ++n) state_step(n);
+            if (zw) z_load(ch, yoff);
+            if (more) xd_load(ch + 1);
+#pragma unroll 1
+            for (int n = N2; n < N; ++n) state_step(n);
+        } else {
+            // few states: everything is fetched up front
+            if (more && stager) {
+                stage_load(Bb, ch + 1, stB);
+                stage_load(Cb, ch + 1, stC);
+            }
+            if (zw) z_load(ch, yoff);
+            if (more) xd_load(ch + 1);
+#pragma unroll 1
+            for (int n = 0; n < N; ++n) state_step(n);
+            if (more && stager) {
+                stage_store(sB[buf ^ 1], stB);
+                stage_store(sC[buf ^ 1], stC);
+            }
         }
 
-        if (zr) {
+        if (zw) {
 #pragma unroll
-            for (int i = 0; i < K; ++i) yv[i] *= silu(decode_raw_at<Tin, K>(zc, i));
+            for (int i = 0; i < K; ++i) yv[i] *= silu(decode_raw_at<Tin, K>(rz, i));
         }
-        if (live && cnt > 0) {
-            Tout *yr = static_cast<Tout *>(p.y) + row + l0;
-            store_y<Tout, K>(yr, cnt == K && aligned16(yr), cnt, yv);
+        if (live) {
+            Tout *yr = at(yw, uint32_t((lane_row + uint32_t(l0)) * sizeof(Tout)));
+            if (full)
+                store_y<Tout, K>(yr, true, K, yv);
+            else if (cnt > 0)
+                store_y<Tout, K>(yr, cnt == K && aligned16(yr), cnt, yv);
         }
-        if (ch + 1 < nchunks && stager) stage_store(buf ^ 1);
-        __syncthreads();
+        lds_barrier();
     }
 
     if (p.hL && live && j == 0) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) p.hL[(size_t(b) * dim + d) * N + n] = sCarry[c * N + n];
+        for (int n = 0; n < N; ++n) p.hL[(size_t(b) * dim + d) * N + n] = aptr[NP + n];
     }
 }
 
 template <typename Tin, typename Tout, int N>
 hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
 {
-    constexpr int K = 16;
+    constexpr int K = kK;
     ScanParams p{a.dim, a.seqlen, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
                  a.Dskip, a.z, a.h0, a.y, a.hL};
     dim3 grid((a.dim + kChannels - 1) / kChannels, a.batch);

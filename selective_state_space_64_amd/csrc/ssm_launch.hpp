@@ -37,8 +37,9 @@ hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream);
 
 // Largest batch the scan grid supports (grid y dimension).
 constexpr int kMaxBatch = 65535;
-// Longest sequence: keeps every in-kernel timestep index inside 32 bits.
-constexpr int kMaxSeqlen = 1 << 30;
+// Longest sequence: the scan addresses the 4 rows of a wave with 32-bit byte
+// offsets, (4 L + 2 chunks) * 4 bytes < 2^32.
+constexpr int kMaxSeqlen = (1 << 28) - (1 << 12);
 // Most (batch, channel) rows one decode launch covers (1-D grid of 256-lane blocks).
 constexpr long long kMaxDecodeRows = (1LL << 31) - 1;
 

@@ -63,7 +63,7 @@ def _call(b, **over):
 ERRORS = [
     ("null_x", dict(x=None), 1), ("null_A", dict(A=None), 1), ("null_y", dict(y=None), 1),
     ("batch0", dict(batch=0), 2), ("dim_neg", dict(dim=-1), 2), ("L0", dict(seqlen=0), 2),
-    ("batch_huge", dict(batch=70000), 2), ("L_huge", dict(seqlen=(1 << 30) + 1), 2),
+    ("batch_huge", dict(batch=70000), 2), ("L_huge", dict(seqlen=(1 << 28) - 4095), 2),
     ("in_dtype", dict(in_dtype=7), 3), ("out_dtype", dict(out_dtype=-1), 3),
     ("N3", dict(dstate=3), 6), ("N32", dict(dstate=32), 6), ("flag_zoh", dict(flags=1), 6),
     ("flag_other", dict(flags=0x80), 6),
