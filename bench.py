@@ -14,6 +14,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I]
        [--no-cpu-baseline] [--no-decode]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +40,29 @@ PEAK_HBM = 8.0e12                          # B/s
 #                 skip fma (1), silu = exp + add + rcp + mul (10), gate mul (1)
 SLOTS_PER_ELEM = 1 + TRANS_SLOTS + 1 + 1 + 1
 SLOTS_PER_ROW_STEP = 1 + (TRANS_SLOTS + 1 + TRANS_SLOTS) + 1 + 1 + (TRANS_SLOTS + 1 + TRANS_SLOTS + 1) + 1
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "scan_fwd_counters.json")
+KERNEL_SOURCES = ("selective_state_space_64_amd/csrc/scan_fwd.hip",
+                  "selective_state_space_64_amd/csrc/ssm_device.hpp")
+
+
+def counter_traffic(workload_name):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE
+    summary, or None when it was taken on other kernel sources or another
+    workload."""
+    try:
+        with open(COUNTERS) as f:
+            rec = json.load(f)
+        h = hashlib.sha256()
+        for src in KERNEL_SOURCES:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except OSError:
+        return None
+    if rec.get("kernel_sources_sha256") != h.hexdigest() or rec.get("workload") != workload_name:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def algorithmic_slots(batch, dim, L, N):
@@ -221,7 +245,7 @@ def main():
                       "median": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
         "hbm_gbps_algorithmic": nbytes / kern_s / 1e9,
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
-                     "frac": achieved / peak, "traffic": None,
+                     "frac": achieved / peak, "traffic": counter_traffic(wl.name),
                      "model": "fp32 VALU issue slots (transcendental = 4), %.4f slots/element algorithmic"
                               % (slots / elems),
                      "hbm": {"achieved": nbytes / kern_s / 1e9, "peak": PEAK_HBM / 1e9,
