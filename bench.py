@@ -54,15 +54,62 @@ def counter_traffic(workload_name):
     try:
         with open(COUNTERS) as f:
             rec = json.load(f)
-        h = hashlib.sha256()
-        for src in KERNEL_SOURCES:
-            with open(os.path.join(ROOT, src), "rb") as f:
-                h.update(f.read())
+        digest = kernel_sources_sha256()
     except OSError:
         return None
-    if rec.get("kernel_sources_sha256") != h.hexdigest() or rec.get("workload") != workload_name:
+    if rec.get("kernel_sources_sha256") != digest or rec.get("workload") != workload_name:
         return None
     return rec["traffic_bytes_per_launch"]
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def ingest_counters(fetch_dir, write_dir, copyf_dir, copyw_dir, copy_mib=256, workload=None):
+    """Per-dispatch mean of FETCH_SIZE / WRITE_SIZE (KiB) for the scan kernel,
+    scaled by what the same counters read for a plain device copy of copy_mib
+    MiB, written with the hash of the kernel sources they were taken on."""
+    import csv
+
+    def mean(d, counter, kernel):
+        vals = []
+        for root, _, files in os.walk(d):
+            for f in files:
+                if f.endswith("counter_collection.csv"):
+                    with open(os.path.join(root, f)) as fh:
+                        for r in csv.DictReader(fh):
+                            if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                                vals.append(float(r["Counter_Value"]))
+        if not vals:
+            raise SystemExit("no %s samples for %s under %s" % (counter, kernel, d))
+        return sum(vals) / len(vals)
+
+    copy_kib = copy_mib * 1024.0
+    fetch = mean(fetch_dir, "FETCH_SIZE", "scan_fwd_kernel")
+    write = mean(write_dir, "WRITE_SIZE", "scan_fwd_kernel")
+    cf = mean(copyf_dir, "FETCH_SIZE", "copyBuffer")
+    cw = mean(copyw_dir, "WRITE_SIZE", "copyBuffer")
+    fs, ws = copy_kib / cf, copy_kib / cw
+    rec = {
+        "kernel": "scan_fwd_kernel (bf16 in, fp32 out, N 16)",
+        "workload": workload,
+        "kernel_sources_sha256": kernel_sources_sha256(),
+        "fetch_size_kib_per_dispatch": fetch,
+        "write_size_kib_per_dispatch": write,
+        "copy_calibration": {"bytes_each_way": int(copy_kib * 1024), "fetch_size_kib": cf,
+                             "write_size_kib": cw, "fetch_scale": fs, "write_scale": ws},
+        "read_bytes_per_launch": fetch * fs * 1024,
+        "write_bytes_per_launch": write * ws * 1024,
+        "traffic_bytes_per_launch": (fetch * fs + write * ws) * 1024,
+    }
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
 
 
 def algorithmic_slots(batch, dim, L, N):
@@ -85,6 +132,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPYF_DIR", "COPYW_DIR"),
+                    help="write profiles/scan_fwd_counters.json from four rocprofv3 --pmc output "
+                         "directories (scan FETCH_SIZE, scan WRITE_SIZE, copy FETCH_SIZE, copy "
+                         "WRITE_SIZE; csv output) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -171,6 +222,11 @@ def bench_decode(torch, ssm, synth, steps_cap=256):
 
 def main():
     args = parse()
+    if args.ingest_counters:
+        from selective_state_space_64_amd import synth
+        rec = ingest_counters(*args.ingest_counters, workload=synth.WORKLOADS[args.workload].name)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: every box here has one GPU and the scan is "
               "benchmarked on a single device (--gpus %d is not supported)" % args.gpus,
@@ -252,6 +308,20 @@ def main():
                              "unit": "GB/s", "frac": nbytes / kern_s / PEAK_HBM,
                              "algorithmic_bytes": nbytes}},
     }
+    # exact zero-order-hold B-bar variant of the same step (SSM_FLAG_ZOH_B)
+    zev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(10)]
+    for _ in range(2):
+        ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                         Dskip=t["Dskip"], z=t["z"], y=y, hL=hL, zoh=True)
+    for a, b in zev:
+        a.record(stream)
+        ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
+                         Dskip=t["Dskip"], z=t["z"], y=y, hL=hL, zoh=True)
+        b.record(stream)
+    torch.cuda.synchronize()
+    zms = float(np.mean([a.elapsed_time(b) for a, b in zev]))
+    result["zoh_variant"] = {"kernel_ms_mean": zms, "elements_per_s": elems / (zms * 1e-3)}
     if not args.no_decode:
         result["decode"] = bench_decode(torch, ssm, synth)
     if not args.no_cpu_baseline:

@@ -15,7 +15,8 @@
  *                     only the contracted output and the final state are.
  *                     B-bar follows the simplified form dB = Delta * B of the
  *                     dynamic-parameterization section of the soft186.com page
- *                     "Mamba选择性状态空间机制：效率提升10倍的核心突破".
+ *                     "Mamba选择性状态空间机制：效率提升10倍的核心突破", or,
+ *                     with SSM_FLAG_ZOH_B, the exact zero-order-hold form.
  *                     Output: y = (C . h + Dskip * x) * silu(z), silu(z) =
  *                     z * sigmoid(z); a NULL z means no gate.
  *
@@ -65,13 +66,14 @@ typedef enum {
     SSM_ERR_BAD_DTYPE = 3,   /* in_dtype or out_dtype is not a value of ssm_dtype_t */
     SSM_ERR_MISALIGNED = 4,  /* a pointer below its element alignment (state: 16 B) */
     SSM_ERR_ALIAS = 5,       /* an output overlaps an input it must not overlap    */
-    SSM_ERR_UNSUPPORTED = 6, /* dstate not in {1,2,4,8,16}, or an unknown flag bit */
+    SSM_ERR_UNSUPPORTED = 6, /* dstate not in {1,2,4,8,16}, or an unknown flag bit   */
     SSM_ERR_WORKSPACE = 7,   /* workspace smaller than ssm_scan_fwd_workspace_bytes */
     SSM_ERR_HIP = 8          /* the HIP runtime rejected the launch                */
 } ssm_status_t;
 
-/* Reserved: exact zero-order-hold B-bar = (Delta A)^-1 (exp(Delta A) - 1) Delta B
- * from the "Method" section.  This version rejects it with SSM_ERR_UNSUPPORTED. */
+/* flags bit 0: use the exact zero-order-hold B-bar of the "Method" section,
+ * B-bar = (Delta A)^-1 (exp(Delta A) - 1) Delta B, instead of Delta B.
+ * Every other bit must be zero (SSM_ERR_UNSUPPORTED otherwise). */
 #define SSM_FLAG_ZOH_B 0x1u
 
 /* SSM_ABI_VERSION of the loaded library. */
@@ -117,7 +119,7 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
  *   Bm, Cm   [batch][dstate]        in_dtype
  *   Dskip    [dim] fp32 or NULL;  z [batch][dim] in_dtype or NULL
  *   y        [batch][dim]           out_dtype; must not overlap any input or state
- * Supported sizes: batch * dim < 2^31, dstate in {1, 2, 4, 8, 16}.
+ * Supported sizes: batch <= 65535, dstate in {1, 2, 4, 8, 16}.
  */
 ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
                               unsigned flags, float *state, const void *x, const void *dt,

@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_F32, SSM_BF16 = 0, 1
+SSM_FLAG_ZOH_B = 0x1
 STATUS = {
     0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_BAD_DTYPE",
     4: "SSM_ERR_MISALIGNED", 5: "SSM_ERR_ALIAS", 6: "SSM_ERR_UNSUPPORTED",
@@ -96,8 +97,9 @@ def _stream(stream, device):
 
 def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
                  out_dtype=torch.float32, return_final_state=True, y=None, hL=None,
-                 stream=None):
-    """Fused selective scan; returns (y, hL) (hL is None unless requested)."""
+                 zoh=False, stream=None):
+    """Fused selective scan; returns (y, hL) (hL is None unless requested).
+    zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -117,15 +119,17 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     ]
     yp = _ptr(y, "y", (batch, dim, L), out_dtype)
     hp = _ptr(hL, "hL", (batch, dim, N), f32)
-    st = lib().ssm_scan_fwd(batch, dim, L, N, _dtype_code(ind), 0, *args, _dtype_code(y.dtype),
+    flags = SSM_FLAG_ZOH_B if zoh else 0
+    st = lib().ssm_scan_fwd(batch, dim, L, N, _dtype_code(ind), flags, *args, _dtype_code(y.dtype),
                             yp, hp, None, 0, _stream(stream, x.device))
     _check(st)
     return y, hL
 
 
 def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None,
-                     out_dtype=torch.float32, y=None, stream=None):
-    """One decode step; updates `state` in place and returns y [batch, dim]."""
+                     out_dtype=torch.float32, y=None, zoh=False, stream=None):
+    """One decode step; updates `state` in place and returns y [batch, dim].
+    zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B)."""
     batch, dim, N = state.shape
     ind = x.dtype
     if y is None:
@@ -139,7 +143,8 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
         _ptr(Dskip, "Dskip", (dim,), f32), _ptr(z, "z", (batch, dim), ind),
     ]
     yp = _ptr(y, "y", (batch, dim), out_dtype)
-    st = lib().ssm_state_update(batch, dim, N, _dtype_code(ind), 0, *args, _dtype_code(y.dtype),
+    flags = SSM_FLAG_ZOH_B if zoh else 0
+    st = lib().ssm_state_update(batch, dim, N, _dtype_code(ind), flags, *args, _dtype_code(y.dtype),
                                 yp, _stream(stream, x.device))
     _check(st)
     return y

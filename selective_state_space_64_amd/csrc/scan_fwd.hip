@@ -6,6 +6,8 @@
 //     Delta_t = softplus(dt_t + dt_bias[d])
 //     h_t[n]  = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t Bm[b,n,t] x_t
 //     y_t     = (sum_n Cm[b,n,t] h_t[n] + Dskip[d] x_t) * silu(z_t)
+// (kZoh: the input term is the exact zero-order-hold B-bar of "Method",
+// phi(Delta_t A[d,n]) Delta_t Bm[b,n,t] x_t with phi(x) = (e^x - 1) / x.)
 // with the state expansion kept on chip ("Hardware-aware state expansion"):
 // only y and the final state are written to HBM.
 //
@@ -168,7 +170,7 @@ __device__ inline T *at(T *base, uint32_t byte_off)
     return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + byte_off);
 }
 
-template <typename Tin, typename Tout, int N, int K>
+template <typename Tin, typename Tout, int N, int K, bool kZoh>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kernel(ScanParams p)
 {
     static_assert(K % 8 == 0, "K must be a multiple of 8");
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         // the end of the sequence get Delta = 0 (identity map: a = 1, b = 0).
         const bool full = chunk_full(ch);
         float delta[K], u[K], yv[K];
+        [[maybe_unused]] float invd[K];  // 1/Delta (exact-ZOH B-bar only)
         float sumd = 0.0f;
         const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
         const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
@@ -309,6 +312,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
                 u[i] = delta[i] * xv;
                 yv[i] = skip * xv;
                 sumd += delta[i];
+                if constexpr (kZoh) invd[i] = rcp_hw(delta[i]);
             }
         } else {
 #pragma unroll
@@ -320,6 +324,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
                 u[i] = in ? dv * xv : 0.0f;
                 yv[i] = skip * xv;
                 sumd += delta[i];
+                if constexpr (kZoh) invd[i] = in ? rcp_hw(dv) : 0.0f;
             }
         }
         const bool more = ch + 1 < nchunks;
@@ -344,10 +349,21 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             load_b(cp, cv);
             cp += Q * kRow;
             float dA[K], bb[K];
+            if constexpr (kZoh) {
+                // exact zero-order hold: B-bar x = phi(Delta A) Delta B x
+                const float inva = rcp_hw(ap) * kLog2e;  // 1/A
 #pragma unroll
-            for (int i = 0; i < K; ++i) {
-                dA[i] = exp2_hw(delta[i] * ap);
-                bb[i] = u[i] * bv[i];
+                for (int i = 0; i < K; ++i) {
+                    const float t = delta[i] * ap;
+                    dA[i] = exp2_hw(t);
+                    bb[i] = (u[i] * bv[i]) * phi_zoh(t * kLn2, dA[i], invd[i] * inva);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < K; ++i) {
+                    dA[i] = exp2_hw(delta[i] * ap);
+                    bb[i] = u[i] * bv[i];
+                }
             }
             float hl = bb[0];
 #pragma unroll
@@ -425,28 +441,34 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     }
 }
 
-template <typename Tin, typename Tout, int N>
+template <typename Tin, typename Tout, int N, bool kZoh>
 hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
 {
     constexpr int K = kK;
     ScanParams p{a.dim, a.seqlen, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
                  a.Dskip, a.z, a.h0, a.y, a.hL};
     dim3 grid((a.dim + kChannels - 1) / kChannels, a.batch);
-    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename Tin, typename Tout>
+template <typename Tin, typename Tout, bool kZoh>
 hipError_t launch_n(const ScanArgs &a, hipStream_t stream)
 {
     switch (a.dstate) {
-    case 1: return launch_typed<Tin, Tout, 1>(a, stream);
-    case 2: return launch_typed<Tin, Tout, 2>(a, stream);
-    case 4: return launch_typed<Tin, Tout, 4>(a, stream);
-    case 8: return launch_typed<Tin, Tout, 8>(a, stream);
-    case 16: return launch_typed<Tin, Tout, 16>(a, stream);
+    case 1: return launch_typed<Tin, Tout, 1, kZoh>(a, stream);
+    case 2: return launch_typed<Tin, Tout, 2, kZoh>(a, stream);
+    case 4: return launch_typed<Tin, Tout, 4, kZoh>(a, stream);
+    case 8: return launch_typed<Tin, Tout, 8, kZoh>(a, stream);
+    case 16: return launch_typed<Tin, Tout, 16, kZoh>(a, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_mode(const ScanArgs &a, hipStream_t stream)
+{
+    return a.zoh ? launch_n<Tin, Tout, true>(a, stream) : launch_n<Tin, Tout, false>(a, stream);
 }
 
 }  // namespace
@@ -454,9 +476,10 @@ hipError_t launch_n(const ScanArgs &a, hipStream_t stream)
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t stream)
 {
     if (a.in_bf16) {
-        return a.out_bf16 ? launch_n<bf16_t, bf16_t>(a, stream) : launch_n<bf16_t, float>(a, stream);
+        return a.out_bf16 ? launch_mode<bf16_t, bf16_t>(a, stream)
+                          : launch_mode<bf16_t, float>(a, stream);
     }
-    return a.out_bf16 ? launch_n<float, bf16_t>(a, stream) : launch_n<float, float>(a, stream);
+    return a.out_bf16 ? launch_mode<float, bf16_t>(a, stream) : launch_mode<float, float>(a, stream);
 }
 
 }  // namespace ssm

@@ -59,7 +59,7 @@ const char *ssm_status_string(ssm_status_t s)
     case SSM_ERR_BAD_DTYPE: return "in_dtype/out_dtype must be SSM_F32 or SSM_BF16";
     case SSM_ERR_MISALIGNED: return "a pointer is not aligned to its element size (state: 16 bytes)";
     case SSM_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
-    case SSM_ERR_UNSUPPORTED: return "unsupported dstate (use 1, 2, 4, 8 or 16) or flag bit";
+    case SSM_ERR_UNSUPPORTED: return "unsupported dstate (use 1, 2, 4, 8 or 16) or unknown flag bit";
     case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_fwd_workspace_bytes";
     case SSM_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     }
@@ -82,7 +82,7 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
         return SSM_ERR_BAD_SHAPE;
-    if (!valid_dstate(dstate) || flags != 0) return SSM_ERR_UNSUPPORTED;
+    if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_ZOH_B) != 0) return SSM_ERR_UNSUPPORTED;
 
     const size_t seq_elems = mul3(batch, dim, seqlen);
     const size_t bc_elems = mul3(batch, dstate, seqlen);
@@ -119,7 +119,7 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
     (void)workspace;
 
     ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
-                    x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL};
+                    (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL};
     const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
@@ -133,10 +133,10 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
     if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1) return SSM_ERR_BAD_SHAPE;
-    if (!valid_dstate(dstate) || flags != 0) return SSM_ERR_UNSUPPORTED;
+    if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_ZOH_B) != 0) return SSM_ERR_UNSUPPORTED;
 
     const size_t rows = mul3(batch, dim, 1);
-    if (rows > ssm::kMaxDecodeRows) return SSM_ERR_BAD_SHAPE;
+    if (batch > ssm::kMaxBatch) return SSM_ERR_BAD_SHAPE;
     const size_t st_elems = mul3(batch, dim, dstate);
     if (!rows || !st_elems) return SSM_ERR_BAD_SHAPE;
 
@@ -168,7 +168,7 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
     if (overlaps(y, ybytes, state, sbytes)) return SSM_ERR_ALIAS;
 
     ssm::UpdateArgs a{batch, dim, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
-                      state, x, dt, dt_bias, A, Bm, Cm, Dskip, z, y};
+                      (flags & SSM_FLAG_ZOH_B) != 0, state, x, dt, dt_bias, A, Bm, Cm, Dskip, z, y};
     const hipError_t e = ssm::launch_state_update(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -172,6 +172,22 @@ __device__ inline float silu(float z)
     return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
 }
 
+// phi(x) = (e^x - 1) / x, the factor that turns Delta*B into the exact
+// zero-order-hold B-bar = (Delta A)^-1 (exp(Delta A) - 1) Delta B = phi(Delta A) Delta B.
+// `abar` = e^x (already computed for A-bar) and inv_x = 1/x.  For |x| < 1/16
+// the Taylor series to x^4 (truncation below 1e-9 relative) avoids the
+// cancellation in abar - 1; elsewhere (abar - 1) / x is accurate to ~1e-6.
+// The select keeps x = 0 (A = 0 or Delta = 0) finite: phi(0) = 1.
+__device__ inline float phi_zoh(float x, float abar, float inv_x)
+{
+    float p = __builtin_fmaf(x, 1.0f / 120.0f, 1.0f / 24.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 6.0f);
+    p = __builtin_fmaf(x, p, 0.5f);
+    p = __builtin_fmaf(x, p, 1.0f);
+    const float big = (abar - 1.0f) * inv_x;
+    return fabsf(x) < 0.0625f ? p : big;
+}
+
 // ---------------------------------------------------------------- DPP lane moves
 // dpp_ctrl encodings (GFX9 DPP): row_shr:s = 0x110 + s within a 16-lane row;
 // row_newbcast:k = 0x150 + k broadcasts lane k of each row to the whole row.

@@ -8,7 +8,7 @@ namespace ssm {
 
 struct ScanArgs {
     int batch, dim, seqlen, dstate;
-    int in_bf16, out_bf16;
+    int in_bf16, out_bf16, zoh;
     const void *x, *dt;
     const float *dt_bias, *A;
     const void *Bm, *Cm;
@@ -21,7 +21,7 @@ struct ScanArgs {
 
 struct UpdateArgs {
     int batch, dim, dstate;
-    int in_bf16, out_bf16;
+    int in_bf16, out_bf16, zoh;
     float *state;
     const void *x, *dt;
     const float *dt_bias, *A;
@@ -35,12 +35,10 @@ struct UpdateArgs {
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream);
 
-// Largest batch the scan grid supports (grid y dimension).
+// Largest batch the kernels' grids support (grid y dimension).
 constexpr int kMaxBatch = 65535;
 // Longest sequence: the scan addresses the 4 rows of a wave with 32-bit byte
 // offsets, (4 L + 2 chunks) * 4 bytes < 2^32.
 constexpr int kMaxSeqlen = (1 << 28) - (1 << 12);
-// Most (batch, channel) rows one decode launch covers (1-D grid of 256-lane blocks).
-constexpr long long kMaxDecodeRows = (1LL << 31) - 1;
 
 }  // namespace ssm

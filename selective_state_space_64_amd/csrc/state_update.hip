@@ -7,6 +7,8 @@
 //     Delta = softplus(dt + dt_bias[d])
 //     h[n]  = exp(Delta A[d,n]) h[n] + Delta Bm[b,n] x
 //     y     = (sum_n Cm[b,n] h[n] + Dskip[d] x) * silu(z)
+// (kZoh: the input term carries the exact zero-order-hold factor
+// phi(Delta A) = (e^{Delta A} - 1) / (Delta A).)
 //
 // The step is bound by moving the state (read + write, 2 x 4N bytes per
 // (b, d)).  One lane owns one (b, d): its N states are one contiguous run of
@@ -48,26 +50,35 @@ __device__ inline void load_f32(const float *p, float *v)
     }
 }
 
-template <typename Tin, typename Tout, int N>
+template <typename Tin, typename Tout, int N, bool kZoh>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
 {
-    const long long idx = (long long)blockIdx.x * kThreads + threadIdx.x;
-    const long long rows = (long long)p.batch * p.dim;
-    if (idx >= rows) return;
-    const int b = int(idx / p.dim);
-    const int d = int(idx - (long long)b * p.dim);
+    // Grid: x over channel blocks, y over the batch, so the batch row (and
+    // with it Bm, Cm) is uniform across the workgroup.
+    const int b = blockIdx.y;
+    const int d = blockIdx.x * kThreads + threadIdx.x;
+    if (d >= p.dim) return;
+    const size_t idx = size_t(b) * p.dim + d;
 
-    float h[N], a[N], bm[N], cm[N];
-    float *st = p.state + idx * N;
-    load_f32<N>(st, h);
-#pragma unroll
-    for (int n = 0; n < N; ++n) a[n] = p.A[size_t(d) * N + n];
+    // Bm and Cm of this sequence: uniform, read once per wave.
     const Tin *Bp = static_cast<const Tin *>(p.Bm) + size_t(b) * N;
     const Tin *Cp = static_cast<const Tin *>(p.Cm) + size_t(b) * N;
+    float bm[N], cm[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) {
         bm[n] = io<Tin>::load1(Bp + n);
         cm[n] = io<Tin>::load1(Cp + n);
+    }
+
+    float h[N], a[N];
+    float *st = p.state + idx * N;
+    load_f32<N>(st, h);
+    const float *Ap = p.A + size_t(d) * N;
+    if (N % 4 == 0 && (reinterpret_cast<uintptr_t>(p.A) & 15u) == 0) {
+        load_f32<N>(Ap, a);
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) a[n] = Ap[n];
     }
     const float xv = io<Tin>::load1(static_cast<const Tin *>(p.x) + idx);
     const float dtv = io<Tin>::load1(static_cast<const Tin *>(p.dt) + idx);
@@ -76,11 +87,16 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
 
     const float delta = softplus(dtv + bias);
     const float u = delta * xv;
+    const float dl = delta * kLog2e;
     float acc = skip * xv;
+    [[maybe_unused]] const float invd = rcp_hw(delta);
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-        const float dA = exp2_hw(delta * (a[n] * kLog2e));
-        h[n] = __builtin_fmaf(dA, h[n], u * bm[n]);
+        const float t = dl * a[n];
+        const float dA = exp2_hw(t);
+        float bterm = u * bm[n];
+        if constexpr (kZoh) bterm *= phi_zoh(t * kLn2, dA, invd * rcp_hw(a[n]));
+        h[n] = __builtin_fmaf(dA, h[n], bterm);
         acc = __builtin_fmaf(cm[n], h[n], acc);
     }
     if (p.z) acc *= silu(io<Tin>::load1(static_cast<const Tin *>(p.z) + idx));
@@ -103,29 +119,33 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
     }
 }
 
-template <typename Tin, typename Tout, int N>
+template <typename Tin, typename Tout, int N, bool kZoh>
 hipError_t launch_typed(const UpdateArgs &a, hipStream_t stream)
 {
     UpdateParams p{a.batch, a.dim, a.state, a.x, a.dt, a.dt_bias, a.A,
                    a.Bm, a.Cm, a.Dskip, a.z, a.y};
-    const long long rows = (long long)a.batch * a.dim;
-    const unsigned blocks = unsigned((rows + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL((state_update_kernel<Tin, Tout, N>), dim3(blocks), dim3(kThreads), 0,
-                       stream, p);
+    dim3 grid((a.dim + kThreads - 1) / kThreads, a.batch);
+    hipLaunchKernelGGL((state_update_kernel<Tin, Tout, N, kZoh>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename Tin, typename Tout>
+template <typename Tin, typename Tout, bool kZoh>
 hipError_t launch_n(const UpdateArgs &a, hipStream_t stream)
 {
     switch (a.dstate) {
-    case 1: return launch_typed<Tin, Tout, 1>(a, stream);
-    case 2: return launch_typed<Tin, Tout, 2>(a, stream);
-    case 4: return launch_typed<Tin, Tout, 4>(a, stream);
-    case 8: return launch_typed<Tin, Tout, 8>(a, stream);
-    case 16: return launch_typed<Tin, Tout, 16>(a, stream);
+    case 1: return launch_typed<Tin, Tout, 1, kZoh>(a, stream);
+    case 2: return launch_typed<Tin, Tout, 2, kZoh>(a, stream);
+    case 4: return launch_typed<Tin, Tout, 4, kZoh>(a, stream);
+    case 8: return launch_typed<Tin, Tout, 8, kZoh>(a, stream);
+    case 16: return launch_typed<Tin, Tout, 16, kZoh>(a, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_mode(const UpdateArgs &a, hipStream_t stream)
+{
+    return a.zoh ? launch_n<Tin, Tout, true>(a, stream) : launch_n<Tin, Tout, false>(a, stream);
 }
 
 }  // namespace
@@ -133,9 +153,10 @@ hipError_t launch_n(const UpdateArgs &a, hipStream_t stream)
 hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream)
 {
     if (a.in_bf16) {
-        return a.out_bf16 ? launch_n<bf16_t, bf16_t>(a, stream) : launch_n<bf16_t, float>(a, stream);
+        return a.out_bf16 ? launch_mode<bf16_t, bf16_t>(a, stream)
+                          : launch_mode<bf16_t, float>(a, stream);
     }
-    return a.out_bf16 ? launch_n<float, bf16_t>(a, stream) : launch_n<float, float>(a, stream);
+    return a.out_bf16 ? launch_mode<float, bf16_t>(a, stream) : launch_mode<float, float>(a, stream);
 }
 
 }  // namespace ssm

@@ -65,8 +65,8 @@ ERRORS = [
     ("batch0", dict(batch=0), 2), ("dim_neg", dict(dim=-1), 2), ("L0", dict(seqlen=0), 2),
     ("batch_huge", dict(batch=70000), 2), ("L_huge", dict(seqlen=(1 << 28) - 4095), 2),
     ("in_dtype", dict(in_dtype=7), 3), ("out_dtype", dict(out_dtype=-1), 3),
-    ("N3", dict(dstate=3), 6), ("N32", dict(dstate=32), 6), ("flag_zoh", dict(flags=1), 6),
-    ("flag_other", dict(flags=0x80), 6),
+    ("N3", dict(dstate=3), 6), ("N32", dict(dstate=32), 6), ("flag_bit1", dict(flags=2), 6),
+    ("flag_other", dict(flags=0x81), 6),
 ]
 
 
@@ -124,7 +124,7 @@ def test_state_update_argument_errors():
     assert call(y=st.data_ptr()) == 5
     assert call(state=b["A"].data_ptr()) == 5
     assert call(N=5) == 6
-    assert call(flags=1) == 6
+    assert call(flags=2) == 6
     torch.cuda.synchronize()
     assert torch.equal(st, keep) and (y == 7.0).all()
     with pytest.raises(ssm.SSMError):
@@ -176,6 +176,7 @@ def test_validation_alignment_and_alias():
     assert _fake_call() == 8
     assert _fake_call(hL=_FAKE["h0"]) == 8                # hL == h0 exactly is allowed
     assert _fake_call(z=None, h0=None, hL=None, Dskip=None, dt_bias=None) == 8
+    assert _fake_call(flags=1) == 8  # SSM_FLAG_ZOH_B is accepted
 
 
 @no_gpu
@@ -202,5 +203,6 @@ def test_state_update_validation():
     assert call(y=_FAKE["h0"]) == 5
     assert call(state=_FAKE["A"]) == 5
     assert call(N=5) == 6
-    assert call(flags=1) == 6
+    assert call(flags=2) == 6
     assert call() == 8
+    assert call(flags=1) == 8  # SSM_FLAG_ZOH_B is accepted
