@@ -34,6 +34,11 @@ MUTANTS = {
     12: "softplus without its max(u, 0) branch",
     13: "ZOH B-bar without the 1/A factor",
     14: "last entry of the final state not returned",
+    15: "conv taps applied in reverse order",
+    16: "conv reads one step ahead (not causal)",
+    17: "initial conv state ignored",
+    18: "conv activation not applied",
+    19: "final conv state stored newest first",
 }
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -67,6 +72,10 @@ class Oracle:
         lib.ssm_oracle_scan_f64.argtypes = [ctypes.c_int] * 5 + [_dp] * 11 + [ctypes.c_int]
         lib.ssm_oracle_state_update_f64.restype = ctypes.c_int
         lib.ssm_oracle_state_update_f64.argtypes = [ctypes.c_int] * 4 + [_dp] * 10 + [ctypes.c_int]
+        lib.ssm_oracle_conv1d_f64.restype = ctypes.c_int
+        lib.ssm_oracle_conv1d_f64.argtypes = [ctypes.c_int] * 5 + [_dp] * 6 + [ctypes.c_int]
+        lib.ssm_oracle_conv1d_update_f64.restype = ctypes.c_int
+        lib.ssm_oracle_conv1d_update_f64.argtypes = [ctypes.c_int] * 4 + [_dp] * 5 + [ctypes.c_int]
         lib.ssm_oracle_mutant_id.restype = ctypes.c_int
         self._lib = lib
         self.mutant = lib.ssm_oracle_mutant_id()
@@ -121,6 +130,45 @@ class Oracle:
             raise RuntimeError("oracle state update failed with code %d" % rc)
         return y, state
 
+    def conv1d(self, x, weight, bias=None, state0=None, silu=True, threads=None):
+        """Causal depthwise conv: y[batch,dim,L] and the final conv state
+        [batch,dim,W-1] (the last W-1 inputs of state0 followed by x)."""
+        x = np.asarray(x)
+        if x.ndim != 3:
+            raise ValueError("x must be [batch, dim, L]")
+        batch, dim, L = x.shape
+        weight = np.asarray(weight)
+        W = weight.shape[1]
+        x = _f64(x, (batch, dim, L), "x")
+        weight = _f64(weight, (dim, W), "weight")
+        bias = _f64(bias, (dim,), "bias")
+        state0 = _f64(state0, (batch, dim, W - 1), "state0")
+        y = np.empty((batch, dim, L), np.float64)
+        stateL = np.empty((batch, dim, W - 1), np.float64)
+        nt = threads or os.cpu_count() or 1
+        rc = self._lib.ssm_oracle_conv1d_f64(
+            batch, dim, L, W, 1 if silu else 0, _ptr(x), _ptr(weight), _ptr(bias), _ptr(state0),
+            _ptr(y), _ptr(stateL), int(nt))
+        if rc != 0:
+            raise RuntimeError("oracle conv1d failed with code %d" % rc)
+        return y, stateL
+
+    def conv1d_update(self, state, x, weight, bias=None, silu=True, threads=None):
+        """One decode step of the conv; returns (y[batch,dim], new_state)."""
+        state = np.array(state, dtype=np.float64, order="C", copy=True)
+        batch, dim, H = state.shape
+        x = _f64(x, (batch, dim), "x")
+        weight = _f64(weight, (dim, H + 1), "weight")
+        bias = _f64(bias, (dim,), "bias")
+        y = np.empty((batch, dim), np.float64)
+        nt = threads or os.cpu_count() or 1
+        rc = self._lib.ssm_oracle_conv1d_update_f64(
+            batch, dim, H + 1, 1 if silu else 0, _ptr(state), _ptr(x), _ptr(weight), _ptr(bias),
+            _ptr(y), int(nt))
+        if rc != 0:
+            raise RuntimeError("oracle conv1d update failed with code %d" % rc)
+        return y, state
+
 
 _default = None
 
@@ -141,3 +189,11 @@ def scan_fwd(*args, **kw):
 
 def state_update(*args, **kw):
     return default().state_update(*args, **kw)
+
+
+def conv1d(*args, **kw):
+    return default().conv1d(*args, **kw)
+
+
+def conv1d_update(*args, **kw):
+    return default().conv1d_update(*args, **kw)

@@ -260,3 +260,149 @@ int ssm_oracle_state_update_f64(int batch, int dim, int dstate, int zoh,
 }
 
 int ssm_oracle_mutant_id(void) { return ORACLE_MUTANT; }
+
+/* ------------------------------------------------------------------------
+ * Causal depthwise 1-D convolution in front of the scan.
+ *
+ * Sources: [MAMBA] glossary entry "Mamba Block" (the block combines an input
+ * projection, a 1-D convolution, the selective SSM and multiplicative
+ * gating); "everything-about-mamba-paper" (blogofoto.com), cache notes (the
+ * inference cache holds the SSM states after the scan together with the
+ * convolutional states); "details-fiction-and-mamba-paper" (dbblog.net),
+ * implementation notes (the fast path pairs the scan kernels with a causal
+ * conv1d kernel); [CN] basic-model example (d_conv = 4).
+ *
+ * Readings of what the pages leave open:
+ *   - Depthwise: channel d has its own taps weight[d][0..W-1] and bias[d].
+ *   - Causal with the tap order of a standard deep-learning conv layer
+ *     (cross-correlation): tap k multiplies the input k - (W-1) steps away,
+ *     so weight[d][W-1] meets the current input.
+ *   - The W-1 inputs before t = 0 come from a conv state [batch][dim][W-1]
+ *     (oldest first), or are zero; the final conv state is the last W-1
+ *     inputs of that extended sequence.
+ *   - The optional activation is silu, applied after the bias.
+ * Definition: with e = (state0, x) of length W-1+L,
+ *     y[t] = act(bias[d] + sum_k weight[d][k] * e[t + k]),  stateL[k] = e[L + k].
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int batch, dim, seqlen, width, act;
+    const double *x, *weight, *bias, *state0;
+    double *y, *stateL;
+} conv_args;
+
+static int conv_row(const conv_args *a, int b, int d)
+{
+    const int L = a->seqlen, W = a->width, H = a->width - 1;
+    const size_t row = (size_t)b * a->dim + d;
+    double *e = (double *)malloc(sizeof(double) * (size_t)(H + L));
+    if (!e) return -2;
+    for (int k = 0; k < H; ++k) {
+        double v = a->state0 ? a->state0[row * H + k] : 0.0;
+#if ORACLE_MUTANT == 17
+        v = 0.0; /* planted: initial conv state ignored */
+#endif
+        e[k] = v;
+    }
+    for (int t = 0; t < L; ++t) e[H + t] = a->x[row * L + t];
+    const double *w = a->weight + (size_t)d * W;
+    for (int t = 0; t < L; ++t) {
+        double s = a->bias ? a->bias[d] : 0.0;
+        for (int k = 0; k < W; ++k) {
+#if ORACLE_MUTANT == 15
+            s += w[W - 1 - k] * e[t + k]; /* planted: taps reversed */
+#elif ORACLE_MUTANT == 16
+            s += w[k] * (t + k + 1 < H + L ? e[t + k + 1] : 0.0); /* planted: one step of look-ahead */
+#else
+            s += w[k] * e[t + k];
+#endif
+        }
+#if ORACLE_MUTANT == 18
+        a->y[row * L + t] = s; /* planted: activation not applied */
+#else
+        a->y[row * L + t] = a->act ? silu(s) : s;
+#endif
+    }
+    if (a->stateL) {
+        for (int k = 0; k < H; ++k) {
+#if ORACLE_MUTANT == 19
+            a->stateL[row * H + k] = e[L + H - 1 - k]; /* planted: final state newest first */
+#else
+            a->stateL[row * H + k] = e[L + k];
+#endif
+        }
+    }
+    free(e);
+    return 0;
+}
+
+typedef struct {
+    const conv_args *a;
+    long first, last;
+    int ok;
+} conv_worker;
+
+static void *conv_rows(void *p)
+{
+    conv_worker *w = (conv_worker *)p;
+    w->ok = 1;
+    for (long r = w->first; r < w->last; ++r) {
+        if (conv_row(w->a, (int)(r / w->a->dim), (int)(r % w->a->dim)) != 0) w->ok = 0;
+    }
+    return NULL;
+}
+
+/*
+ * Whole-sequence causal conv.  Shapes: x, y [batch][dim][L]; weight [dim][W];
+ * bias [dim] or NULL; state0, stateL [batch][dim][W-1] or NULL (stateL may be
+ * state0: every row reads its state0 before writing stateL).  act != 0 applies
+ * silu.  Returns 0, -1 on bad arguments, -2 on allocation failure.
+ */
+int ssm_oracle_conv1d_f64(int batch, int dim, int seqlen, int width, int act,
+                          const double *x, const double *weight, const double *bias,
+                          const double *state0, double *y, double *stateL, int nthreads)
+{
+    if (batch < 1 || dim < 1 || seqlen < 1 || width < 1) return -1;
+    if (!x || !weight || !y) return -1;
+    conv_args a = {batch, dim, seqlen, width, act, x, weight, bias, state0, y, stateL};
+    const long rows = (long)batch * dim;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > rows) nthreads = (int)rows;
+    if (nthreads > 256) nthreads = 256;
+    pthread_t tid[256];
+    int created[256];
+    conv_worker w[256];
+    int ok = 1;
+    for (int i = 0; i < nthreads; ++i) {
+        w[i].a = &a;
+        w[i].first = rows * i / nthreads;
+        w[i].last = rows * (i + 1) / nthreads;
+        w[i].ok = 0;
+        created[i] = 0;
+        if (i == 0) continue;
+        if (pthread_create(&tid[i], NULL, conv_rows, &w[i]) == 0) {
+            created[i] = 1;
+        } else {
+            conv_rows(&w[i]);
+        }
+    }
+    conv_rows(&w[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (created[i]) pthread_join(tid[i], NULL);
+    }
+    for (int i = 0; i < nthreads; ++i) ok &= w[i].ok;
+    return ok ? 0 : -2;
+}
+
+/*
+ * Decode step of the conv: the whole-sequence conv at L = 1 starting from
+ * `state` [batch][dim][W-1], which receives the shifted window.
+ * x, y [batch][dim].
+ */
+int ssm_oracle_conv1d_update_f64(int batch, int dim, int width, int act, double *state,
+                                 const double *x, const double *weight, const double *bias,
+                                 double *y, int nthreads)
+{
+    if (!state && width > 1) return -1;
+    return ssm_oracle_conv1d_f64(batch, dim, 1, width, act, x, weight, bias, state, y, state,
+                                 nthreads);
+}

@@ -312,9 +312,88 @@ def pin_softplus_silu(o):
         assert abs(y[0, 0, 0] - float(ref)) <= 4e-16 * abs(float(ref)) + 1e-300, (zv, y, ref)
 
 
+# --------------------------------------------------------------------------
+# Causal depthwise conv in front of the scan (glossary entry "Mamba Block";
+# conv state in the inference cache, "everything-about-mamba-paper";
+# d_conv = 4, soft186.com basic-model example).
+# --------------------------------------------------------------------------
+def _rand_conv(rng, batch, dim, L, W, state=True):
+    return dict(x=rng.standard_normal((batch, dim, L)), weight=rng.standard_normal((dim, W)),
+                bias=rng.standard_normal(dim),
+                state0=rng.standard_normal((batch, dim, W - 1)) if state else None)
+
+
+def pin_conv_hand_examples(o):
+    with open(os.path.join(GOLDEN, "conv_hand_examples.json")) as f:
+        spec = json.load(f)
+    for case in spec["cases"]:
+        y, sL = o.conv1d(_arr(case["x"]), _arr(case["weight"]), bias=_arr(case["bias"]),
+                         state0=_arr(case["state0"]), silu=case["silu"])
+        np.testing.assert_allclose(y, _arr(case["y"]), rtol=1e-14, atol=1e-14, err_msg=case["name"])
+        np.testing.assert_allclose(sL, _arr(case["stateL"]), rtol=0, atol=0, err_msg=case["name"])
+
+
+def pin_conv_library(o):
+    """Special case of a library routine: torch's grouped conv1d (a
+    cross-correlation) over the history-extended input, in fp64 on the CPU."""
+    import torch
+    rng = np.random.default_rng(31)
+    for W in (2, 3, 4):
+        for silu in (False, True):
+            p = _rand_conv(rng, 2, 5, 37, W)
+            y, _ = o.conv1d(p["x"], p["weight"], bias=p["bias"], state0=p["state0"], silu=silu)
+            e = torch.from_numpy(np.concatenate([p["state0"], p["x"]], axis=2))
+            ref = torch.nn.functional.conv1d(e, torch.from_numpy(p["weight"])[:, None, :],
+                                             torch.from_numpy(p["bias"]), groups=5).numpy()
+            if silu:
+                ref = ref * expit(ref)
+            np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-14)
+
+
+def pin_conv_impulse(o):
+    """A unit impulse at t0 with zero history returns the taps newest-last:
+    y[t] = bias + w[W-1-(t-t0)] for t0 <= t < t0 + W, and bias elsewhere."""
+    W, L, t0 = 4, 12, 5
+    w = np.array([[0.5, -1.25, 2.0, 3.5]])
+    x = np.zeros((1, 1, L))
+    x[0, 0, t0] = 1.0
+    y, sL = o.conv1d(x, w, bias=np.array([0.25]), silu=False)
+    ref = np.full(L, 0.25)
+    for t in range(t0, t0 + W):
+        ref[t] += w[0, W - 1 - (t - t0)]
+    np.testing.assert_array_equal(y[0, 0], ref)
+    np.testing.assert_array_equal(sL[0, 0], x[0, 0, L - (W - 1):])
+
+
+def pin_conv_split_resume(o):
+    """Feeding the final conv state of x[:, :, :L1] as the history of
+    x[:, :, L1:] reproduces the whole run, also for pieces shorter than W-1."""
+    rng = np.random.default_rng(32)
+    for W in (2, 3, 4):
+        p = _rand_conv(rng, 2, 3, 29, W)
+        y, sL = o.conv1d(**p)
+        for cut in (1, 2, 13, 28):
+            y1, s1 = o.conv1d(p["x"][:, :, :cut], p["weight"], p["bias"], p["state0"])
+            y2, s2 = o.conv1d(p["x"][:, :, cut:], p["weight"], p["bias"], s1)
+            np.testing.assert_allclose(np.concatenate([y1, y2], axis=2), y, rtol=1e-14, atol=1e-15)
+            np.testing.assert_array_equal(s2, sL)
+
+
+def pin_conv_decode_equals_prefill(o):
+    rng = np.random.default_rng(33)
+    p = _rand_conv(rng, 3, 4, 9, 4)
+    y, sL = o.conv1d(**p)
+    state = p["state0"].copy()
+    for t in range(9):
+        yt, state = o.conv1d_update(state, p["x"][:, :, t], p["weight"], p["bias"])
+        np.testing.assert_allclose(yt, y[:, :, t], rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(state, sL)
+
+
 PINS = [pin_hand_examples, pin_lti_convolution, pin_small_delta, pin_large_delta, pin_gated_rnn,
         pin_bracketings, pin_split_resume, pin_decode_equals_scan, pin_linearity,
-        pin_equivariance, pin_softplus_silu]
+        pin_equivariance, pin_softplus_silu, pin_conv_hand_examples, pin_conv_library,
+        pin_conv_impulse, pin_conv_split_resume, pin_conv_decode_equals_prefill]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
