@@ -150,29 +150,33 @@ def to_dev(inp, name):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
 
-def cpu_baseline(inp, block=512):
-    """The fp64 oracle as it stands, on all host cores, over the whole workload
-    (processed in channel blocks to bound host memory)."""
+def cpu_baseline(inp, block=512, min_seconds=10.0):
+    """The fp64 oracle as it stands, on all host cores, over whole passes of the
+    workload (channel blocks bound host memory), repeated until about
+    min_seconds of oracle time have been measured."""
     import oracle
     wl = inp.wl
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     A, Dk, bias = (inp.A.astype(np.float64), inp.Dskip.astype(np.float64),
                    inp.dt_bias.astype(np.float64))
     Bm, Cm = inp.values("Bm"), inp.values("Cm")
-    elapsed = 0.0
+    blocks = []
     for d0 in range(0, wl.dim, block):
         d1 = min(wl.dim, d0 + block)
-        x = synth_vals(inp, "x", d0, d1)
-        dt = synth_vals(inp, "dt", d0, d1)
-        z = synth_vals(inp, "z", d0, d1)
-        t0 = time.perf_counter()
-        oracle.scan_fwd(x, dt, A[d0:d1], Bm, Cm, dt_bias=bias[d0:d1], Dskip=Dk[d0:d1], z=z,
-                        threads=threads)
-        elapsed += time.perf_counter() - t0
-    elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
+        blocks.append((d0, d1, synth_vals(inp, "x", d0, d1), synth_vals(inp, "dt", d0, d1),
+                       synth_vals(inp, "z", d0, d1)))
+    elapsed, passes = 0.0, 0
+    while passes == 0 or elapsed < min_seconds:
+        for d0, d1, x, dt, z in blocks:
+            t0 = time.perf_counter()
+            oracle.scan_fwd(x, dt, A[d0:d1], Bm, Cm, dt_bias=bias[d0:d1], Dskip=Dk[d0:d1], z=z,
+                            threads=threads)
+            elapsed += time.perf_counter() - t0
+        passes += 1
+    elems = wl.batch * wl.dim * wl.seqlen * wl.dstate * passes
     return {"value": elems / elapsed, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": "whole workload (%d x %d x %d x %d), fp64 sequential recurrence, %.2f s"
-                      % (wl.batch, wl.dim, wl.seqlen, wl.dstate, elapsed)}
+            "sample": "%d passes over the whole workload (%d x %d x %d x %d), fp64 sequential "
+                      "recurrence, %.2f s" % (passes, wl.batch, wl.dim, wl.seqlen, wl.dstate, elapsed)}
 
 
 def synth_vals(inp, name, d0, d1):
