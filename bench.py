@@ -224,6 +224,48 @@ def bench_decode(torch, ssm, synth, steps_cap=256):
             "note": "one launch per token, state fp32 in place; 21 MB state can stay in the 256 MB MALL"}
 
 
+def bench_conv(torch, ssm, synth, wl, x, launches=20):
+    """Causal depthwise conv (W 4, silu, bf16 in and out) over the layer's x,
+    and its decode step on the decode workload's shape; HBM-bound."""
+    w, b = synth.conv_parameters(wl, 4)
+    wt, bt = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda()
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        ssm.ssm_conv1d_fwd(x, wt, bias=bt, y=y, return_final_state=False)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        ssm.ssm_conv1d_fwd(x, wt, bias=bt, y=y, return_final_state=False)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    nbytes = 2 * x.numel() * x.element_size() + wl.dim * 5 * 4
+    out = {"workload": "conv1d W4 silu, %s" % wl.name, "kernel_ms_mean": ms,
+           "outputs_per_s": x.numel() / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "hbm_gbps_algorithmic": nbytes / (ms * 1e-3) / 1e9,
+           "hbm_frac": nbytes / (ms * 1e-3) / PEAK_HBM}
+    dwl = synth.WORKLOADS[4]
+    state = torch.zeros((dwl.batch, dwl.dim, 3), device="cuda")
+    xs = torch.randn((64, dwl.batch, dwl.dim), device="cuda").to(torch.bfloat16)
+    ys = torch.empty((64, dwl.batch, dwl.dim), device="cuda", dtype=torch.bfloat16)
+    wd, bd = synth.conv_parameters(dwl, 4)
+    wd, bd = torch.from_numpy(wd).cuda(), torch.from_numpy(bd).cuda()
+    for s in range(8):
+        ssm.ssm_conv1d_update(state, xs[s], wd, bias=bd, y=ys[s])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(64):
+        ssm.ssm_conv1d_update(state, xs[s], wd, bias=bd, y=ys[s])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out["decode_us_per_call"] = e0.elapsed_time(e1) / 64 * 1e3
+    out["decode_workload"] = "conv1d update W4, batch %d dim %d" % (dwl.batch, dwl.dim)
+    return out
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -328,6 +370,7 @@ def main():
     result["zoh_variant"] = {"kernel_ms_mean": zms, "elements_per_s": elems / (zms * 1e-3)}
     if not args.no_decode:
         result["decode"] = bench_decode(torch, ssm, synth)
+        result["conv1d"] = bench_conv(torch, ssm, synth, wl, t["x"])
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(result), flush=True)

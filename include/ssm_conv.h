@@ -1,0 +1,75 @@
+/*
+ * ssm_conv.h -- C ABI of the causal depthwise 1-D convolution that feeds the
+ * selective scan, and of its single-token decode step (gfx950).
+ *
+ * The Mamba block applies a short 1-D convolution over the sequence before
+ * the selective SSM (glossary entry "Mamba Block" of the page "Mamba:
+ * Linear-Time Sequence Modeling with Selective State Spaces"; the basic-model
+ * example of the soft186.com page "Mamba选择性状态空间机制：效率提升10倍的核心突破"
+ * uses d_conv = 4).  The inference cache keeps the convolutional state beside
+ * the SSM state ("everything-about-mamba-paper", blogofoto.com), and the fast
+ * path pairs the scan kernels with a causal conv1d kernel
+ * ("details-fiction-and-mamba-paper", dbblog.net).
+ *
+ * The pages give no formula for the convolution; this library computes, per
+ * (batch b, channel d), with e = (state0[b][d][0..W-2], x[b][d][0..L-1]):
+ *     y[b][d][t]        = act(bias[d] + sum_{k<W} weight[d][k] * e[t + k])
+ *     stateL[b][d][k]   = e[L + k]                    (k < W-1)
+ * i.e. a depthwise cross-correlation whose last tap weight[d][W-1] meets the
+ * current input, left-padded by the conv state (oldest first) or zeros;
+ * act = silu (z * sigmoid(z)) when SSM_CONV_SILU is set, else the identity.
+ *
+ * Conventions are those of ssm.h: caller-owned, densely packed, row-major
+ * device pointers; nothing is allocated or retained; argument errors return a
+ * status before anything is enqueued (nothing is written); a failed launch
+ * returns SSM_ERR_HIP; calls are asynchronous on `stream` (NULL = default).
+ * Every pointer must be aligned to its element size.
+ */
+#ifndef SSM_CONV_H
+#define SSM_CONV_H
+
+#include "ssm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* flags bit 0: apply silu after the bias.  Other bits must be zero
+ * (SSM_ERR_UNSUPPORTED). */
+#define SSM_CONV_SILU 0x1u
+
+/*
+ * Causal conv over whole sequences.
+ *   width    W in {2, 3, 4} (SSM_ERR_UNSUPPORTED otherwise)
+ *   x        [batch][dim][seqlen]  in_dtype
+ *   weight   [dim][width]          fp32
+ *   bias     [dim] fp32, or NULL (zero)
+ *   state0   [batch][dim][width-1] fp32 inputs preceding x[., ., 0], oldest
+ *            first, or NULL (zeros)
+ *   y        [batch][dim][seqlen]  out_dtype; must not overlap any input
+ *   stateL   [batch][dim][width-1] fp32 final conv state, or NULL (not
+ *            returned); may be exactly state0 (each row reads its state0
+ *            before writing stateL) but must not otherwise overlap an input or y
+ * Supported sizes: batch, dim, seqlen >= 1 with batch * dim * seqlen < 2^62.
+ */
+ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype_t in_dtype,
+                            unsigned flags, const void *x, const float *weight,
+                            const float *bias, const float *state0, ssm_dtype_t out_dtype,
+                            void *y, float *stateL, void *stream);
+
+/*
+ * One decode step: the same operation at seqlen = 1 on a persistent state.
+ *   state    [batch][dim][width-1] fp32, read and overwritten in place with
+ *            the window shifted by one (the new input last)
+ *   x        [batch][dim] in_dtype;  weight [dim][width] fp32;  bias [dim] or NULL
+ *   y        [batch][dim] out_dtype; must not overlap any input or state
+ */
+ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dtype,
+                               unsigned flags, float *state, const void *x, const float *weight,
+                               const float *bias, ssm_dtype_t out_dtype, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_CONV_H */

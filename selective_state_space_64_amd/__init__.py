@@ -1,6 +1,7 @@
 """Selective state-space (S6) scan for AMD MI355X (gfx950).
 
-Thin Python binding over the C ABI in ``include/ssm.h`` (``libssm.so``):
+Thin Python binding over the C ABI in ``include/ssm.h`` and
+``include/ssm_conv.h`` (``libssm.so``):
 argument marshalling only.  Every step of the computation runs in the HIP
 kernels of ``csrc/``; PyTorch only provides device memory and the stream.
 There is no CPU fallback: if the library is missing or no GPU is present the
@@ -8,9 +9,12 @@ calls raise.
 
     y, hL = ssm_scan_fwd(x, dt, A, Bm, Cm, dt_bias=..., Dskip=..., z=..., h0=...)
     y = ssm_state_update(state, x, dt, A, Bm, Cm, dt_bias=..., Dskip=..., z=...)
+    y, stateL = ssm_conv1d_fwd(x, weight, bias=..., state0=..., silu=True)
+    y = ssm_conv1d_update(state, x, weight, bias=..., silu=True)
 
 Layouts: x, dt, z, y [batch, dim, L]; Bm, Cm [batch, N, L]; A [dim, N];
-Dskip, dt_bias [dim]; h0, hL, state [batch, dim, N] (decode: drop L).
+Dskip, dt_bias [dim]; h0, hL, state [batch, dim, N] (decode: drop L);
+conv weight [dim, W], bias [dim], conv state [batch, dim, W-1].
 """
 import ctypes
 import os
@@ -22,13 +26,14 @@ LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 SSM_FLAG_ZOH_B = 0x1
+SSM_CONV_SILU = 0x1
 STATUS = {
     0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_BAD_DTYPE",
     4: "SSM_ERR_MISALIGNED", 5: "SSM_ERR_ALIAS", 6: "SSM_ERR_UNSUPPORTED",
     7: "SSM_ERR_WORKSPACE", 8: "SSM_ERR_HIP",
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
-           "ssm_scan_fwd", "ssm_state_update"]
+           "ssm_scan_fwd", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_update"]
 
 
 class SSMError(RuntimeError):
@@ -59,6 +64,10 @@ def lib():
         L.ssm_scan_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 9 + [i, vp, vp, vp, sz, vp]
         L.ssm_state_update.restype = i
         L.ssm_state_update.argtypes = [i, i, i, i, u] + [vp] * 9 + [i, vp, vp]
+        L.ssm_conv1d_fwd.restype = i
+        L.ssm_conv1d_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 4 + [i, vp, vp, vp]
+        L.ssm_conv1d_update.restype = i
+        L.ssm_conv1d_update.argtypes = [i, i, i, i, u] + [vp] * 4 + [i, vp, vp]
         _lib = L
     return _lib
 
@@ -150,5 +159,50 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     return y
 
 
+def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=None,
+                   return_final_state=True, y=None, stateL=None, stream=None):
+    """Causal depthwise conv over [batch, dim, L]; returns (y, stateL).
+    out_dtype defaults to x's dtype (the conv output feeds the scan's x)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    W = weight.shape[-1]
+    out_dtype = out_dtype or x.dtype
+    if y is None:
+        y = torch.empty((batch, dim, L), dtype=out_dtype, device=x.device)
+    if stateL is None and return_final_state:
+        stateL = torch.empty((batch, dim, W - 1), dtype=torch.float32, device=x.device)
+    f32 = torch.float32
+    args = [_ptr(x, "x", (batch, dim, L), x.dtype), _ptr(weight, "weight", (dim, W), f32),
+            _ptr(bias, "bias", (dim,), f32), _ptr(state0, "state0", (batch, dim, W - 1), f32)]
+    yp = _ptr(y, "y", (batch, dim, L), y.dtype)
+    sp = _ptr(stateL, "stateL", (batch, dim, W - 1), f32)
+    st = lib().ssm_conv1d_fwd(batch, dim, L, W, _dtype_code(x.dtype), SSM_CONV_SILU if silu else 0,
+                              *args, _dtype_code(y.dtype), yp, sp, _stream(stream, x.device))
+    _check(st)
+    return y, stateL
+
+
+def ssm_conv1d_update(state, x, weight, *, bias=None, silu=True, out_dtype=None, y=None,
+                      stream=None):
+    """One decode step of the conv; shifts `state` [batch, dim, W-1] in place
+    and returns y [batch, dim]."""
+    batch, dim, H = state.shape
+    out_dtype = out_dtype or x.dtype
+    if y is None:
+        y = torch.empty((batch, dim), dtype=out_dtype, device=x.device)
+    f32 = torch.float32
+    args = [_ptr(state, "state", (batch, dim, H), f32), _ptr(x, "x", (batch, dim), x.dtype),
+            _ptr(weight, "weight", (dim, H + 1), f32), _ptr(bias, "bias", (dim,), f32)]
+    yp = _ptr(y, "y", (batch, dim), y.dtype)
+    st = lib().ssm_conv1d_update(batch, dim, H + 1, _dtype_code(x.dtype),
+                                 SSM_CONV_SILU if silu else 0, *args, _dtype_code(y.dtype), yp,
+                                 _stream(stream, x.device))
+    _check(st)
+    return y
+
+
 scan_fwd = ssm_scan_fwd
 state_update = ssm_state_update
+conv1d_fwd = ssm_conv1d_fwd
+conv1d_update = ssm_conv1d_update

@@ -1,0 +1,302 @@
+// conv1d.hip -- causal depthwise 1-D convolution that feeds the selective
+// scan, and its single-token decode step, for gfx950.
+//
+// The Mamba block runs a short 1-D convolution over the sequence before the
+// selective SSM (glossary entry "Mamba Block" of the page "Mamba: Linear-Time
+// Sequence Modeling with Selective State Spaces"; d_conv = 4 in the
+// basic-model example of the soft186.com page), and the inference cache keeps
+// its convolutional state beside the SSM state ("everything-about-mamba-paper").
+// Per (batch b, channel d), with the W-1 inputs before t = 0 taken from the
+// conv state (oldest first) or zero:
+//     y[t] = act(bias[d] + sum_k weight[d][k] * x[t - (W-1) + k])
+// so weight[d][W-1] meets the current input; act is silu or the identity.
+//
+// The forward pass reads each input once and writes each output once: it is
+// bound by HBM bandwidth, not arithmetic (W fma + one silu per output).  A
+// lane owns 8 consecutive outputs of one row; consecutive lanes own
+// consecutive runs of the same row, so a wave reads and writes contiguous
+// 1 KB (bf16) stretches with 16-byte vector accesses.  The W-1 inputs before a
+// run are the previous lane's last inputs (a lane shuffle, so every input is
+// read from memory once), the conv state for a row's first run, or, for lane 0
+// of a wave, W-1 element loads.
+// The first run's lane also writes the row's final conv state, after reading
+// the initial one, so the two may be the same buffer.
+#include "ssm_device.hpp"
+#include "ssm_launch.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kRun = 8;          // outputs per lane
+constexpr int kConvThreads = 256;
+
+struct ConvParams {
+    int dim, seqlen, runs_per_row;
+    unsigned div_mul, div_shift;  // g / runs_per_row == (umulhi(g, mul) + g) >> shift
+    long long total_runs;
+    const void *x;
+    const float *weight, *bias, *state0;
+    void *y;
+    float *stateL;
+};
+
+// Division by a fixed divisor 1 <= d < 2^31 through one high multiply
+// (round-up reciprocal: m = floor(2^32 (2^s - d) / d) + 1 with 2^s >= d),
+// exact for every 32-bit numerator.
+struct MagicDiv {
+    unsigned mul, shift;
+};
+
+MagicDiv magic_div(unsigned d)
+{
+    unsigned s = 0;
+    while ((1ull << s) < d) ++s;
+    const unsigned long long m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+    return {unsigned(m), s};
+}
+
+__device__ inline unsigned div_magic(unsigned n, unsigned mul, unsigned shift)
+{
+    const unsigned t = __umulhi(n, mul);
+    return unsigned((static_cast<unsigned long long>(t) + n) >> shift);
+}
+
+template <int W>
+__device__ inline void load_taps(const float *w, float *taps)
+{
+#pragma unroll
+    for (int k = 0; k < W; ++k) taps[k] = w[k];
+}
+
+template <typename Tout>
+__device__ inline void store_run(Tout *p, bool vec, int count, const float *v);
+
+template <>
+__device__ inline void store_run<float>(float *p, bool vec, int count, const float *v)
+{
+    if (vec) {
+        f32x4 *q = reinterpret_cast<f32x4 *>(p);
+        q[0] = f32x4{v[0], v[1], v[2], v[3]};
+        q[1] = f32x4{v[4], v[5], v[6], v[7]};
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRun; ++i)
+            if (i < count) p[i] = v[i];
+    }
+}
+
+template <>
+__device__ inline void store_run<bf16_t>(bf16_t *p, bool vec, int count, const float *v)
+{
+    if (vec) {
+        *reinterpret_cast<u32x4 *>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRun; ++i)
+            if (i < count) p[i].bits = uint16_t(pack_bf16x2(v[i], 0.0f) & 0xffffu);
+    }
+}
+
+// vec_in / vec_out: every run of every row starts on a 16-byte boundary of x
+// (resp. y), decided on the host from the base addresses and seqlen.
+template <typename Tin, typename Tout, int W, bool kWide>
+__global__ void __launch_bounds__(kConvThreads)
+conv1d_fwd_kernel(ConvParams p, bool vec_in, bool vec_out, bool act)
+{
+    constexpr int H = W - 1;
+    const long long g = (long long)blockIdx.x * kConvThreads + threadIdx.x;
+    const bool live = g < p.total_runs;
+    long long row;
+    int j;
+    if constexpr (kWide) {
+        row = g / p.runs_per_row;
+        j = int(g - row * p.runs_per_row);
+    } else {
+        const unsigned q = div_magic(unsigned(g), p.div_mul, p.div_shift);
+        row = q;
+        j = int(unsigned(g) - q * unsigned(p.runs_per_row));
+    }
+    const int L = p.seqlen;
+    const int t0 = j * kRun;
+    const int count = live ? min(kRun, L - t0) : 0;
+
+    const Tin *xr = static_cast<const Tin *>(p.x) + row * L;
+    float e[H + kRun];  // e[H + i] = x[t0 + i]; e[0..H) the inputs before the run
+    if (live) {
+        load_run<Tin, kRun>(xr + t0, vec_in && count == kRun, count, e + H);
+    } else {
+#pragma unroll
+        for (int i = 0; i < H + kRun; ++i) e[i] = 0.0f;
+    }
+    // The H inputs before the run are the previous lane's last H inputs when
+    // that lane holds the previous run of the same row (j > 0, not lane 0).
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int k = 0; k < H; ++k) e[k] = __shfl_up(e[kRun + k], 1, 64);
+    if (!live) return;
+    if (j == 0) {
+#pragma unroll
+        for (int k = 0; k < H; ++k) e[k] = p.state0 ? p.state0[row * H + k] : 0.0f;
+    } else if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < H; ++k) e[k] = io<Tin>::load1(xr + t0 - H + k);
+    }
+    const int d = int(row % p.dim);
+
+    float taps[W];
+    load_taps<W>(p.weight + (size_t)d * W, taps);
+    const float b = p.bias ? p.bias[d] : 0.0f;
+    float out[kRun];
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+        float s = b;
+#pragma unroll
+        for (int k = 0; k < W; ++k) s = __builtin_fmaf(taps[k], e[i + k], s);
+        out[i] = act ? silu(s) : s;
+    }
+    store_run<Tout>(static_cast<Tout *>(p.y) + row * L + t0, vec_out && count == kRun, count,
+                    out);
+
+    if (j == 0 && p.stateL) {
+        // Final state = the last H entries of (state0, x).  This lane already
+        // holds state0 in e[0..H); entries inside x are read from memory.
+        float fin[H > 0 ? H : 1];
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const int idx = L - H + k;  // position in x; < 0 means inside state0
+            fin[k] = idx >= 0 ? io<Tin>::load1(xr + idx) : e[idx + H];
+        }
+#pragma unroll
+        for (int k = 0; k < H; ++k) p.stateL[row * H + k] = fin[k];
+    }
+}
+
+struct ConvUpdateParams {
+    int batch, dim;
+    float *state;
+    const void *x;
+    const float *weight, *bias;
+    void *y;
+};
+
+// One lane per (batch, channel): y = act(bias + sum_k w[k] e[k]) over
+// e = (state, x), then state <- the last W-1 entries of e, in place.
+template <typename Tin, typename Tout, int W>
+__global__ void __launch_bounds__(kConvThreads)
+conv1d_update_kernel(ConvUpdateParams p, bool act)
+{
+    constexpr int H = W - 1;
+    const long long row = (long long)blockIdx.x * kConvThreads + threadIdx.x;
+    if (row >= (long long)p.batch * p.dim) return;
+    const int d = int(row % p.dim);
+    float e[W];
+#pragma unroll
+    for (int k = 0; k < H; ++k) e[k] = p.state[row * H + k];
+    e[H] = io<Tin>::load1(static_cast<const Tin *>(p.x) + row);
+    float taps[W];
+    load_taps<W>(p.weight + (size_t)d * W, taps);
+    float s = p.bias ? p.bias[d] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < W; ++k) s = __builtin_fmaf(taps[k], e[k], s);
+    const float v = act ? silu(s) : s;
+    if constexpr (sizeof(Tout) == 4) {
+        static_cast<float *>(p.y)[row] = v;
+    } else {
+        static_cast<bf16_t *>(p.y)[row].bits = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu);
+    }
+#pragma unroll
+    for (int k = 0; k < H; ++k) p.state[row * H + k] = e[k + 1];
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+template <typename Tin, typename Tout, int W>
+hipError_t launch_conv_typed(const ConvArgs &a, hipStream_t stream)
+{
+    ConvParams p;
+    p.dim = a.dim;
+    p.seqlen = a.seqlen;
+    p.runs_per_row = (a.seqlen + kRun - 1) / kRun;
+    p.total_runs = (long long)a.batch * a.dim * p.runs_per_row;
+    p.x = a.x;
+    p.weight = a.weight;
+    p.bias = a.bias;
+    p.state0 = a.state0;
+    p.y = a.y;
+    p.stateL = a.stateL;
+    // Every run starts at element row * L + 8 j; 16-byte vectors need that
+    // offset times the element size to be a multiple of 16 on a 16-byte base.
+    const bool vec_in = aligned16(a.x) && (size_t(a.seqlen) * sizeof(Tin)) % 16 == 0 &&
+                        (kRun * sizeof(Tin)) % 16 == 0;
+    const bool vec_out = aligned16(a.y) && (size_t(a.seqlen) * sizeof(Tout)) % 16 == 0 &&
+                         (kRun * sizeof(Tout)) % 16 == 0;
+    const long long blocks = (p.total_runs + kConvThreads - 1) / kConvThreads;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (p.total_runs + kConvThreads <= (1ll << 32)) {
+        const MagicDiv m = magic_div(unsigned(p.runs_per_row));
+        p.div_mul = m.mul;
+        p.div_shift = m.shift;
+        hipLaunchKernelGGL((conv1d_fwd_kernel<Tin, Tout, W, false>), dim3(unsigned(blocks)),
+                           dim3(kConvThreads), 0, stream, p, vec_in, vec_out, a.silu != 0);
+    } else {
+        hipLaunchKernelGGL((conv1d_fwd_kernel<Tin, Tout, W, true>), dim3(unsigned(blocks)),
+                           dim3(kConvThreads), 0, stream, p, vec_in, vec_out, a.silu != 0);
+    }
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout, int W>
+hipError_t launch_update_typed(const ConvUpdateArgs &a, hipStream_t stream)
+{
+    ConvUpdateParams p{a.batch, a.dim, a.state, a.x, a.weight, a.bias, a.y};
+    const long long rows = (long long)a.batch * a.dim;
+    const long long blocks = (rows + kConvThreads - 1) / kConvThreads;
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((conv1d_update_kernel<Tin, Tout, W>), dim3(unsigned(blocks)),
+                       dim3(kConvThreads), 0, stream, p, a.silu != 0);
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t conv_width(const ConvArgs &a, hipStream_t s)
+{
+    switch (a.width) {
+    case 2: return launch_conv_typed<Tin, Tout, 2>(a, s);
+    case 3: return launch_conv_typed<Tin, Tout, 3>(a, s);
+    case 4: return launch_conv_typed<Tin, Tout, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename Tin, typename Tout>
+hipError_t update_width(const ConvUpdateArgs &a, hipStream_t s)
+{
+    switch (a.width) {
+    case 2: return launch_update_typed<Tin, Tout, 2>(a, s);
+    case 3: return launch_update_typed<Tin, Tout, 3>(a, s);
+    case 4: return launch_update_typed<Tin, Tout, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream)
+{
+    if (a.in_bf16) {
+        return a.out_bf16 ? conv_width<bf16_t, bf16_t>(a, stream) : conv_width<bf16_t, float>(a, stream);
+    }
+    return a.out_bf16 ? conv_width<float, bf16_t>(a, stream) : conv_width<float, float>(a, stream);
+}
+
+hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t stream)
+{
+    if (a.in_bf16) {
+        return a.out_bf16 ? update_width<bf16_t, bf16_t>(a, stream)
+                          : update_width<bf16_t, float>(a, stream);
+    }
+    return a.out_bf16 ? update_width<float, bf16_t>(a, stream) : update_width<float, float>(a, stream);
+}
+
+}  // namespace ssm

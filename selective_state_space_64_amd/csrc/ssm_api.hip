@@ -2,6 +2,7 @@
 // and dispatch to the gfx950 kernels.  Every argument error is detected here,
 // before anything is enqueued, so a failing call has no side effects.
 #include "ssm.h"
+#include "ssm_conv.h"
 
 #include <stdint.h>
 
@@ -59,7 +60,8 @@ const char *ssm_status_string(ssm_status_t s)
     case SSM_ERR_BAD_DTYPE: return "in_dtype/out_dtype must be SSM_F32 or SSM_BF16";
     case SSM_ERR_MISALIGNED: return "a pointer is not aligned to its element size (state: 16 bytes)";
     case SSM_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
-    case SSM_ERR_UNSUPPORTED: return "unsupported dstate (use 1, 2, 4, 8 or 16) or unknown flag bit";
+    case SSM_ERR_UNSUPPORTED:
+        return "unsupported dstate (1, 2, 4, 8 or 16) or conv width (2, 3 or 4), or an unknown flag bit";
     case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_fwd_workspace_bytes";
     case SSM_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     }
@@ -170,6 +172,87 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
     ssm::UpdateArgs a{batch, dim, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
                       (flags & SSM_FLAG_ZOH_B) != 0, state, x, dt, dt_bias, A, Bm, Cm, Dskip, z, y};
     const hipError_t e = ssm::launch_state_update(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype_t in_dtype,
+                            unsigned flags, const void *x, const float *weight,
+                            const float *bias, const float *state0, ssm_dtype_t out_dtype,
+                            void *y, float *stateL, void *stream)
+{
+    if (!x || !weight || !y) return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1 || seqlen < 1) return SSM_ERR_BAD_SHAPE;
+    if (width < 2 || width > 4 || (flags & ~SSM_CONV_SILU) != 0) return SSM_ERR_UNSUPPORTED;
+    const size_t seq_elems = mul3(batch, dim, seqlen);
+    const size_t st_elems = mul3(batch, dim, width - 1);
+    if (!seq_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+
+    const size_t in = dsize(in_dtype);
+    if (misaligned(x, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)weight, (const void *)bias, (const void *)state0,
+                          (const void *)stateL})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+
+    const size_t ybytes = seq_elems * dsize(out_dtype);
+    const size_t sbytes = st_elems * sizeof(float);
+    struct In {
+        const void *p;
+        size_t bytes;
+    } inputs[] = {{x, seq_elems * in},
+                  {weight, size_t(dim) * width * sizeof(float)},
+                  {bias, dim * sizeof(float)},
+                  {state0, sbytes}};
+    for (const In &i : inputs) {
+        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        // stateL may be exactly state0 (read before written per row), nothing else
+        if (stateL && !(i.p == state0 && stateL == state0) && overlaps(stateL, sbytes, i.p, i.bytes))
+            return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, ybytes, stateL, sbytes)) return SSM_ERR_ALIAS;
+
+    ssm::ConvArgs a{batch, dim, seqlen, width, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                    (flags & SSM_CONV_SILU) != 0, x, weight, bias, state0, y, stateL};
+    const hipError_t e = ssm::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dtype,
+                               unsigned flags, float *state, const void *x, const float *weight,
+                               const float *bias, ssm_dtype_t out_dtype, void *y, void *stream)
+{
+    if (!state || !x || !weight || !y) return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1) return SSM_ERR_BAD_SHAPE;
+    if (width < 2 || width > 4 || (flags & ~SSM_CONV_SILU) != 0) return SSM_ERR_UNSUPPORTED;
+    const size_t rows = mul3(batch, dim, 1);
+    const size_t st_elems = mul3(batch, dim, width - 1);
+    if (!rows || !st_elems) return SSM_ERR_BAD_SHAPE;
+
+    const size_t in = dsize(in_dtype);
+    if (misaligned(x, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)state, (const void *)weight, (const void *)bias})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+
+    const size_t ybytes = rows * dsize(out_dtype);
+    const size_t sbytes = st_elems * sizeof(float);
+    struct In {
+        const void *p;
+        size_t bytes;
+    } inputs[] = {{x, rows * in},
+                  {weight, size_t(dim) * width * sizeof(float)},
+                  {bias, dim * sizeof(float)}};
+    for (const In &i : inputs) {
+        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        if (overlaps(state, sbytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, ybytes, state, sbytes)) return SSM_ERR_ALIAS;
+
+    ssm::ConvUpdateArgs a{batch, dim, width, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                          (flags & SSM_CONV_SILU) != 0, state, x, weight, bias, y};
+    const hipError_t e = ssm::launch_conv1d_update(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -31,9 +31,29 @@ struct UpdateArgs {
     void *y;
 };
 
-// Both return hipSuccess or the launch error; arguments are already validated.
+struct ConvArgs {
+    int batch, dim, seqlen, width;
+    int in_bf16, out_bf16, silu;
+    const void *x;
+    const float *weight, *bias, *state0;
+    void *y;
+    float *stateL;
+};
+
+struct ConvUpdateArgs {
+    int batch, dim, width;
+    int in_bf16, out_bf16, silu;
+    float *state;
+    const void *x;
+    const float *weight, *bias;
+    void *y;
+};
+
+// All return hipSuccess or the launch error; arguments are already validated.
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream);
+hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream);
+hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t stream);
 
 // Largest batch the kernels' grids support (grid y dimension).
 constexpr int kMaxBatch = 65535;

@@ -16,6 +16,9 @@ Recipe (the pages' layer sizes; no dataset or trained weights involved):
   * Dskip = 1 for the tiny case, else N(1, 0.1).
   * h0 (when asked for) and the decode state ~ N(0, 1), fp32.
   * bf16 tensors are the fp32 draws rounded to nearest-even.
+  * Conv taps weight[d, k] and bias[d] (width W = 4 unless stated) follow the
+    default initialisation of a depthwise conv layer, U(-1/sqrt(W), 1/sqrt(W)),
+    fp32; the conv state (when asked for) ~ N(0, 1), fp32.
 """
 from dataclasses import dataclass, field
 import math
@@ -24,7 +27,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TENSOR_IDS = {"x": 0, "dt": 1, "z": 2, "Bm": 3, "Cm": 4, "Dskip": 5, "delta0": 6, "h0": 7}
+TENSOR_IDS = {"x": 0, "dt": 1, "z": 2, "Bm": 3, "Cm": 4, "Dskip": 5, "delta0": 6, "h0": 7,
+              "conv_w": 8, "conv_b": 9, "conv_state": 10}
 
 
 @dataclass(frozen=True)
@@ -151,6 +155,23 @@ def parameters(wl, dim=None, dstate=None):
     delta0 = np.exp(u)
     dt_bias = np.log(np.expm1(delta0)).astype(np.float32)
     return A, Dskip, dt_bias
+
+
+def conv_parameters(wl, width=4, dim=None):
+    """Depthwise conv taps [dim, width] and bias [dim] (fp32)."""
+    dim = dim or wl.dim
+    bound = 1.0 / math.sqrt(width)
+    w = np.random.default_rng([wl.seed, TENSOR_IDS["conv_w"], width]).uniform(
+        -bound, bound, (dim, width)).astype(np.float32)
+    b = np.random.default_rng([wl.seed, TENSOR_IDS["conv_b"], width]).uniform(
+        -bound, bound, dim).astype(np.float32)
+    return w, b
+
+
+def conv_state(wl, width=4, threads=None):
+    """A conv state [batch, dim, width - 1] ~ N(0, 1) (fp32)."""
+    threads = threads or min(16, os.cpu_count() or 1)
+    return _fill_rows(wl.seed, "conv_state", wl.batch, wl.dim, width - 1, threads)
 
 
 def make_inputs(wl, with_h0=False, threads=None, seqlen=None):

@@ -13,9 +13,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    with open(os.path.join(ROOT, "include", "ssm.h")) as f:
-        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
-    return sorted(set(re.findall(r"\b(ssm_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            with open(os.path.join(inc, h)) as f:
+                text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+            names |= set(re.findall(r"\b(ssm_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -206,3 +211,78 @@ def test_state_update_validation():
     assert call(flags=2) == 6
     assert call() == 8
     assert call(flags=1) == 8  # SSM_FLAG_ZOH_B is accepted
+
+
+# ---------------------------------------------------------------- conv entry points
+_CFAKE = {k: 0x10000000 * (i + 1) for i, k in enumerate(["x", "w", "bias", "s0", "y", "sL"])}
+
+
+def _conv_call(L, **over):
+    a = dict(batch=2, dim=8, seqlen=40, width=4, ind=1, flags=1, outd=1, **_CFAKE)
+    a.update(over)
+    return L.ssm_conv1d_fwd(a["batch"], a["dim"], a["seqlen"], a["width"], a["ind"], a["flags"],
+                            a["x"], a["w"], a["bias"], a["s0"], a["outd"], a["y"], a["sL"], None)
+
+
+def _conv_update_call(L, **over):
+    a = dict(batch=2, dim=8, width=4, ind=1, flags=1, state=_CFAKE["s0"], x=_CFAKE["x"],
+             w=_CFAKE["w"], bias=_CFAKE["bias"], outd=0, y=_CFAKE["y"])
+    a.update(over)
+    return L.ssm_conv1d_update(a["batch"], a["dim"], a["width"], a["ind"], a["flags"], a["state"],
+                               a["x"], a["w"], a["bias"], a["outd"], a["y"], None)
+
+
+CONV_ERRORS = [
+    ("null_x", dict(x=None), 1), ("null_w", dict(w=None), 1), ("null_y", dict(y=None), 1),
+    ("batch0", dict(batch=0), 2), ("dim0", dict(dim=0), 2), ("L0", dict(seqlen=0), 2),
+    ("in_dtype", dict(ind=2), 3), ("out_dtype", dict(outd=9), 3),
+    ("width1", dict(width=1), 6), ("width5", dict(width=5), 6), ("flag2", dict(flags=2), 6),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,over,status", CONV_ERRORS, ids=[e[0] for e in CONV_ERRORS])
+def test_conv_validation_rejects_before_launch(name, over, status):
+    assert _conv_call(ssm.lib(), **over) == status
+
+
+@no_gpu
+def test_conv_validation_alignment_alias_and_update():
+    L = ssm.lib()
+    assert _conv_call(L, x=_CFAKE["x"] + 1) == 4
+    assert _conv_call(L, w=_CFAKE["w"] + 2) == 4
+    assert _conv_call(L, sL=_CFAKE["sL"] + 2) == 4
+    assert _conv_call(L, outd=0, y=_CFAKE["y"] + 2) == 4
+    assert _conv_call(L, y=_CFAKE["x"] + 1280 - 2) == 5      # y over the tail of x
+    assert _conv_call(L, sL=_CFAKE["bias"]) == 5
+    assert _conv_call(L, sL=_CFAKE["s0"] + 4) == 5           # partial overlap with state0
+    assert _conv_call(L, sL=_CFAKE["y"] + 16) == 5
+    assert _conv_call(L) == 8                                 # valid: reaches the launch
+    assert _conv_call(L, sL=_CFAKE["s0"]) == 8                # stateL == state0 allowed
+    assert _conv_call(L, bias=None, s0=None, sL=None, flags=0, width=2) == 8
+    assert _conv_update_call(L, state=None) == 1
+    assert _conv_update_call(L, dim=-3) == 2
+    assert _conv_update_call(L, width=7) == 6
+    assert _conv_update_call(L, state=_CFAKE["s0"] + 2) == 4
+    assert _conv_update_call(L, y=_CFAKE["s0"]) == 5
+    assert _conv_update_call(L, state=_CFAKE["w"]) == 5
+    assert _conv_update_call(L) == 8
+
+
+@pytest.mark.gpu
+def test_conv_argument_errors_write_nothing():
+    g = torch.Generator().manual_seed(1)
+    x = torch.randn(2, 8, 40, generator=g).to(torch.bfloat16).cuda()
+    w = torch.randn(8, 4, generator=g).cuda()
+    s0 = torch.randn(2, 8, 3, generator=g).cuda()
+    y = torch.full((2, 8, 40), 7.0, device="cuda")
+    sL = torch.full((2, 8, 3), 7.0, device="cuda")
+    L = ssm.lib()
+    base = dict(x=x.data_ptr(), w=w.data_ptr(), bias=None, s0=s0.data_ptr(), outd=0,
+                y=y.data_ptr(), sL=sL.data_ptr())
+    for name, over, status in CONV_ERRORS:
+        assert _conv_call(L, **{**base, **over}) == status, name
+    assert _conv_call(L, **{**base, "sL": s0.data_ptr() + 4}) == 5
+    assert _conv_call(L, **{**base, "y": x.data_ptr()}) == 5
+    torch.cuda.synchronize()
+    assert (y == 7.0).all() and (sL == 7.0).all()
