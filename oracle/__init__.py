@@ -39,6 +39,13 @@ MUTANTS = {
     17: "initial conv state ignored",
     18: "conv activation not applied",
     19: "final conv state stored newest first",
+    20: "backward: Delta gradient without the A-bar term",
+    21: "backward: A gradient without the Delta factor",
+    22: "backward: adjoint state not decayed by A-bar",
+    23: "backward: gradient of the final state ignored",
+    24: "backward: gate derivative sigmoid(z) instead of silu'(z)",
+    25: "backward: softplus derivative taken as softplus",
+    26: "backward: C gradient paired with the previous state",
 }
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -76,6 +83,8 @@ class Oracle:
         lib.ssm_oracle_conv1d_f64.argtypes = [ctypes.c_int] * 5 + [_dp] * 6 + [ctypes.c_int]
         lib.ssm_oracle_conv1d_update_f64.restype = ctypes.c_int
         lib.ssm_oracle_conv1d_update_f64.argtypes = [ctypes.c_int] * 4 + [_dp] * 5 + [ctypes.c_int]
+        lib.ssm_oracle_scan_bwd_f64.restype = ctypes.c_int
+        lib.ssm_oracle_scan_bwd_f64.argtypes = [ctypes.c_int] * 4 + [_dp] * 20 + [ctypes.c_int]
         lib.ssm_oracle_mutant_id.restype = ctypes.c_int
         self._lib = lib
         self.mutant = lib.ssm_oracle_mutant_id()
@@ -129,6 +138,41 @@ class Oracle:
         if rc != 0:
             raise RuntimeError("oracle state update failed with code %d" % rc)
         return y, state
+
+    def scan_bwd(self, x, dt, A, Bm, Cm, dy, dt_bias=None, Dskip=None, z=None, h0=None,
+                 dhL=None, threads=None):
+        """Vector-Jacobian products of scan_fwd (Delta*B form) for the loss
+        sum(dy * y) + sum(dhL * hL).  Returns a dict with dx, ddt, dz (None
+        without z), dBm, dCm, dA, dDskip, ddt_bias and dh0."""
+        x = np.asarray(x)
+        batch, dim, L = x.shape
+        A = np.asarray(A)
+        N = A.shape[1]
+        x = _f64(x, (batch, dim, L), "x")
+        dt = _f64(dt, (batch, dim, L), "dt")
+        A = _f64(A, (dim, N), "A")
+        Bm = _f64(Bm, (batch, N, L), "Bm")
+        Cm = _f64(Cm, (batch, N, L), "Cm")
+        dy = _f64(dy, (batch, dim, L), "dy")
+        dt_bias = _f64(dt_bias, (dim,), "dt_bias")
+        Dskip = _f64(Dskip, (dim,), "Dskip")
+        z = _f64(z, (batch, dim, L), "z")
+        h0 = _f64(h0, (batch, dim, N), "h0")
+        dhL = _f64(dhL, (batch, dim, N), "dhL")
+        g = {k: np.empty(shape, np.float64) for k, shape in (
+            ("dx", (batch, dim, L)), ("ddt", (batch, dim, L)), ("ddt_bias", (dim,)),
+            ("dA", (dim, N)), ("dBm", (batch, N, L)), ("dCm", (batch, N, L)), ("dDskip", (dim,)),
+            ("dh0", (batch, dim, N)))}
+        g["dz"] = np.empty((batch, dim, L), np.float64) if z is not None else None
+        nt = threads or os.cpu_count() or 1
+        rc = self._lib.ssm_oracle_scan_bwd_f64(
+            batch, dim, L, N, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm),
+            _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dhL), _ptr(g["dx"]), _ptr(g["ddt"]),
+            _ptr(g["ddt_bias"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]), _ptr(g["dDskip"]),
+            _ptr(g["dz"]), _ptr(g["dh0"]), int(nt))
+        if rc != 0:
+            raise RuntimeError("oracle scan backward failed with code %d" % rc)
+        return g
 
     def conv1d(self, x, weight, bias=None, state0=None, silu=True, threads=None):
         """Causal depthwise conv: y[batch,dim,L] and the final conv state
@@ -189,6 +233,10 @@ def scan_fwd(*args, **kw):
 
 def state_update(*args, **kw):
     return default().state_update(*args, **kw)
+
+
+def scan_bwd(*args, **kw):
+    return default().scan_bwd(*args, **kw)
 
 
 def conv1d(*args, **kw):

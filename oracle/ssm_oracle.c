@@ -406,3 +406,229 @@ int ssm_oracle_conv1d_update_f64(int batch, int dim, int width, int act, double 
     return ssm_oracle_conv1d_f64(batch, dim, 1, width, act, x, weight, bias, state, y, state,
                                  nthreads);
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass of the scan (B-bar = Delta B form).
+ *
+ * [MAMBA] "Hardware-aware state expansion": the backward pass recomputes the
+ * intermediate states instead of reading them from memory.  The oracle has no
+ * memory constraint: it runs the forward recurrence of one row, keeps every
+ * state h_t, and then applies the chain rule step by step in reverse time.
+ * Loss convention: l = sum(dy * y) + sum(dhL * hL), so the outputs are the
+ * vector-Jacobian products of the scan's forward map.
+ *   dx, ddt, dz          [batch][dim][L]  (ddt is d l / d dt: the raw step)
+ *   dBm, dCm             [batch][N][L]    (summed over channels)
+ *   dA                   [dim][N]         (summed over batch and time)
+ *   dDskip, ddt_bias     [dim]            (summed over batch and time)
+ *   dh0                  [batch][dim][N]
+ * Only the Delta B form of B-bar is differentiated here.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int batch, dim, seqlen, dstate;
+    const double *x, *dt, *dt_bias, *A, *Bm, *Cm, *Dskip, *z, *h0, *dy, *dhL;
+    double *dx, *ddt, *dz, *dh0;
+} bwd_args;
+
+/* Per-thread accumulators for the gradients that sum over rows. */
+typedef struct {
+    double *dBm, *dCm, *dA, *dDskip, *ddt_bias;
+} bwd_acc;
+
+static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+static int bwd_row(const bwd_args *a, const bwd_acc *acc, int b, int d)
+{
+    const int L = a->seqlen, N = a->dstate;
+    const size_t row = ((size_t)b * a->dim + d) * (size_t)L;
+    const double *x = a->x + row, *dt = a->dt + row, *dy = a->dy + row;
+    const double *z = a->z ? a->z + row : NULL;
+    const double *Bm = a->Bm + (size_t)b * N * L;
+    const double *Cm = a->Cm + (size_t)b * N * L;
+    const double *Arow = a->A + (size_t)d * N;
+    const double bias = a->dt_bias ? a->dt_bias[d] : 0.0;
+    const double skip = a->Dskip ? a->Dskip[d] : 0.0;
+    double *hs = (double *)malloc(sizeof(double) * ((size_t)L + 1) * N);
+    double *s = (double *)malloc(sizeof(double) * (size_t)L);
+    double *lam = (double *)malloc(sizeof(double) * (size_t)N);
+    if (!hs || !s || !lam) { free(hs); free(s); free(lam); return -2; }
+
+    /* forward, keeping every state: hs[(t+1) N + n] = h_t[n], hs[n] = h_{-1} */
+    for (int n = 0; n < N; ++n) hs[n] = a->h0 ? a->h0[((size_t)b * a->dim + d) * N + n] : 0.0;
+    for (int t = 0; t < L; ++t) {
+        const double delta = softplus(dt[t] + bias);
+        double acc_s = 0.0;
+        for (int n = 0; n < N; ++n) {
+            const double h = exp(delta * Arow[n]) * hs[(size_t)t * N + n] +
+                             delta * Bm[(size_t)n * L + t] * x[t];
+            hs[(size_t)(t + 1) * N + n] = h;
+            acc_s += Cm[(size_t)n * L + t] * h;
+        }
+        s[t] = acc_s + skip * x[t];
+    }
+
+    /* reverse: lam[n] carries d l / d h_t[n] from the future */
+    for (int n = 0; n < N; ++n) {
+        double g = a->dhL ? a->dhL[((size_t)b * a->dim + d) * N + n] : 0.0;
+#if ORACLE_MUTANT == 23
+        g = 0.0; /* planted: gradient of the final state ignored */
+#endif
+        lam[n] = g;
+    }
+    double dskip = 0.0, dbias = 0.0;
+    for (int t = L - 1; t >= 0; --t) {
+        const double u = dt[t] + bias;
+        const double delta = softplus(u);
+        double ds = dy[t];
+        if (z) {
+            const double sg = sigmoid(z[t]);
+#if ORACLE_MUTANT == 24
+            a->dz[row + t] = dy[t] * s[t] * sg; /* planted: sigmoid for silu' */
+#else
+            a->dz[row + t] = dy[t] * s[t] * sg * (1.0 + z[t] * (1.0 - sg));
+#endif
+            ds = dy[t] * z[t] * sg;
+        }
+        dskip += ds * x[t];
+        double dxt = ds * skip, ddelta = 0.0;
+        for (int n = 0; n < N; ++n) {
+            const double An = Arow[n];
+            const double bn = Bm[(size_t)n * L + t], cn = Cm[(size_t)n * L + t];
+            const double h = hs[(size_t)(t + 1) * N + n];
+            const double hp = hs[(size_t)t * N + n];
+            const double abar = exp(delta * An);
+            lam[n] += ds * cn;                                   /* readout y_t <- C h_t */
+#if ORACLE_MUTANT == 26
+            acc->dCm[((size_t)b * N + n) * L + t] += ds * hp;    /* planted: C meets h_{t-1} */
+#else
+            acc->dCm[((size_t)b * N + n) * L + t] += ds * h;
+#endif
+#if ORACLE_MUTANT == 20
+            ddelta += lam[n] * bn * x[t];                        /* planted: no A-bar term */
+#else
+            ddelta += lam[n] * (An * abar * hp + bn * x[t]);     /* h_t = abar h_{t-1} + delta B x */
+#endif
+#if ORACLE_MUTANT == 21
+            acc->dA[(size_t)d * N + n] += lam[n] * abar * hp;    /* planted: Delta factor dropped */
+#else
+            acc->dA[(size_t)d * N + n] += lam[n] * delta * abar * hp;
+#endif
+            acc->dBm[((size_t)b * N + n) * L + t] += lam[n] * delta * x[t];
+            dxt += lam[n] * delta * bn;
+#if ORACLE_MUTANT != 22
+            lam[n] *= abar;                                      /* -> d l / d h_{t-1} */
+#endif
+        }
+#if ORACLE_MUTANT == 25
+        const double du = ddelta * delta; /* planted: softplus' taken as softplus */
+#else
+        const double du = ddelta * sigmoid(u); /* softplus'(u) = sigmoid(u) */
+#endif
+        a->ddt[row + t] = du;
+        dbias += du;
+        a->dx[row + t] = dxt;
+    }
+    if (a->dh0) {
+        for (int n = 0; n < N; ++n) a->dh0[((size_t)b * a->dim + d) * N + n] = lam[n];
+    }
+    acc->dDskip[d] += dskip;
+    acc->ddt_bias[d] += dbias;
+    free(hs); free(s); free(lam);
+    return 0;
+}
+
+typedef struct {
+    const bwd_args *a;
+    bwd_acc acc;
+    long first, last;
+    int ok;
+} bwd_worker;
+
+static void *bwd_rows(void *p)
+{
+    bwd_worker *w = (bwd_worker *)p;
+    w->ok = 1;
+    for (long r = w->first; r < w->last; ++r) {
+        if (bwd_row(w->a, &w->acc, (int)(r / w->a->dim), (int)(r % w->a->dim)) != 0) w->ok = 0;
+    }
+    return NULL;
+}
+
+/*
+ * Whole-sequence backward.  dhL, z, h0, Dskip, dt_bias may be NULL (zero /
+ * absent); dh0 may be NULL (not returned).  Row-summed gradients are built in
+ * per-thread buffers and added in thread order, so results do not depend on
+ * scheduling.  Returns 0, -1 on bad arguments, -2 on allocation failure.
+ */
+int ssm_oracle_scan_bwd_f64(int batch, int dim, int seqlen, int dstate,
+                            const double *x, const double *dt, const double *dt_bias,
+                            const double *A, const double *Bm, const double *Cm,
+                            const double *Dskip, const double *z, const double *h0,
+                            const double *dy, const double *dhL, double *dx, double *ddt,
+                            double *ddt_bias, double *dA, double *dBm, double *dCm,
+                            double *dDskip, double *dz, double *dh0, int nthreads)
+{
+    if (batch < 1 || dim < 1 || seqlen < 1 || dstate < 1) return -1;
+    if (!x || !dt || !A || !Bm || !Cm || !dy || !dx || !ddt || !ddt_bias || !dA || !dBm ||
+        !dCm || !dDskip)
+        return -1;
+    if (z && !dz) return -1;
+    bwd_args a = {batch, dim, seqlen, dstate, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy, dhL,
+                  dx, ddt, dz, dh0};
+    const long rows = (long)batch * dim;
+    const size_t nbc = (size_t)batch * dstate * seqlen, na = (size_t)dim * dstate;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > rows) nthreads = (int)rows;
+    if (nthreads > 64) nthreads = 64;
+    pthread_t tid[64];
+    int created[64];
+    bwd_worker w[64];
+    int ok = 1;
+    for (int i = 0; i < nthreads; ++i) {
+        w[i].a = &a;
+        w[i].first = rows * i / nthreads;
+        w[i].last = rows * (i + 1) / nthreads;
+        w[i].ok = 0;
+        w[i].acc.dBm = (double *)calloc(nbc, sizeof(double));
+        w[i].acc.dCm = (double *)calloc(nbc, sizeof(double));
+        w[i].acc.dA = (double *)calloc(na, sizeof(double));
+        w[i].acc.dDskip = (double *)calloc((size_t)dim, sizeof(double));
+        w[i].acc.ddt_bias = (double *)calloc((size_t)dim, sizeof(double));
+        if (!w[i].acc.dBm || !w[i].acc.dCm || !w[i].acc.dA || !w[i].acc.dDskip ||
+            !w[i].acc.ddt_bias)
+            ok = 0;
+    }
+    if (ok) {
+        for (int i = 0; i < nthreads; ++i) {
+            created[i] = 0;
+            if (i == 0) continue;
+            if (pthread_create(&tid[i], NULL, bwd_rows, &w[i]) == 0) {
+                created[i] = 1;
+            } else {
+                bwd_rows(&w[i]);
+            }
+        }
+        bwd_rows(&w[0]);
+        for (int i = 1; i < nthreads; ++i) {
+            if (created[i]) pthread_join(tid[i], NULL);
+        }
+        for (int i = 0; i < nthreads; ++i) ok &= w[i].ok;
+    }
+    if (ok) {
+        for (size_t k = 0; k < nbc; ++k) { dBm[k] = 0.0; dCm[k] = 0.0; }
+        for (size_t k = 0; k < na; ++k) dA[k] = 0.0;
+        for (int k = 0; k < dim; ++k) { dDskip[k] = 0.0; ddt_bias[k] = 0.0; }
+        for (int i = 0; i < nthreads; ++i) {
+            for (size_t k = 0; k < nbc; ++k) { dBm[k] += w[i].acc.dBm[k]; dCm[k] += w[i].acc.dCm[k]; }
+            for (size_t k = 0; k < na; ++k) dA[k] += w[i].acc.dA[k];
+            for (int k = 0; k < dim; ++k) {
+                dDskip[k] += w[i].acc.dDskip[k];
+                ddt_bias[k] += w[i].acc.ddt_bias[k];
+            }
+        }
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        free(w[i].acc.dBm); free(w[i].acc.dCm); free(w[i].acc.dA);
+        free(w[i].acc.dDskip); free(w[i].acc.ddt_bias);
+    }
+    return ok ? 0 : -2;
+}

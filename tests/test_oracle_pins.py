@@ -390,10 +390,82 @@ def pin_conv_decode_equals_prefill(o):
     np.testing.assert_array_equal(state, sL)
 
 
+# --------------------------------------------------------------------------
+# Backward pass ("Hardware-aware state expansion": the backward recomputes the
+# states).  The oracle returns the vector-Jacobian products of the forward
+# map for l = sum(dy * y) + sum(dhL * hL); these pins tie it to the (pinned)
+# forward oracle.
+# --------------------------------------------------------------------------
+def _bwd_problem(seed, batch=2, dim=3, L=23, N=4):
+    rng = np.random.default_rng(seed)
+    p = _rand_problem(rng, batch, dim, L, N)
+    dy = rng.standard_normal((batch, dim, L))
+    dhL = rng.standard_normal((batch, dim, N))
+    return rng, p, dy, dhL
+
+
+def _loss(o, p, dy, dhL):
+    y, hL = o.scan_fwd(**p)
+    return float((dy * y).sum() + (dhL * hL).sum())
+
+
+def pin_bwd_linear_inputs(o):
+    """The loss is affine in each of x, h0, Bm, Cm and Dskip when the other
+    inputs are held fixed, so the directional derivative along v is exactly
+    l(input = v) - l(input = 0): <grad, v> must match it to rounding (no step
+    size involved)."""
+    rng, p, dy, dhL = _bwd_problem(41)
+    g = o.scan_bwd(dy=dy, dhL=dhL, **p)
+    for name, gname in (("x", "dx"), ("h0", "dh0"), ("Bm", "dBm"), ("Cm", "dCm"),
+                        ("Dskip", "dDskip")):
+        v = rng.standard_normal(p[name].shape)
+        lhs = (_loss(o, {**p, name: v}, dy, dhL)
+               - _loss(o, {**p, name: np.zeros_like(v)}, dy, dhL))
+        rhs = float((g[gname] * v).sum())
+        assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs)), (name, lhs, rhs)
+
+
+def pin_bwd_finite_differences(o):
+    """Central differences of the forward oracle along random directions, for
+    every input including the non-linear ones (dt, dt_bias, A, z)."""
+    rng, p, dy, dhL = _bwd_problem(42)
+    g = o.scan_bwd(dy=dy, dhL=dhL, **p)
+    names = {"x": "dx", "dt": "ddt", "dt_bias": "ddt_bias", "A": "dA", "Bm": "dBm", "Cm": "dCm",
+             "Dskip": "dDskip", "z": "dz", "h0": "dh0"}
+    eps = 1e-6
+    for name, gname in names.items():
+        v = rng.standard_normal(p[name].shape)
+        fd = (_loss(o, {**p, name: p[name] + eps * v}, dy, dhL)
+              - _loss(o, {**p, name: p[name] - eps * v}, dy, dhL)) / (2 * eps)
+        an = float((g[gname] * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+def pin_bwd_no_gate_no_state(o):
+    """Without gate, skip, bias and h0 the same identities hold, and the
+    returned dh0 is the adjoint at t = -1 (finite differences through h0)."""
+    rng, p, dy, dhL = _bwd_problem(43, L=9, N=2)
+    for k in ("z", "Dskip", "dt_bias", "h0"):
+        p[k] = None
+    g = o.scan_bwd(dy=dy, dhL=dhL, **p)
+    assert g["dz"] is None
+    v = rng.standard_normal(dhL.shape)
+    eps = 1e-6
+    fd = (_loss(o, {**p, "h0": eps * v}, dy, dhL) - _loss(o, {**p, "h0": -eps * v}, dy, dhL)) / (2 * eps)
+    assert abs(fd - float((g["dh0"] * v).sum())) <= 1e-7 * max(1.0, abs(fd))
+    v = rng.standard_normal(p["dt"].shape)
+    fd = (_loss(o, {**p, "dt": p["dt"] + eps * v}, dy, dhL)
+          - _loss(o, {**p, "dt": p["dt"] - eps * v}, dy, dhL)) / (2 * eps)
+    assert abs(fd - float((g["ddt"] * v).sum())) <= 1e-6 * max(1.0, abs(fd))
+    # the bias gradient is the time-and-batch sum of the dt gradient
+    np.testing.assert_allclose(g["ddt_bias"], g["ddt"].sum(axis=(0, 2)), rtol=1e-12, atol=1e-13)
+
+
 PINS = [pin_hand_examples, pin_lti_convolution, pin_small_delta, pin_large_delta, pin_gated_rnn,
         pin_bracketings, pin_split_resume, pin_decode_equals_scan, pin_linearity,
         pin_equivariance, pin_softplus_silu, pin_conv_hand_examples, pin_conv_library,
-        pin_conv_impulse, pin_conv_split_resume, pin_conv_decode_equals_prefill]
+        pin_conv_impulse, pin_conv_split_resume, pin_conv_decode_equals_prefill,
+        pin_bwd_linear_inputs, pin_bwd_finite_differences, pin_bwd_no_gate_no_state]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
