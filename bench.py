@@ -44,6 +44,7 @@ SLOTS_PER_ROW_STEP = 1 + (TRANS_SLOTS + 1 + TRANS_SLOTS) + 1 + 1 + (TRANS_SLOTS 
 
 COUNTERS = os.path.join(ROOT, "profiles", "scan_fwd_counters.json")
 KERNEL_SOURCES = ("selective_state_space_64_amd/csrc/scan_fwd.hip",
+                  "selective_state_space_64_amd/csrc/scan_common.hpp",
                   "selective_state_space_64_amd/csrc/ssm_device.hpp")
 
 
@@ -266,6 +267,34 @@ def bench_conv(torch, ssm, synth, wl, x, launches=20):
     return out
 
 
+def bench_bwd(torch, ssm, wl, t, launches=10):
+    """Backward pass (all three launches of one ssm_scan_bwd call) on the
+    layer, dy ~ N(0, 1) fp32, gradients fp32."""
+    dy = torch.randn((wl.batch, wl.dim, wl.seqlen), device="cuda")
+    ws = torch.empty(ssm.lib().ssm_scan_bwd_workspace_bytes(wl.batch, wl.dim, wl.seqlen, wl.dstate),
+                     dtype=torch.uint8, device="cuda")
+
+    def call():
+        return ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy, dt_bias=t["dt_bias"],
+                                Dskip=t["Dskip"], z=t["z"], workspace=ws)
+
+    for _ in range(2):
+        call()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for e0, e1 in evs:
+        e0.record(stream)
+        call()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
+    return {"workload": "scan backward, %s" % wl.name, "ms_mean": ms,
+            "elements_per_s": elems / (ms * 1e-3),
+            "note": "zero-fill + chunk-state recompute + reverse pass; includes output allocation"}
+
+
 def main():
     args = parse()
     if args.ingest_counters:
@@ -371,6 +400,7 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(torch, ssm, synth)
         result["conv1d"] = bench_conv(torch, ssm, synth, wl, t["x"])
+        result["backward"] = bench_bwd(torch, ssm, wl, t)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(result), flush=True)

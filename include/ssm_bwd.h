@@ -1,0 +1,71 @@
+/*
+ * ssm_bwd.h -- C ABI of the backward pass of the selective scan (gfx950).
+ *
+ * The page "Mamba: Linear-Time Sequence Modeling with Selective State Spaces"
+ * ("Hardware-aware state expansion") describes the fused kernel's backward
+ * pass: the intermediate states are recomputed on chip rather than stored
+ * in and read back from HBM.  ssm_scan_bwd returns the gradients of
+ *     l = sum(dy * y) + sum(dhL * hL)
+ * with respect to every input of ssm_scan_fwd (see ssm.h for the forward map
+ * and layouts), for the Delta * B form of B-bar (flags must be 0: the exact
+ * zero-order-hold form has no backward here).
+ *
+ * Per (b, d), with u_t = dt_t + dt_bias, Delta_t = softplus(u_t),
+ * A-bar_t = exp(Delta_t A), s_t = C_t . h_t + Dskip x_t, ds_t = dy_t silu(z_t):
+ *     lambda_t = ds_t C_t + A-bar_{t+1} lambda_{t+1},  lambda_{L-1} = ds C + dhL
+ *     dx_t = Dskip ds_t + sum_n lambda_t Delta_t B_t
+ *     ddt_t = sigmoid(u_t) sum_n lambda_t (A A-bar_t h_{t-1} + B_t x_t)
+ *     dz_t = dy_t s_t silu'(z_t)
+ *     dBm[b,n,t] = sum_d lambda_t Delta_t x_t,   dCm[b,n,t] = sum_d ds_t h_t
+ *     dA[d,n] = sum_{b,t} lambda_t Delta_t A-bar_t h_{t-1}
+ *     dDskip[d] = sum_{b,t} ds_t x_t,  ddt_bias[d] = sum_{b,t} ddt_t
+ *     dh0 = A-bar_0 lambda_0
+ *
+ * Conventions are those of ssm.h (caller-owned device pointers, densely
+ * packed, nothing allocated; argument errors return before any launch and
+ * write nothing; SSM_ERR_HIP on a failed launch; asynchronous on `stream`).
+ * The sums over channels and over batch and time are accumulated with fp32
+ * atomic adds, so their rounding (not their value) may differ between runs.
+ */
+#ifndef SSM_BWD_H
+#define SSM_BWD_H
+
+#include "ssm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Device workspace ssm_scan_bwd needs: the recomputed state entering every
+ * 128-step chunk, batch * dim * ceil(seqlen / 128) * dstate fp32 values. */
+size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
+
+/*
+ * Inputs: the forward inputs exactly as given to ssm_scan_fwd, plus
+ *   dy       [batch][dim][seqlen]  grad_dtype  gradient of y
+ *   dhL      [batch][dim][dstate]  fp32 gradient of the final state, or NULL (zero)
+ * Outputs (all overwritten; none may overlap an input, another output or
+ * the workspace):
+ *   dx, ddt  [batch][dim][seqlen]  grad_dtype (ddt: gradient of the raw dt)
+ *   dz       [batch][dim][seqlen]  grad_dtype; required when z is given,
+ *            ignored (may be NULL) otherwise
+ *   dBm, dCm [batch][dstate][seqlen] fp32
+ *   dA       [dim][dstate] fp32
+ *   dDskip, ddt_bias [dim] fp32, or NULL (not computed)
+ *   dh0      [batch][dim][dstate] fp32, or NULL (not returned)
+ *   workspace, workspace_bytes: at least ssm_scan_bwd_workspace_bytes(...)
+ * Supported sizes: as ssm_scan_fwd.
+ */
+ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+                          unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                          const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                          const void *z, const float *h0, ssm_dtype_t grad_dtype,
+                          const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                          float *dBm, float *dCm, float *dA, float *dDskip, float *ddt_bias,
+                          float *dh0, void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_BWD_H */

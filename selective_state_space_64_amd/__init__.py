@@ -1,7 +1,7 @@
 """Selective state-space (S6) scan for AMD MI355X (gfx950).
 
-Thin Python binding over the C ABI in ``include/ssm.h`` and
-``include/ssm_conv.h`` (``libssm.so``):
+Thin Python binding over the C ABI in ``include/ssm.h``, ``include/ssm_bwd.h``
+and ``include/ssm_conv.h`` (``libssm.so``):
 argument marshalling only.  Every step of the computation runs in the HIP
 kernels of ``csrc/``; PyTorch only provides device memory and the stream.
 There is no CPU fallback: if the library is missing or no GPU is present the
@@ -9,6 +9,7 @@ calls raise.
 
     y, hL = ssm_scan_fwd(x, dt, A, Bm, Cm, dt_bias=..., Dskip=..., z=..., h0=...)
     y = ssm_state_update(state, x, dt, A, Bm, Cm, dt_bias=..., Dskip=..., z=...)
+    grads = ssm_scan_bwd(x, dt, A, Bm, Cm, dy, dt_bias=..., Dskip=..., z=..., h0=..., dhL=...)
     y, stateL = ssm_conv1d_fwd(x, weight, bias=..., state0=..., silu=True)
     y = ssm_conv1d_update(state, x, weight, bias=..., silu=True)
 
@@ -33,7 +34,8 @@ STATUS = {
     7: "SSM_ERR_WORKSPACE", 8: "SSM_ERR_HIP",
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
-           "ssm_scan_fwd", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_update"]
+           "ssm_scan_fwd", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_update",
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd"]
 
 
 class SSMError(RuntimeError):
@@ -64,6 +66,10 @@ def lib():
         L.ssm_scan_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 9 + [i, vp, vp, vp, sz, vp]
         L.ssm_state_update.restype = i
         L.ssm_state_update.argtypes = [i, i, i, i, u] + [vp] * 9 + [i, vp, vp]
+        L.ssm_scan_bwd_workspace_bytes.restype = sz
+        L.ssm_scan_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        L.ssm_scan_bwd.restype = i
+        L.ssm_scan_bwd.argtypes = [i, i, i, i, i, u] + [vp] * 9 + [i] + [vp] * 12 + [sz, vp]
         L.ssm_conv1d_fwd.restype = i
         L.ssm_conv1d_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 4 + [i, vp, vp, vp]
         L.ssm_conv1d_update.restype = i
@@ -159,6 +165,51 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     return y
 
 
+def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=None, dhL=None,
+                 grad_dtype=torch.float32, workspace=None, stream=None):
+    """Gradients of sum(dy * y) + sum(dhL * hL) through ssm_scan_fwd (Delta*B
+    form).  Returns a dict: dx, ddt, dz (None without z) in grad_dtype; dBm,
+    dCm, dA, dDskip, ddt_bias, dh0 in fp32 (dDskip / ddt_bias / dh0 are
+    computed for every call)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    N = A.shape[-1]
+    ind, dev, f32 = x.dtype, x.device, torch.float32
+    g = {
+        "dx": torch.empty((batch, dim, L), dtype=grad_dtype, device=dev),
+        "ddt": torch.empty((batch, dim, L), dtype=grad_dtype, device=dev),
+        "dz": torch.empty((batch, dim, L), dtype=grad_dtype, device=dev) if z is not None else None,
+        "dBm": torch.empty((batch, N, L), dtype=f32, device=dev),
+        "dCm": torch.empty((batch, N, L), dtype=f32, device=dev),
+        "dA": torch.empty((dim, N), dtype=f32, device=dev),
+        "dDskip": torch.empty((dim,), dtype=f32, device=dev),
+        "ddt_bias": torch.empty((dim,), dtype=f32, device=dev),
+        "dh0": torch.empty((batch, dim, N), dtype=f32, device=dev),
+    }
+    need = lib().ssm_scan_bwd_workspace_bytes(batch, dim, L, N)
+    if workspace is None:
+        workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+    args = [
+        _ptr(x, "x", (batch, dim, L), ind), _ptr(dt, "dt", (batch, dim, L), ind),
+        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
+        _ptr(Bm, "Bm", (batch, N, L), ind), _ptr(Cm, "Cm", (batch, N, L), ind),
+        _ptr(Dskip, "Dskip", (dim,), f32), _ptr(z, "z", (batch, dim, L), ind),
+        _ptr(h0, "h0", (batch, dim, N), f32),
+    ]
+    gargs = [
+        _ptr(dy, "dy", (batch, dim, L), grad_dtype), _ptr(dhL, "dhL", (batch, dim, N), f32),
+        _ptr(g["dx"], "dx"), _ptr(g["ddt"], "ddt"), _ptr(g["dz"], "dz"), _ptr(g["dBm"], "dBm"),
+        _ptr(g["dCm"], "dCm"), _ptr(g["dA"], "dA"), _ptr(g["dDskip"], "dDskip"),
+        _ptr(g["ddt_bias"], "ddt_bias"), _ptr(g["dh0"], "dh0"),
+    ]
+    st = lib().ssm_scan_bwd(batch, dim, L, N, _dtype_code(ind), 0, *args, _dtype_code(grad_dtype),
+                            *gargs, _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                            _stream(stream, dev))
+    _check(st)
+    return g
+
+
 def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=None,
                    return_final_state=True, y=None, stateL=None, stream=None):
     """Causal depthwise conv over [batch, dim, L]; returns (y, stateL).
@@ -203,6 +254,7 @@ def ssm_conv1d_update(state, x, weight, *, bias=None, silu=True, out_dtype=None,
 
 
 scan_fwd = ssm_scan_fwd
+scan_bwd = ssm_scan_bwd
 state_update = ssm_state_update
 conv1d_fwd = ssm_conv1d_fwd
 conv1d_update = ssm_conv1d_update

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssm.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["ssm_api.hip", "scan_fwd.hip", "state_update.hip", "conv1d.hip"]
+SOURCES = ["ssm_api.hip", "scan_fwd.hip", "state_update.hip", "conv1d.hip", "scan_bwd.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of the generated code on purpose.
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

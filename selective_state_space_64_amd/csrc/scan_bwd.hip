@@ -1,0 +1,484 @@
+// scan_bwd.hip -- backward pass of the fused selective scan for gfx950.
+//
+// Gradients of l = sum(dy * y) + sum(dhL * hL) through the forward map of
+// scan_fwd.hip (B-bar = Delta B), with the states recomputed on chip instead
+// of being stored ("Hardware-aware state expansion" section of the page
+// "Mamba: Linear-Time Sequence Modeling with Selective State Spaces": the
+// backward pass recomputes the intermediate states).  Per (b, d) the adjoint
+//     lambda_t = ds_t C_t + A-bar_{t+1} lambda_{t+1},   ds_t = dy_t silu(z_t)
+// runs backwards in time; with hp_t = A-bar_t h_{t-1} = h_t - Delta_t B_t x_t
+//     dx_t      = Dskip ds_t + sum_n lambda_t Delta_t B_t
+//     dDelta_t  = sum_n lambda_t (A hp_t + B_t x_t),   ddt_t = dDelta_t sigmoid(u_t)
+//     dA[d,n]  += lambda_t Delta_t hp_t                 dBm[b,n,t] += lambda_t Delta_t x_t
+//     dCm[b,n,t] += ds_t h_t                            dz_t = dy_t s_t silu'(z_t)
+// where s_t = C_t . h_t + Dskip x_t is the forward readout before the gate.
+//
+// Three launches:
+//   1. zero the gradients that are sums over rows (dBm, dCm, dA, dDskip, ddt_bias);
+//   2. chunk_states_kernel: the forward recurrence once more, keeping only the
+//      state entering every 128-step chunk (the workspace, batch*dim*chunks*N
+//      floats);
+//   3. scan_bwd_kernel: chunks in reverse order.  Per chunk and state n the
+//      workgroup recomputes the chunk's states from its checkpoint with the
+//      forward in-row scan, folds the adjoint of each lane's 8 steps into an
+//      affine map, composes the maps of a row with the mirrored (reverse
+//      time) DPP scan, replays the lane's steps backwards and accumulates the
+//      gradients.  Sums over channels (dBm, dCm) go through LDS atomics per
+//      chunk, then one global atomic add per (n, t) per workgroup.
+// The layout and lane mapping are those of the forward kernel: a workgroup
+// owns one batch row and 16 channels, each 16-lane DPP row one channel, lane
+// j the steps [l0 + 8j, l0 + 8j + 8) of a chunk.
+#include "scan_common.hpp"
+#include "ssm_device.hpp"
+#include "ssm_launch.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kRowB = 16;
+constexpr int kWavesB = 4;
+constexpr int kThreadsB = 64 * kWavesB;
+constexpr int kChanB = kThreadsB / kRowB;  // channels per workgroup
+constexpr int kKB = 4;                     // consecutive steps per lane
+constexpr int kTB = kRowB * kKB;           // steps per chunk
+
+struct BwdParams {
+    int dim, seqlen, nchunks;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *h0;
+    const void *dy;
+    const float *dhL;
+    void *dx, *ddt, *dz;
+    float *dBm, *dCm, *dA, *dDskip, *ddt_bias, *dh0;
+    float *ck;  // [batch][dim][nchunks][N] state entering each chunk
+};
+
+// A lane's run of K = 4 steps is 8 bytes of bf16 or 16 bytes of fp32: one
+// vector access when the address allows it, else guarded element accesses
+// (count = steps inside the sequence; the rest read as 0 / are not written).
+static_assert(kKB == 4, "run helpers below move exactly 4 elements");
+
+template <typename T>
+__device__ inline bool run_aligned(const T *q)
+{
+    return (reinterpret_cast<uintptr_t>(q) & (4 * sizeof(T) - 1)) == 0;
+}
+
+template <typename T>
+__device__ inline void load4(const T *q, int count, float *out)
+{
+    if (count == 4 && run_aligned(q)) {
+        if constexpr (sizeof(T) == 4) {
+            const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(q));
+            out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+        } else {
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(q));
+            out[0] = io<bf16_t>::lo(v.x); out[1] = io<bf16_t>::hi(v.x);
+            out[2] = io<bf16_t>::lo(v.y); out[3] = io<bf16_t>::hi(v.y);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = (i < count) ? io<T>::load1(q + i) : 0.0f;
+    }
+}
+
+template <typename T>
+__device__ inline void store4(T *q, int count, const float *v)
+{
+    if (count == 4 && run_aligned(q)) {
+        if constexpr (sizeof(T) == 4) {
+            *reinterpret_cast<f32x4 *>(q) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2 *>(q) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i >= count) continue;
+            if constexpr (sizeof(T) == 4) {
+                reinterpret_cast<float *>(q)[i] = v[i];
+            } else {
+                reinterpret_cast<uint16_t *>(q)[i] = uint16_t(pack_bf16x2(v[i], 0.0f) & 0xffffu);
+            }
+        }
+    }
+}
+
+__device__ inline float sigmoid_hw(float v) { return rcp_hw(1.0f + exp2_hw(-v * kLog2e)); }
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
+__device__ inline float row_sum(float v)
+{
+    v += __shfl_xor(v, 8, kRowB);
+    v += __shfl_xor(v, 4, kRowB);
+    v += __shfl_xor(v, 2, kRowB);
+    v += __shfl_xor(v, 1, kRowB);
+    return v;
+}
+
+// Bm or Cm of one chunk into LDS as fp32, layout [n][q][lane] of float4 (the
+// forward kernel's layout): thread (sn, sj) stages the K steps of lane sj.
+template <typename Tin, int K>
+__device__ inline void stage_chunk(float4 *dst, const Tin *src, int L, int chunk, int sn, int sj)
+{
+    constexpr int T = kRowB * K, Q = K / 4;
+    const int l = chunk * T + sj * K;
+    const int cnt = max(0, min(K, L - l));
+    const Tin *q = src + size_t(sn) * size_t(L) + l;
+    float v[K];
+    load4<Tin>(q, cnt, v);
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+        dst[(sn * Q + i) * kRowB + sj] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+}
+
+template <int K>
+__device__ inline void lds_run(const float4 *src, float *v)
+{
+#pragma unroll
+    for (int q = 0; q < K / 4; ++q) {
+        const float4 w = src[q * kRowB];
+        v[4 * q] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+    }
+}
+
+__global__ void bwd_zero_kernel(float *a, size_t na, float *b, size_t nb, float *c, size_t nc,
+                                float *d, size_t nd, float *e, size_t ne)
+{
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < na; i += stride) a[i] = 0.0f;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nb; i += stride) b[i] = 0.0f;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nc; i += stride) c[i] = 0.0f;
+    if (d)
+        for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nd; i += stride) d[i] = 0.0f;
+    if (e)
+        for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < ne; i += stride) e[i] = 0.0f;
+}
+
+// The state entering every chunk, from the forward recurrence (per state:
+// lane fold, row scan, carry).
+template <typename Tin, int N>
+__global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
+{
+    constexpr int K = kKB, T = kTB, Q = K / 4, NP = N + 1;
+    __shared__ float4 sB[N * Q * kRowB];
+    __shared__ float sAP[kChanB * NP];
+    __shared__ float sCar[kChanB * NP];
+
+    const int tid = threadIdx.x, j = tid & (kRowB - 1), c = tid / kRowB;
+    const int b = blockIdx.y, dim = p.dim, L = p.seqlen;
+    const int d = int(blockIdx.x) * kChanB + c;
+    const bool live = d < dim;
+    const int dc = live ? d : dim - 1;
+    const size_t rowo = (size_t(b) * dim + dc) * size_t(L);
+    const Tin *xr = static_cast<const Tin *>(p.x) + rowo;
+    const Tin *dtr = static_cast<const Tin *>(p.dt) + rowo;
+    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * N * L;
+
+    for (int s = tid; s < kChanB * NP; s += kThreadsB) {
+        const int cc = s / NP, n = s % NP;
+        const int dd = min(int(blockIdx.x) * kChanB + cc, dim - 1);
+        sAP[s] = n < N ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
+        sCar[s] = (n < N && p.h0) ? p.h0[(size_t(b) * dim + dd) * N + n] : 0.0f;
+    }
+    const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    const bool stager = tid < N * kRowB;
+    const int sn = stager ? tid / kRowB : 0, sj = tid % kRowB;
+    const float *ap = sAP + c * NP;
+    float *car = sCar + c * NP;
+
+    for (int ch = 0; ch < p.nchunks; ++ch) {
+        lds_barrier();
+        if (stager) stage_chunk<Tin, K>(sB, Bb, L, ch, sn, sj);
+        const int l0 = ch * T + j * K;
+        const int cnt = max(0, min(K, L - l0));
+        float xv[K], dv[K], delta[K], w[K];
+        load4<Tin>(xr + l0, cnt, xv);
+        load4<Tin>(dtr + l0, cnt, dv);
+        float sumd = 0.0f;
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+            const float dl = softplus(dv[i] + bias);
+            delta[i] = i < cnt ? dl : 0.0f;
+            w[i] = delta[i] * xv[i];
+            sumd += delta[i];
+        }
+        lds_barrier();
+        const float4 *bp = sB + j;
+#pragma unroll 1
+        for (int n = 0; n < N; ++n) {
+            const float a1 = ap[n];
+            float bv[K];
+            lds_run<K>(bp + n * Q * kRowB, bv);
+            float hl = w[0] * bv[0];
+#pragma unroll
+            for (int i = 1; i < K; ++i) hl = __builtin_fmaf(exp2_hw(delta[i] * a1), hl, w[i] * bv[i]);
+            float aa = exp2_hw(sumd * a1);
+            const float cin = car[n];
+            float hend, h = cin;
+            row_scan(aa, hl, hend, h);
+            if (j == kRowB - 1) car[n] = hend;
+            if (j == 0 && live) p.ck[((size_t(b) * dim + d) * p.nchunks + ch) * N + n] = cin;
+        }
+    }
+}
+
+template <typename Tin, typename Tg, int N>
+__global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
+{
+    constexpr int K = kKB, T = kTB, Q = K / 4, NP = N + 1;
+    __shared__ float4 sB[N * Q * kRowB];
+    __shared__ float4 sC[N * Q * kRowB];
+    // Per-channel dBm / dCm terms of one state, double-buffered by state
+    // parity: [buffer][dBm, dCm][channel][step].
+    __shared__ float4 sP[2][2][kChanB][T / 4];
+    __shared__ float sAP[kChanB * NP];  // A * log2(e)
+    __shared__ float sH[kChanB * NP];   // forward state entering the chunk
+    __shared__ float sMu[kChanB * NP];  // adjoint entering the chunk from its right
+    __shared__ float sDA[kChanB * NP];  // dA partial sums
+
+    const int tid = threadIdx.x, j = tid & (kRowB - 1), c = tid / kRowB;
+    const int b = blockIdx.y, dim = p.dim, L = p.seqlen;
+    const int d = int(blockIdx.x) * kChanB + c;
+    const bool live = d < dim;
+    const int dc = live ? d : dim - 1;
+    const size_t rowo = (size_t(b) * dim + dc) * size_t(L);
+    const Tin *xr = static_cast<const Tin *>(p.x) + rowo;
+    const Tin *dtr = static_cast<const Tin *>(p.dt) + rowo;
+    const Tin *zr = p.z ? static_cast<const Tin *>(p.z) + rowo : nullptr;
+    const Tg *dyr = static_cast<const Tg *>(p.dy) + rowo;
+    Tg *dxr = static_cast<Tg *>(p.dx) + rowo;
+    Tg *ddtr = static_cast<Tg *>(p.ddt) + rowo;
+    Tg *dzr = p.dz ? static_cast<Tg *>(p.dz) + rowo : nullptr;
+    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * N * L;
+    const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * N * L;
+
+    for (int s = tid; s < kChanB * NP; s += kThreadsB) {
+        const int cc = s / NP, n = s % NP;
+        const int dd = min(int(blockIdx.x) * kChanB + cc, dim - 1);
+        sAP[s] = n < N ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
+        sMu[s] = (n < N && p.dhL) ? p.dhL[(size_t(b) * dim + dd) * N + n] : 0.0f;
+        sDA[s] = 0.0f;
+    }
+    const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
+    const bool stager = tid < N * kRowB;
+    const int sn = stager ? tid / kRowB : 0, sj = tid % kRowB;
+    const float *ap = sAP + c * NP;
+    const float *hs = sH + c * NP;
+    float *mus = sMu + c * NP;
+    float *das = sDA + c * NP;
+    float dskip_acc = 0.0f, dbias_acc = 0.0f;
+
+    for (int ch = p.nchunks - 1; ch >= 0; --ch) {
+        lds_barrier();
+        if (stager) {
+            stage_chunk<Tin, K>(sB, Bb, L, ch, sn, sj);
+            stage_chunk<Tin, K>(sC, Cb, L, ch, sn, sj);
+        }
+        for (int s = tid; s < kChanB * N; s += kThreadsB) {
+            const int cc = s / N, n = s % N;
+            const int dd = min(int(blockIdx.x) * kChanB + cc, dim - 1);
+            sH[cc * NP + n] = p.ck[((size_t(b) * dim + dd) * p.nchunks + ch) * N + n];
+        }
+
+        // Per-step quantities of this lane's K steps.  Steps past the end of
+        // the sequence and dead channels get Delta = 0 and ds = 0: identity
+        // maps that add nothing to any sum.
+        const int l0 = ch * T + j * K;
+        const int cnt = live ? max(0, min(K, L - l0)) : 0;
+        float xv[K], delta[K], ds[K], sacc[K], gx[K], gdel[K], sgu[K], gzf[K];
+        float sumd = 0.0f;
+        {
+            float dv[K], gy[K], zv[K];
+            load4<Tin>(xr + l0, cnt, xv);
+            load4<Tin>(dtr + l0, cnt, dv);
+            load4<Tg>(dyr + l0, cnt, gy);
+            if (zr) load4<Tin>(zr + l0, cnt, zv);
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                const bool in = i < cnt;
+                const float uv = dv[i] + bias;
+                const float dl = softplus(uv);
+                delta[i] = in ? dl : 0.0f;
+                sgu[i] = sigmoid_hw(uv);  // softplus'(u)
+                float g = 1.0f;
+                gzf[i] = 0.0f;
+                if (zr) {
+                    const float sz = sigmoid_hw(zv[i]);
+                    g = zv[i] * sz;                                            // silu(z)
+                    gzf[i] = gy[i] * (sz * __builtin_fmaf(zv[i], 1.0f - sz, 1.0f));  // dy silu'(z)
+                }
+                ds[i] = in ? gy[i] * g : 0.0f;
+                sacc[i] = skip * xv[i];
+                gx[i] = skip * ds[i];
+                gdel[i] = 0.0f;
+                sumd += delta[i];
+                dskip_acc = __builtin_fmaf(ds[i], xv[i], dskip_acc);
+            }
+        }
+        lds_barrier();
+
+        const float4 *bp = sB + j, *cp = sC + j;
+#pragma unroll 1
+        for (int n = 0; n < N; ++n) {
+            const float a1 = ap[n];
+            const float An = a1 * kLn2;
+            float bv[K], cv[K], da[K], hh[K];
+            lds_run<K>(bp + n * Q * kRowB, bv);
+            lds_run<K>(cp + n * Q * kRowB, cv);
+
+            // forward states of this chunk, from the checkpoint (the input
+            // term Delta x B is recomputed where needed to save registers)
+#pragma unroll
+            for (int i = 0; i < K; ++i) da[i] = exp2_hw(delta[i] * a1);
+            float hl = (delta[0] * xv[0]) * bv[0];
+#pragma unroll
+            for (int i = 1; i < K; ++i) hl = __builtin_fmaf(da[i], hl, (delta[i] * xv[i]) * bv[i]);
+            const float ptot = exp2_hw(sumd * a1);
+            float aa = ptot;
+            float hend, h = hs[n];
+            row_scan(aa, hl, hend, h);
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                h = __builtin_fmaf(da[i], h, (delta[i] * xv[i]) * bv[i]);
+                hh[i] = h;
+                sacc[i] = __builtin_fmaf(cv[i], h, sacc[i]);
+            }
+
+            // adjoint: lane map mu_out = ptot mu_in + q over the lane's steps,
+            // mu = A-bar lambda of the step just after the lane's last one
+            float q = ds[K - 1] * cv[K - 1];
+#pragma unroll
+            for (int i = K - 2; i >= 0; --i) q = __builtin_fmaf(da[i + 1], q, ds[i] * cv[i]);
+            float pm = ptot, qm = da[0] * q;
+            float mend, mu = mus[n];
+            row_scan_rev(pm, qm, mend, mu);
+            if (j == 0) {
+                mus[n] = mend;
+                if (ch == 0 && live && p.dh0) p.dh0[(size_t(b) * dim + d) * N + n] = mend;
+            }
+            float lam = mu, dap = 0.0f, gbv[K], gcv[K];
+#pragma unroll
+            for (int i = K - 1; i >= 0; --i) {
+                lam = __builtin_fmaf(ds[i], cv[i], lam);
+                const float wx = delta[i] * xv[i];
+                const float hpa = hh[i] - wx * bv[i];  // A-bar h_{t-1}
+                gdel[i] = __builtin_fmaf(lam, __builtin_fmaf(bv[i], xv[i], An * hpa), gdel[i]);
+                const float ld = lam * delta[i];
+                dap = __builtin_fmaf(ld, hpa, dap);
+                gx[i] = __builtin_fmaf(ld, bv[i], gx[i]);
+                gbv[i] = lam * wx;
+                gcv[i] = ds[i] * hh[i];
+                lam *= da[i];
+            }
+            dap = row_sum(dap);
+            if (j == 0) das[n] += dap;
+
+            // dBm[b, n, t] and dCm[b, n, t] sum over channels: each lane
+            // leaves its terms in LDS, then one thread per (quantity, step)
+            // adds the 16 channels and issues one global atomic add.
+            const int pb = n & 1;
+#pragma unroll
+            for (int q4 = 0; q4 < K / 4; ++q4) {
+                sP[pb][0][c][j * (K / 4) + q4] =
+                    make_float4(gbv[4 * q4], gbv[4 * q4 + 1], gbv[4 * q4 + 2], gbv[4 * q4 + 3]);
+                sP[pb][1][c][j * (K / 4) + q4] =
+                    make_float4(gcv[4 * q4], gcv[4 * q4 + 1], gcv[4 * q4 + 2], gcv[4 * q4 + 3]);
+            }
+            lds_barrier();
+            if (tid < 2 * T) {
+                const int qq = tid / T, t = tid % T;
+                const float *col = reinterpret_cast<const float *>(&sP[pb][qq][0][0]) + t;
+                float acc = 0.0f;
+#pragma unroll
+                for (int cc = 0; cc < kChanB; ++cc) acc += col[cc * T];
+                const int tt = ch * T + t;
+                if (tt < L) atomicAdd(&(qq ? p.dCm : p.dBm)[(size_t(b) * N + n) * L + tt], acc);
+            }
+        }
+
+        // per-step gradients of this chunk
+        {
+            float gdt[K], gz[K];
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                gdt[i] = gdel[i] * sgu[i];
+                dbias_acc += i < cnt ? gdt[i] : 0.0f;
+                gz[i] = gzf[i] * sacc[i];
+            }
+            if (cnt > 0) {
+                store4<Tg>(dxr + l0, cnt, gx);
+                store4<Tg>(ddtr + l0, cnt, gdt);
+                if (zr) store4<Tg>(dzr + l0, cnt, gz);
+            }
+        }
+
+    }
+
+    lds_barrier();
+    for (int s = tid; s < kChanB * N; s += kThreadsB) {
+        const int cc = s / N, n = s % N;
+        const int dd = int(blockIdx.x) * kChanB + cc;
+        if (dd < dim) atomicAdd(&p.dA[size_t(dd) * N + n], sDA[cc * NP + n]);
+    }
+    dskip_acc = row_sum(dskip_acc);
+    dbias_acc = row_sum(dbias_acc);
+    if (j == 0 && live) {
+        if (p.dDskip) atomicAdd(&p.dDskip[d], dskip_acc);
+        if (p.ddt_bias) atomicAdd(&p.ddt_bias[d], dbias_acc);
+    }
+}
+
+template <typename Tin, typename Tg, int N>
+hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
+{
+    BwdParams p{a.dim, a.seqlen, (a.seqlen + kTB - 1) / kTB, a.x, a.dt, a.dt_bias, a.A, a.Bm,
+                a.Cm, a.Dskip, a.z, a.h0, a.dy, a.dhL, a.dx, a.ddt, a.dz, a.dBm, a.dCm, a.dA,
+                a.dDskip, a.ddt_bias, a.dh0, static_cast<float *>(a.workspace)};
+    const size_t nbc = size_t(a.batch) * N * a.seqlen;
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, stream, a.dBm, nbc, a.dCm, nbc,
+                       a.dA, size_t(a.dim) * N, a.dDskip, size_t(a.dim), a.ddt_bias, size_t(a.dim));
+    const dim3 grid((a.dim + kChanB - 1) / kChanB, a.batch);
+    hipLaunchKernelGGL((chunk_states_kernel<Tin, N>), grid, dim3(kThreadsB), 0, stream, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, N>), grid, dim3(kThreadsB), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tg>
+hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream)
+{
+    switch (a.dstate) {
+    case 1: return launch_bwd_typed<Tin, Tg, 1>(a, stream);
+    case 2: return launch_bwd_typed<Tin, Tg, 2>(a, stream);
+    case 4: return launch_bwd_typed<Tin, Tg, 4>(a, stream);
+    case 8: return launch_bwd_typed<Tin, Tg, 8>(a, stream);
+    case 16: return launch_bwd_typed<Tin, Tg, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    const size_t nchunks = (size_t(seqlen) + kTB - 1) / kTB;
+    return size_t(batch) * size_t(dim) * nchunks * size_t(dstate) * sizeof(float);
+}
+
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream)
+{
+    if (a.in_bf16) {
+        return a.grad_bf16 ? launch_bwd_n<bf16_t, bf16_t>(a, stream)
+                           : launch_bwd_n<bf16_t, float>(a, stream);
+    }
+    return a.grad_bf16 ? launch_bwd_n<float, bf16_t>(a, stream) : launch_bwd_n<float, float>(a, stream);
+}
+
+}  // namespace ssm

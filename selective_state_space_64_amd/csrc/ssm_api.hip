@@ -2,6 +2,7 @@
 // and dispatch to the gfx950 kernels.  Every argument error is detected here,
 // before anything is enqueued, so a failing call has no side effects.
 #include "ssm.h"
+#include "ssm_bwd.h"
 #include "ssm_conv.h"
 
 #include <stdint.h>
@@ -253,6 +254,79 @@ ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dty
     ssm::ConvUpdateArgs a{batch, dim, width, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
                           (flags & SSM_CONV_SILU) != 0, state, x, weight, bias, y};
     const hipError_t e = ssm::launch_conv1d_update(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    if (batch < 1 || dim < 1 || seqlen < 1 || dstate < 1) return 0;
+    return ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate);
+}
+
+ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+                          unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                          const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                          const void *z, const float *h0, ssm_dtype_t grad_dtype,
+                          const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                          float *dBm, float *dCm, float *dA, float *dDskip, float *ddt_bias,
+                          float *dh0, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!x || !dt || !A || !Bm || !Cm || !dy || !dx || !ddt || !dBm || !dCm || !dA)
+        return SSM_ERR_NULL_ARG;
+    if (z && !dz) return SSM_ERR_NULL_ARG;
+    if (!z) dz = nullptr;
+    if (!valid_dtype(in_dtype) || !valid_dtype(grad_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
+        return SSM_ERR_BAD_SHAPE;
+    if (!valid_dstate(dstate) || flags != 0) return SSM_ERR_UNSUPPORTED;
+
+    const size_t seq_elems = mul3(batch, dim, seqlen);
+    const size_t bc_elems = mul3(batch, dstate, seqlen);
+    const size_t st_elems = mul3(batch, dim, dstate);
+    if (!seq_elems || !bc_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+    const size_t ws_need = ssm_scan_bwd_workspace_bytes(batch, dim, seqlen, dstate);
+    if (!workspace && ws_need) return SSM_ERR_NULL_ARG;
+
+    const size_t in = dsize(in_dtype), gs = dsize(grad_dtype);
+    for (const void *p : {x, dt, Bm, Cm, z})
+        if (misaligned(p, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {dy, (const void *)dx, (const void *)ddt, (const void *)dz})
+        if (misaligned(p, gs)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)dt_bias, (const void *)A, (const void *)Dskip,
+                          (const void *)h0, (const void *)dhL, (const void *)dBm, (const void *)dCm,
+                          (const void *)dA, (const void *)dDskip, (const void *)ddt_bias,
+                          (const void *)dh0, (const void *)workspace})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+
+    struct Buf {
+        const void *p;
+        size_t bytes;
+    };
+    const size_t fb = sizeof(float);
+    const Buf inputs[] = {{x, seq_elems * in},  {dt, seq_elems * in},  {dt_bias, dim * fb},
+                          {A, size_t(dim) * dstate * fb},
+                          {Bm, bc_elems * in},  {Cm, bc_elems * in},  {Dskip, dim * fb},
+                          {z, seq_elems * in},  {h0, st_elems * fb},  {dy, seq_elems * gs},
+                          {dhL, st_elems * fb}};
+    const Buf outputs[] = {{dx, seq_elems * gs},     {ddt, seq_elems * gs},   {dz, seq_elems * gs},
+                           {dBm, bc_elems * fb},     {dCm, bc_elems * fb},
+                           {dA, size_t(dim) * dstate * fb},
+                           {dDskip, dim * fb},       {ddt_bias, dim * fb},    {dh0, st_elems * fb},
+                           {workspace, ws_need}};
+    const int nout = int(sizeof(outputs) / sizeof(outputs[0]));
+    for (int o = 0; o < nout; ++o) {
+        for (const Buf &i : inputs)
+            if (overlaps(outputs[o].p, outputs[o].bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < nout; ++o2)
+            if (overlaps(outputs[o].p, outputs[o].bytes, outputs[o2].p, outputs[o2].bytes))
+                return SSM_ERR_ALIAS;
+    }
+    if (workspace_bytes < ws_need) return SSM_ERR_WORKSPACE;
+
+    ssm::BwdArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, grad_dtype == SSM_BF16,
+                   x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy, dhL, dx, ddt, dz, dBm, dCm, dA,
+                   dDskip, ddt_bias, dh0, workspace};
+    const hipError_t e = ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

@@ -49,11 +49,31 @@ struct ConvUpdateArgs {
     void *y;
 };
 
+struct BwdArgs {
+    int batch, dim, seqlen, dstate;
+    int in_bf16, grad_bf16;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *h0;
+    const void *dy;
+    const float *dhL;
+    void *dx, *ddt, *dz;
+    float *dBm, *dCm, *dA, *dDskip, *ddt_bias, *dh0;
+    void *workspace;
+};
+
+// Device workspace of the backward pass: the state entering every chunk.
+size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
+
 // All return hipSuccess or the launch error; arguments are already validated.
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream);
 hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t stream);
+hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream);
 
 // Largest batch the kernels' grids support (grid y dimension).
 constexpr int kMaxBatch = 65535;

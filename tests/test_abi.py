@@ -31,6 +31,40 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def _declared_signatures():
+    """{name: [parameter types]} from the prototypes in include/*.h."""
+    sigs = {}
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if not h.endswith(".h"):
+            continue
+        with open(os.path.join(inc, h)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for m in re.finditer(r"\b(ssm_[a-z_0-9]+)\s*\(([^)]*)\)\s*;", text):
+            params = [p.strip() for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+            sigs[m.group(1)] = params
+    return sigs
+
+
+def test_binding_argtypes_match_prototypes():
+    """Every ctypes prototype has the header's parameter count, and each
+    pointer parameter is passed as a pointer (a mismatch would hand an
+    unconverted Python int to the C side)."""
+    L = ssm.lib()
+    sigs = _declared_signatures()
+    assert set(sigs) == set(ssm.EXPORTS)
+    for name, params in sigs.items():
+        argtypes = getattr(L, name).argtypes
+        assert len(argtypes) == len(params), (name, len(argtypes), len(params))
+        for decl, at in zip(params, argtypes):
+            if "*" in decl:
+                assert at in (ctypes.c_void_p, ctypes.c_char_p), (name, decl, at)
+            elif decl.startswith("size_t"):
+                assert at == ctypes.c_size_t, (name, decl, at)
+            else:
+                assert at in (ctypes.c_int, ctypes.c_uint), (name, decl, at)
+
+
 def test_host_only_entry_points():
     L = ssm.lib()
     assert L.ssm_abi_version() == 1
