@@ -13,21 +13,26 @@
 //     dCm[b,n,t] += ds_t h_t                            dz_t = dy_t s_t silu'(z_t)
 // where s_t = C_t . h_t + Dskip x_t is the forward readout before the gate.
 //
-// Three launches:
-//   1. zero the gradients that are sums over rows (dBm, dCm, dA, dDskip, ddt_bias);
-//   2. chunk_states_kernel: the forward recurrence once more, keeping only the
-//      state entering every 128-step chunk (the workspace, batch*dim*chunks*N
-//      floats);
-//   3. scan_bwd_kernel: chunks in reverse order.  Per chunk and state n the
-//      workgroup recomputes the chunk's states from its checkpoint with the
-//      forward in-row scan, folds the adjoint of each lane's 8 steps into an
-//      affine map, composes the maps of a row with the mirrored (reverse
+// Four launches:
+//   1. zero the accumulated gradients (dA, dDskip, ddt_bias) and the partial
+//      dBm / dCm sums;
+//   2. chunk_states_kernel: the forward recurrence once more (8 steps per
+//      lane, 128-step row chunks), keeping only the state entering every
+//      64-step chunk (batch*dim*ceil(L/64)*N floats of workspace);
+//   3. scan_bwd_kernel: 64-step chunks in reverse order.  Per chunk and state
+//      n the workgroup recomputes the chunk's states from its checkpoint with
+//      the forward in-row scan, folds the adjoint of each lane's 4 steps into
+//      an affine map, composes the maps of a row with the mirrored (reverse
 //      time) DPP scan, replays the lane's steps backwards and accumulates the
-//      gradients.  Sums over channels (dBm, dCm) go through LDS atomics per
-//      chunk, then one global atomic add per (n, t) per workgroup.
-// The layout and lane mapping are those of the forward kernel: a workgroup
-// owns one batch row and 16 channels, each 16-lane DPP row one channel, lane
-// j the steps [l0 + 8j, l0 + 8j + 8) of a chunk.
+//      gradients.  dBm and dCm sum over channels: each lane leaves its terms
+//      in LDS, the workgroup adds its 16 channels, and one atomic add per
+//      (state, step) goes to one of 8 partial copies chosen by workgroup
+//      index, so that the workgroups sharing a copy sit on one XCD (the
+//      dispatcher deals workgroups to the 8 XCDs in turn) and their atomics
+//      resolve in that XCD's L2;
+//   4. bwd_sum_kernel: dBm, dCm = the sum of the 8 copies.
+// The layout and lane mapping follow the forward kernel: a workgroup owns one
+// batch row and 16 channels, each 16-lane DPP row one channel.
 #include "scan_common.hpp"
 #include "ssm_device.hpp"
 #include "ssm_launch.hpp"
@@ -42,8 +47,10 @@ constexpr int kChanB = kThreadsB / kRowB;  // channels per workgroup
 constexpr int kKB = 4;                     // consecutive steps per lane
 constexpr int kTB = kRowB * kKB;           // steps per chunk
 
+constexpr int kCopies = 8;                 // partial dBm / dCm copies (one per XCD)
+
 struct BwdParams {
-    int dim, seqlen, nchunks;
+    int batch, dim, seqlen, nchunks;
     const void *x, *dt;
     const float *dt_bias, *A;
     const void *Bm, *Cm;
@@ -54,7 +61,8 @@ struct BwdParams {
     const float *dhL;
     void *dx, *ddt, *dz;
     float *dBm, *dCm, *dA, *dDskip, *ddt_bias, *dh0;
-    float *ck;  // [batch][dim][nchunks][N] state entering each chunk
+    float *ck;    // [batch][dim][nchunks][N] state entering each 64-step chunk
+    float *part;  // [kCopies][2][batch][N][seqlen] partial dBm, dCm sums
 };
 
 // A lane's run of K = 4 steps is 8 bytes of bf16 or 16 bytes of fp32: one
@@ -122,6 +130,35 @@ __device__ inline float row_sum(float v)
     return v;
 }
 
+// Sum over the 16 lanes of each DPP row, left in the row's last lane (an
+// inclusive row scan; lanes without a partner keep their value).  Each
+// v_add_f32_dpp reads the register the previous one wrote, hence the two
+// wait states in between.  All 64 lanes must be active.
+__device__ inline float row_total_last(float v)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf"
+        : "+v"(v));
+    return v;
+}
+
+// v + the value of the neighbouring lane (lanes 2i and 2i + 1 exchange).
+__device__ inline float add_lane_pair(float v)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(v));
+    return v;
+}
+
 // Bm or Cm of one chunk into LDS as fp32, layout [n][q][lane] of float4 (the
 // forward kernel's layout): thread (sn, sj) stages the K steps of lane sj.
 template <typename Tin, int K>
@@ -149,24 +186,44 @@ __device__ inline void lds_run(const float4 *src, float *v)
 }
 
 __global__ void bwd_zero_kernel(float *a, size_t na, float *b, size_t nb, float *c, size_t nc,
-                                float *d, size_t nd, float *e, size_t ne)
+                                float *d, size_t nd)
 {
     const size_t stride = size_t(gridDim.x) * blockDim.x;
-    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < na; i += stride) a[i] = 0.0f;
-    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nb; i += stride) b[i] = 0.0f;
-    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nc; i += stride) c[i] = 0.0f;
+    const size_t i0 = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (size_t i = i0; i < na; i += stride) a[i] = 0.0f;
+    for (size_t i = i0; i < nb; i += stride) b[i] = 0.0f;
+    if (c)
+        for (size_t i = i0; i < nc; i += stride) c[i] = 0.0f;
     if (d)
-        for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < nd; i += stride) d[i] = 0.0f;
-    if (e)
-        for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < ne; i += stride) e[i] = 0.0f;
+        for (size_t i = i0; i < nd; i += stride) d[i] = 0.0f;
 }
 
-// The state entering every chunk, from the forward recurrence (per state:
-// lane fold, row scan, carry).
+// dBm, dCm = sum over the partial copies ([kCopies][2][n] floats).
+__global__ void bwd_sum_kernel(const float *part, size_t n, float *dB, float *dC)
+{
+    const size_t stride = size_t(gridDim.x) * blockDim.x;
+    for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kCopies; ++k) {
+            sb += part[(2 * size_t(k)) * n + i];
+            sc += part[(2 * size_t(k) + 1) * n + i];
+        }
+        dB[i] = sb;
+        dC[i] = sc;
+    }
+}
+
+// The state entering every 64-step chunk, from the forward recurrence.  Rows
+// of 16 lanes with 8 steps per lane cover 128 steps, i.e. two backward
+// chunks: the state entering the first is the carry, the state entering the
+// second is lane 7's inclusive result.  Per state: lane fold, row scan,
+// carry.
 template <typename Tin, int N>
 __global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
 {
-    constexpr int K = kKB, T = kTB, Q = K / 4, NP = N + 1;
+    constexpr int K = 8, T = kRowB * K, Q = K / 4, NP = N + 1;
+    static_assert(T == 2 * kTB, "one row chunk spans two backward chunks");
     __shared__ float4 sB[N * Q * kRowB];
     __shared__ float sAP[kChanB * NP];
     __shared__ float sCar[kChanB * NP];
@@ -192,15 +249,26 @@ __global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
     const int sn = stager ? tid / kRowB : 0, sj = tid % kRowB;
     const float *ap = sAP + c * NP;
     float *car = sCar + c * NP;
+    float *ckr = p.ck + (size_t(b) * dim + d) * size_t(p.nchunks) * N;  // used when live
+    const int nrow = (L + T - 1) / T;
 
-    for (int ch = 0; ch < p.nchunks; ++ch) {
+    for (int ch = 0; ch < nrow; ++ch) {
         lds_barrier();
-        if (stager) stage_chunk<Tin, K>(sB, Bb, L, ch, sn, sj);
+        if (stager) {
+            const int l = ch * T + sj * K;
+            const int cnt = max(0, min(K, L - l));
+            const Tin *q = Bb + size_t(sn) * size_t(L) + l;
+            float v[K];
+            load_run<Tin, K>(q, cnt == K && (reinterpret_cast<uintptr_t>(q) & 15u) == 0, cnt, v);
+#pragma unroll
+            for (int i = 0; i < Q; ++i)
+                sB[(sn * Q + i) * kRowB + sj] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        }
         const int l0 = ch * T + j * K;
         const int cnt = max(0, min(K, L - l0));
         float xv[K], dv[K], delta[K], w[K];
-        load4<Tin>(xr + l0, cnt, xv);
-        load4<Tin>(dtr + l0, cnt, dv);
+        load_run<Tin, K>(xr + l0, cnt == K && (reinterpret_cast<uintptr_t>(xr + l0) & 15u) == 0, cnt, xv);
+        load_run<Tin, K>(dtr + l0, cnt == K && (reinterpret_cast<uintptr_t>(dtr + l0) & 15u) == 0, cnt, dv);
         float sumd = 0.0f;
 #pragma unroll
         for (int i = 0; i < K; ++i) {
@@ -211,11 +279,16 @@ __global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
         }
         lds_barrier();
         const float4 *bp = sB + j;
+        const bool second = 2 * ch + 1 < p.nchunks;
 #pragma unroll 1
         for (int n = 0; n < N; ++n) {
             const float a1 = ap[n];
             float bv[K];
-            lds_run<K>(bp + n * Q * kRowB, bv);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const float4 v4 = bp[(n * Q + q) * kRowB];
+                bv[4 * q] = v4.x; bv[4 * q + 1] = v4.y; bv[4 * q + 2] = v4.z; bv[4 * q + 3] = v4.w;
+            }
             float hl = w[0] * bv[0];
 #pragma unroll
             for (int i = 1; i < K; ++i) hl = __builtin_fmaf(exp2_hw(delta[i] * a1), hl, w[i] * bv[i]);
@@ -224,7 +297,8 @@ __global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
             float hend, h = cin;
             row_scan(aa, hl, hend, h);
             if (j == kRowB - 1) car[n] = hend;
-            if (j == 0 && live) p.ck[((size_t(b) * dim + d) * p.nchunks + ch) * N + n] = cin;
+            if (live && j == 0) ckr[size_t(2 * ch) * N + n] = cin;
+            if (live && j == kRowB / 2 - 1 && second) ckr[size_t(2 * ch + 1) * N + n] = hend;
         }
     }
 }
@@ -275,6 +349,10 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
     float *mus = sMu + c * NP;
     float *das = sDA + c * NP;
     float dskip_acc = 0.0f, dbias_acc = 0.0f;
+    // this workgroup's partial copy of dBm / dCm, at batch row b
+    const size_t bnl = size_t(p.batch) * N * L;
+    const unsigned wg = blockIdx.x + blockIdx.y * gridDim.x;
+    float *part = p.part + size_t(wg % kCopies) * 2 * bnl + size_t(b) * N * L;
 
     for (int ch = p.nchunks - 1; ch >= 0; --ch) {
         lds_barrier();
@@ -293,7 +371,8 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
         // maps that add nothing to any sum.
         const int l0 = ch * T + j * K;
         const int cnt = live ? max(0, min(K, L - l0)) : 0;
-        float xv[K], delta[K], ds[K], sacc[K], gx[K], gdel[K], sgu[K], gzf[K];
+        // per step: sb = sum_n lambda B, sah = sum_n lambda A A-bar h_{t-1}
+        float xv[K], delta[K], w[K], ds[K], sacc[K], sb[K], sah[K], sgu[K], gzf[K];
         float sumd = 0.0f;
         {
             float dv[K], gy[K], zv[K];
@@ -307,6 +386,7 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
                 const float uv = dv[i] + bias;
                 const float dl = softplus(uv);
                 delta[i] = in ? dl : 0.0f;
+                w[i] = delta[i] * xv[i];
                 sgu[i] = sigmoid_hw(uv);  // softplus'(u)
                 float g = 1.0f;
                 gzf[i] = 0.0f;
@@ -317,8 +397,8 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
                 }
                 ds[i] = in ? gy[i] * g : 0.0f;
                 sacc[i] = skip * xv[i];
-                gx[i] = skip * ds[i];
-                gdel[i] = 0.0f;
+                sb[i] = 0.0f;
+                sah[i] = 0.0f;
                 sumd += delta[i];
                 dskip_acc = __builtin_fmaf(ds[i], xv[i], dskip_acc);
             }
@@ -338,16 +418,16 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
             // term Delta x B is recomputed where needed to save registers)
 #pragma unroll
             for (int i = 0; i < K; ++i) da[i] = exp2_hw(delta[i] * a1);
-            float hl = (delta[0] * xv[0]) * bv[0];
+            float hl = w[0] * bv[0];
 #pragma unroll
-            for (int i = 1; i < K; ++i) hl = __builtin_fmaf(da[i], hl, (delta[i] * xv[i]) * bv[i]);
+            for (int i = 1; i < K; ++i) hl = __builtin_fmaf(da[i], hl, w[i] * bv[i]);
             const float ptot = exp2_hw(sumd * a1);
             float aa = ptot;
             float hend, h = hs[n];
             row_scan(aa, hl, hend, h);
 #pragma unroll
             for (int i = 0; i < K; ++i) {
-                h = __builtin_fmaf(da[i], h, (delta[i] * xv[i]) * bv[i]);
+                h = __builtin_fmaf(da[i], h, w[i] * bv[i]);
                 hh[i] = h;
                 sacc[i] = __builtin_fmaf(cv[i], h, sacc[i]);
             }
@@ -368,22 +448,23 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
 #pragma unroll
             for (int i = K - 1; i >= 0; --i) {
                 lam = __builtin_fmaf(ds[i], cv[i], lam);
-                const float wx = delta[i] * xv[i];
-                const float hpa = hh[i] - wx * bv[i];  // A-bar h_{t-1}
-                gdel[i] = __builtin_fmaf(lam, __builtin_fmaf(bv[i], xv[i], An * hpa), gdel[i]);
-                const float ld = lam * delta[i];
-                dap = __builtin_fmaf(ld, hpa, dap);
-                gx[i] = __builtin_fmaf(ld, bv[i], gx[i]);
-                gbv[i] = lam * wx;
+                const float hpa = __builtin_fmaf(-w[i], bv[i], hh[i]);  // A-bar h_{t-1}
+                const float lh = lam * hpa;
+                sah[i] = __builtin_fmaf(An, lh, sah[i]);
+                dap = __builtin_fmaf(delta[i], lh, dap);
+                sb[i] = __builtin_fmaf(lam, bv[i], sb[i]);
+                gbv[i] = lam * w[i];
                 gcv[i] = ds[i] * hh[i];
                 lam *= da[i];
             }
-            dap = row_sum(dap);
-            if (j == 0) das[n] += dap;
+            dap = row_total_last(dap);
+            if (j == kRowB - 1) das[n] += dap;
 
             // dBm[b, n, t] and dCm[b, n, t] sum over channels: each lane
-            // leaves its terms in LDS, then one thread per (quantity, step)
-            // adds the 16 channels and issues one global atomic add.
+            // leaves its terms in LDS; neighbouring lanes 2i, 2i + 1 add 8
+            // channels each for one (quantity, step), combine through DPP,
+            // and the even lane issues the atomic add into this workgroup's
+            // copy.
             const int pb = n & 1;
 #pragma unroll
             for (int q4 = 0; q4 < K / 4; ++q4) {
@@ -393,23 +474,27 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
                     make_float4(gcv[4 * q4], gcv[4 * q4 + 1], gcv[4 * q4 + 2], gcv[4 * q4 + 3]);
             }
             lds_barrier();
-            if (tid < 2 * T) {
-                const int qq = tid / T, t = tid % T;
-                const float *col = reinterpret_cast<const float *>(&sP[pb][qq][0][0]) + t;
+            {
+                const int pair = tid >> 1;  // 0..127 = (quantity, step)
+                const int half = tid & 1;
+                const int qq = pair / T, t = pair % T;
+                const float *col = reinterpret_cast<const float *>(&sP[pb][qq][half * (kChanB / 2)][0]) + t;
                 float acc = 0.0f;
 #pragma unroll
-                for (int cc = 0; cc < kChanB; ++cc) acc += col[cc * T];
+                for (int cc = 0; cc < kChanB / 2; ++cc) acc += col[cc * T];
+                acc = add_lane_pair(acc);
                 const int tt = ch * T + t;
-                if (tt < L) atomicAdd(&(qq ? p.dCm : p.dBm)[(size_t(b) * N + n) * L + tt], acc);
+                if (half == 0 && tt < L) atomicAdd(&part[size_t(qq) * bnl + size_t(n) * L + tt], acc);
             }
         }
 
         // per-step gradients of this chunk
         {
-            float gdt[K], gz[K];
+            float gx[K], gdt[K], gz[K];
 #pragma unroll
             for (int i = 0; i < K; ++i) {
-                gdt[i] = gdel[i] * sgu[i];
+                gx[i] = __builtin_fmaf(delta[i], sb[i], skip * ds[i]);
+                gdt[i] = __builtin_fmaf(xv[i], sb[i], sah[i]) * sgu[i];
                 dbias_acc += i < cnt ? gdt[i] : 0.0f;
                 gz[i] = gzf[i] * sacc[i];
             }
@@ -439,15 +524,20 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
 template <typename Tin, typename Tg, int N>
 hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
 {
-    BwdParams p{a.dim, a.seqlen, (a.seqlen + kTB - 1) / kTB, a.x, a.dt, a.dt_bias, a.A, a.Bm,
-                a.Cm, a.Dskip, a.z, a.h0, a.dy, a.dhL, a.dx, a.ddt, a.dz, a.dBm, a.dCm, a.dA,
-                a.dDskip, a.ddt_bias, a.dh0, static_cast<float *>(a.workspace)};
+    const int nchunks = (a.seqlen + kTB - 1) / kTB;
+    float *ck = static_cast<float *>(a.workspace);
+    float *part = ck + size_t(a.batch) * a.dim * nchunks * N;
+    BwdParams p{a.batch, a.dim, a.seqlen, nchunks, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
+                a.Dskip, a.z, a.h0, a.dy, a.dhL, a.dx, a.ddt, a.dz, a.dBm, a.dCm, a.dA,
+                a.dDskip, a.ddt_bias, a.dh0, ck, part};
     const size_t nbc = size_t(a.batch) * N * a.seqlen;
-    hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, stream, a.dBm, nbc, a.dCm, nbc,
-                       a.dA, size_t(a.dim) * N, a.dDskip, size_t(a.dim), a.ddt_bias, size_t(a.dim));
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, stream, part,
+                       size_t(kCopies) * 2 * nbc, a.dA, size_t(a.dim) * N, a.dDskip, size_t(a.dim),
+                       a.ddt_bias, size_t(a.dim));
     const dim3 grid((a.dim + kChanB - 1) / kChanB, a.batch);
     hipLaunchKernelGGL((chunk_states_kernel<Tin, N>), grid, dim3(kThreadsB), 0, stream, p);
     hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, N>), grid, dim3(kThreadsB), 0, stream, p);
+    hipLaunchKernelGGL(bwd_sum_kernel, dim3(1024), dim3(256), 0, stream, part, nbc, a.dBm, a.dCm);
     return hipGetLastError();
 }
 
@@ -469,7 +559,9 @@ hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream)
 size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 {
     const size_t nchunks = (size_t(seqlen) + kTB - 1) / kTB;
-    return size_t(batch) * size_t(dim) * nchunks * size_t(dstate) * sizeof(float);
+    const size_t checkpoints = size_t(batch) * size_t(dim) * nchunks * size_t(dstate);
+    const size_t partials = size_t(kCopies) * 2 * size_t(batch) * size_t(dstate) * size_t(seqlen);
+    return (checkpoints + partials) * sizeof(float);
 }
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream)

@@ -298,6 +298,8 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           (const void *)dh0, (const void *)workspace})
         if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
 
+    if (workspace_bytes < ws_need) return SSM_ERR_WORKSPACE;
+
     struct Buf {
         const void *p;
         size_t bytes;
@@ -321,8 +323,6 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
             if (overlaps(outputs[o].p, outputs[o].bytes, outputs[o2].p, outputs[o2].bytes))
                 return SSM_ERR_ALIAS;
     }
-    if (workspace_bytes < ws_need) return SSM_ERR_WORKSPACE;
-
     ssm::BwdArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, grad_dtype == SSM_BF16,
                    x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy, dhL, dx, ddt, dz, dBm, dCm, dA,
                    dDskip, ddt_bias, dh0, workspace};
