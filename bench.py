@@ -71,6 +71,9 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
+SCAN_KERNEL = "scan_fwd_kernel<ssm::bf16_t, float, 16, 8, false>"
+
+
 def ingest_counters(fetch_dir, write_dir, copyf_dir, copyw_dir, copy_mib=256, workload=None):
     """Per-dispatch mean of FETCH_SIZE / WRITE_SIZE (KiB) for the scan kernel,
     scaled by what the same counters read for a plain device copy of copy_mib
@@ -91,13 +94,13 @@ def ingest_counters(fetch_dir, write_dir, copyf_dir, copyw_dir, copy_mib=256, wo
         return sum(vals) / len(vals)
 
     copy_kib = copy_mib * 1024.0
-    fetch = mean(fetch_dir, "FETCH_SIZE", "scan_fwd_kernel")
-    write = mean(write_dir, "WRITE_SIZE", "scan_fwd_kernel")
+    fetch = mean(fetch_dir, "FETCH_SIZE", SCAN_KERNEL)
+    write = mean(write_dir, "WRITE_SIZE", SCAN_KERNEL)
     cf = mean(copyf_dir, "FETCH_SIZE", "copyBuffer")
     cw = mean(copyw_dir, "WRITE_SIZE", "copyBuffer")
     fs, ws = copy_kib / cf, copy_kib / cw
     rec = {
-        "kernel": "scan_fwd_kernel (bf16 in, fp32 out, N 16)",
+        "kernel": SCAN_KERNEL,
         "workload": workload,
         "kernel_sources_sha256": kernel_sources_sha256(),
         "fetch_size_kib_per_dispatch": fetch,
@@ -243,10 +246,13 @@ def bench_conv(torch, ssm, synth, wl, x, launches=20):
     torch.cuda.synchronize()
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     nbytes = 2 * x.numel() * x.element_size() + wl.dim * 5 * 4
+    achieved = nbytes / (ms * 1e-3)
     out = {"workload": "conv1d W4 silu, %s" % wl.name, "kernel_ms_mean": ms,
-           "outputs_per_s": x.numel() / (ms * 1e-3), "algorithmic_bytes": nbytes,
-           "hbm_gbps_algorithmic": nbytes / (ms * 1e-3) / 1e9,
-           "hbm_frac": nbytes / (ms * 1e-3) / PEAK_HBM}
+           "outputs_per_s": x.numel() / (ms * 1e-3),
+           "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
+                        "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
+                        "algorithmic_bytes": nbytes,
+                        "model": "x read once (2 B) + y written once (2 B) per output, plus taps"}}
     dwl = synth.WORKLOADS[4]
     state = torch.zeros((dwl.batch, dwl.dim, 3), device="cuda")
     xs = torch.randn((64, dwl.batch, dwl.dim), device="cuda").to(torch.bfloat16)
@@ -267,20 +273,39 @@ def bench_conv(torch, ssm, synth, wl, x, launches=20):
     return out
 
 
+BWD_SLOTS_PER_ELEM = 17      # recompute 8 + adjoint 2 + dBm, dCm 2 + dA 3 + dx/dDelta sums 2
+BWD_SLOTS_PER_ROW_STEP = 40  # softplus 9, sigmoid(u) 9, silu + silu' 14, gradient assembly 8
+
+
 def bench_bwd(torch, ssm, wl, t, launches=10):
-    """Backward pass (all three launches of one ssm_scan_bwd call) on the
-    layer, dy ~ N(0, 1) fp32, gradients fp32."""
+    """Backward pass (all launches of one ssm_scan_bwd call: zero-fill,
+    chunk states, reverse pass, sum of partial copies) on the layer,
+    dy ~ N(0, 1) fp32, gradients fp32, outputs and workspace preallocated."""
     dy = torch.randn((wl.batch, wl.dim, wl.seqlen), device="cuda")
     ws = torch.empty(ssm.lib().ssm_scan_bwd_workspace_bytes(wl.batch, wl.dim, wl.seqlen, wl.dstate),
                      dtype=torch.uint8, device="cuda")
+    L = ssm.lib()
+    f32 = torch.float32
+    g = {k: torch.empty(shape, dtype=f32, device="cuda") for k, shape in (
+        ("dx", (wl.batch, wl.dim, wl.seqlen)), ("ddt", (wl.batch, wl.dim, wl.seqlen)),
+        ("dz", (wl.batch, wl.dim, wl.seqlen)), ("dBm", (wl.batch, wl.dstate, wl.seqlen)),
+        ("dCm", (wl.batch, wl.dstate, wl.seqlen)), ("dA", (wl.dim, wl.dstate)),
+        ("dDskip", (wl.dim,)), ("ddt_bias", (wl.dim,)))}
+    stream = torch.cuda.current_stream()
+    ptr = lambda k: t[k].data_ptr()
 
     def call():
-        return ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy, dt_bias=t["dt_bias"],
-                                Dskip=t["Dskip"], z=t["z"], workspace=ws)
+        st = L.ssm_scan_bwd(wl.batch, wl.dim, wl.seqlen, wl.dstate, 1 if wl.dtype == "bf16" else 0, 0, ptr("x"), ptr("dt"),
+                            ptr("dt_bias"), ptr("A"), ptr("Bm"), ptr("Cm"), ptr("Dskip"), ptr("z"),
+                            None, 0, dy.data_ptr(), None, g["dx"].data_ptr(), g["ddt"].data_ptr(),
+                            g["dz"].data_ptr(), g["dBm"].data_ptr(), g["dCm"].data_ptr(),
+                            g["dA"].data_ptr(), g["dDskip"].data_ptr(), g["ddt_bias"].data_ptr(),
+                            None, ws.data_ptr(), ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError("ssm_scan_bwd failed with status %d" % st)
 
     for _ in range(2):
         call()
-    stream = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(launches)]
     for e0, e1 in evs:
@@ -290,9 +315,15 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
     torch.cuda.synchronize()
     ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
+    slots = elems * BWD_SLOTS_PER_ELEM + wl.batch * wl.dim * wl.seqlen * BWD_SLOTS_PER_ROW_STEP
+    achieved = slots / (ms * 1e-3) / 1e12
     return {"workload": "scan backward, %s" % wl.name, "ms_mean": ms,
             "elements_per_s": elems / (ms * 1e-3),
-            "note": "zero-fill + chunk-state recompute + reverse pass; includes output allocation"}
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_SLOTS / 1e12,
+                         "unit": "TOP/s", "frac": achieved / (PEAK_SLOTS / 1e12), "traffic": None,
+                         "model": "fp32 VALU issue slots (transcendental = 4), %.2f slots/element"
+                                  % (slots / elems)},
+            "note": "zero-fill + chunk-state recompute + reverse pass + partial-copy sum"}
 
 
 def main():
