@@ -217,6 +217,32 @@ def bench_decode(torch, ssm, synth, steps_cap=256):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+
+    # the same loop captured once in a HIP graph and replayed (no launch
+    # overhead per token); checked against the eager loop before timing
+    ref_state, ref_y = state.clone(), ys[:steps].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        state.copy_(state0)
+        loop()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    state.copy_(state0)
+    with torch.cuda.graph(graph):
+        loop()
+    state.copy_(state0)
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(state, ref_state) and torch.equal(ys[:steps], ref_y))
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1) / steps
     per_call_bytes = (2 * wl.batch * wl.dim * wl.dstate * 4 + 3 * wl.batch * wl.dim * 2
                       + 2 * wl.batch * wl.dstate * 2 + wl.dim * wl.dstate * 4 + 2 * wl.dim * 4
                       + wl.batch * wl.dim * 4)
@@ -225,6 +251,8 @@ def bench_decode(torch, ssm, synth, steps_cap=256):
             "elements_per_s": elems / (ms * 1e-3),
             "hbm_gbps_algorithmic": per_call_bytes / (ms * 1e-3) / 1e9,
             "bytes_per_call": per_call_bytes,
+            "graph_us_per_call": graph_ms * 1e3, "graph_matches_eager": graph_ok,
+            "graph_hbm_gbps_algorithmic": per_call_bytes / (graph_ms * 1e-3) / 1e9,
             "note": "one launch per token, state fp32 in place; 21 MB state can stay in the 256 MB MALL"}
 
 

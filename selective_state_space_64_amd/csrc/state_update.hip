@@ -11,10 +11,11 @@
 // phi(Delta A) = (e^{Delta A} - 1) / (Delta A).)
 //
 // The step is bound by moving the state (read + write, 2 x 4N bytes per
-// (b, d)).  One lane owns one (b, d): its N states are one contiguous run of
-// 4N bytes, so a wave reads and writes 64 consecutive runs with 16-byte
-// vector accesses (the state is 16-byte aligned).  A, Bm and Cm are shared
-// across lanes and come from cache.
+// (b, d)).  R = N / 4 consecutive lanes share one (b, d) and each owns four
+// of its states (16 bytes), so a wave reads and writes one contiguous
+// kilobyte of state per access; the readout sum over n is finished across
+// the R lanes with DPP quad permutes.  The per-(b, d) scalars (Delta, x, z)
+// are computed by each of the R lanes.  A, Bm and Cm come from cache.
 #include "ssm_device.hpp"
 #include "ssm_launch.hpp"
 
@@ -50,35 +51,57 @@ __device__ inline void load_f32(const float *p, float *v)
     }
 }
 
+// Sum over groups of R consecutive lanes (R = 1, 2 or 4: within a DPP quad);
+// every lane of a group gets the total.  All lanes of the wave must be active.
+template <int R>
+__device__ inline float group_sum(float v)
+{
+    if constexpr (R >= 2) {
+        asm volatile("s_nop 1\n\t"
+                     "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                     : "+v"(v));
+    }
+    if constexpr (R >= 4) {
+        asm volatile("s_nop 1\n\t"
+                     "v_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                     : "+v"(v));
+    }
+    return v;
+}
+
 template <typename Tin, typename Tout, int N, bool kZoh>
 __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
 {
+    constexpr int S = N < 4 ? N : 4;  // states per lane
+    constexpr int R = N / S;          // lanes per (b, d)
     // Grid: x over channel blocks, y over the batch, so the batch row (and
     // with it Bm, Cm) is uniform across the workgroup.
     const int b = blockIdx.y;
-    const int d = blockIdx.x * kThreads + threadIdx.x;
-    if (d >= p.dim) return;
+    const int g = blockIdx.x * kThreads + threadIdx.x;
+    const int r = g % R;              // which S states of the row
+    const bool live = g / R < p.dim;
+    const int d = live ? g / R : p.dim - 1;  // dead lanes still join the DPP sum
     const size_t idx = size_t(b) * p.dim + d;
+    const int n0 = r * S;
 
-    // Bm and Cm of this sequence: uniform, read once per wave.
-    const Tin *Bp = static_cast<const Tin *>(p.Bm) + size_t(b) * N;
-    const Tin *Cp = static_cast<const Tin *>(p.Cm) + size_t(b) * N;
-    float bm[N], cm[N];
+    const Tin *Bp = static_cast<const Tin *>(p.Bm) + size_t(b) * N + n0;
+    const Tin *Cp = static_cast<const Tin *>(p.Cm) + size_t(b) * N + n0;
+    float bm[S], cm[S];
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
+    for (int n = 0; n < S; ++n) {
         bm[n] = io<Tin>::load1(Bp + n);
         cm[n] = io<Tin>::load1(Cp + n);
     }
 
-    float h[N], a[N];
-    float *st = p.state + idx * N;
-    load_f32<N>(st, h);
-    const float *Ap = p.A + size_t(d) * N;
-    if (N % 4 == 0 && (reinterpret_cast<uintptr_t>(p.A) & 15u) == 0) {
-        load_f32<N>(Ap, a);
+    float h[S], a[S];
+    float *st = p.state + idx * N + n0;
+    load_f32<S>(st, h);
+    const float *Ap = p.A + size_t(d) * N + n0;
+    if (S == 4 && (reinterpret_cast<uintptr_t>(p.A) & 15u) == 0) {
+        load_f32<S>(Ap, a);
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) a[n] = Ap[n];
+        for (int n = 0; n < S; ++n) a[n] = Ap[n];
     }
     const float xv = io<Tin>::load1(static_cast<const Tin *>(p.x) + idx);
     const float dtv = io<Tin>::load1(static_cast<const Tin *>(p.dt) + idx);
@@ -88,10 +111,10 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
     const float delta = softplus(dtv + bias);
     const float u = delta * xv;
     const float dl = delta * kLog2e;
-    float acc = skip * xv;
+    float acc = 0.0f;
     [[maybe_unused]] const float invd = rcp_hw(delta);
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
+    for (int n = 0; n < S; ++n) {
         const float t = dl * a[n];
         const float dA = exp2_hw(t);
         float bterm = u * bm[n];
@@ -99,23 +122,22 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
         h[n] = __builtin_fmaf(dA, h[n], bterm);
         acc = __builtin_fmaf(cm[n], h[n], acc);
     }
+    acc = group_sum<R>(acc) + skip * xv;
     if (p.z) acc *= silu(io<Tin>::load1(static_cast<const Tin *>(p.z) + idx));
+    if (!live) return;
 
-    if constexpr (N % 4 == 0) {
-        f32x4 *q = reinterpret_cast<f32x4 *>(st);
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            f32x4 w = {h[4 * i], h[4 * i + 1], h[4 * i + 2], h[4 * i + 3]};
-            q[i] = w;
-        }
+    if constexpr (S == 4) {
+        *reinterpret_cast<f32x4 *>(st) = f32x4{h[0], h[1], h[2], h[3]};
     } else {
 #pragma unroll
-        for (int i = 0; i < N; ++i) st[i] = h[i];
+        for (int i = 0; i < S; ++i) st[i] = h[i];
     }
-    if constexpr (sizeof(Tout) == 4) {
-        static_cast<float *>(p.y)[idx] = acc;
-    } else {
-        static_cast<uint16_t *>(p.y)[idx] = uint16_t(pack_bf16x2(acc, 0.0f) & 0xffffu);
+    if (r == 0) {
+        if constexpr (sizeof(Tout) == 4) {
+            static_cast<float *>(p.y)[idx] = acc;
+        } else {
+            static_cast<uint16_t *>(p.y)[idx] = uint16_t(pack_bf16x2(acc, 0.0f) & 0xffffu);
+        }
     }
 }
 
@@ -124,7 +146,8 @@ hipError_t launch_typed(const UpdateArgs &a, hipStream_t stream)
 {
     UpdateParams p{a.batch, a.dim, a.state, a.x, a.dt, a.dt_bias, a.A,
                    a.Bm, a.Cm, a.Dskip, a.z, a.y};
-    dim3 grid((a.dim + kThreads - 1) / kThreads, a.batch);
+    constexpr int R = N < 4 ? 1 : N / 4;
+    dim3 grid(unsigned((size_t(a.dim) * R + kThreads - 1) / kThreads), a.batch);
     hipLaunchKernelGGL((state_update_kernel<Tin, Tout, N, kZoh>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

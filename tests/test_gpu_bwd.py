@@ -182,8 +182,10 @@ def test_bwd_argument_errors():
     dAo = torch.full((8, 4), 7.0, device="cuda")
     ws = torch.empty(L.ssm_scan_bwd_workspace_bytes(1, 8, 40, 4), dtype=torch.uint8, device="cuda")
 
+    zt = to_dev(inp, "z")
+
     def call(**o):
-        a = dict(flags=0, z=f(to_dev(inp, "z")), dz=f(outs[2]), dx=f(outs[0]), dBm=f(dB))
+        a = dict(flags=0, z=f(zt), dz=f(outs[2]), dx=f(outs[0]), dBm=f(dB))
         a.update(o)
         return L.ssm_scan_bwd(1, 8, 40, 4, 0, a["flags"], f(x), f(dt), None, f(A), f(Bm), f(Cm),
                               None, a["z"], None, 0, f(dy), None, a["dx"], f(outs[1]), a["dz"],
@@ -195,3 +197,57 @@ def test_bwd_argument_errors():
     assert call(dBm=f(dC)) == 5        # two outputs overlapping
     torch.cuda.synchronize()
     assert all((t == 7.0).all() for t in outs + [dB, dC, dAo])
+
+
+def _offset_copy(t, off=1):
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def test_bwd_unaligned_pointers_and_guard_bands():
+    """Inputs, dy and the per-step gradients one element off a 16-byte
+    boundary (every run takes the element path) at L = 1024 whose rows would
+    otherwise be vector-aligned; NaN guard bands around every output stay
+    untouched."""
+    batch, dim, N, L = 2, 21, 16, 1024
+    inp = synth.make_inputs(workload("bwdu", batch, dim, N, L, "bf16", seed=11), with_h0=True)
+    rng = np.random.default_rng(11)
+    dy = rng.standard_normal((batch, dim, L), dtype=np.float32)
+    G = 64
+    nan_bits = torch.tensor([0x7FC0DEAD], dtype=torch.int32).view(torch.float32).item()
+    shapes = {"dx": (batch, dim, L), "ddt": (batch, dim, L), "dz": (batch, dim, L),
+              "dBm": (batch, N, L), "dCm": (batch, N, L), "dA": (dim, N), "dDskip": (dim,),
+              "ddt_bias": (dim,), "dh0": (batch, dim, N)}
+    bigs, outs = {}, {}
+    for k, shp in shapes.items():
+        n = int(np.prod(shp))
+        off = 1 if k in ("dx", "ddt", "dz") else 0
+        bigs[k] = (torch.full((n + 2 * G + off,), nan_bits, device="cuda"), G + off, n)
+        outs[k] = bigs[k][0][G + off:G + off + n].view(shp)
+    args = [_offset_copy(to_dev(inp, k)) for k in ("x", "dt")] + [to_dev(inp, "A")] + \
+           [_offset_copy(to_dev(inp, k)) for k in ("Bm", "Cm")]
+    z = _offset_copy(to_dev(inp, "z"))
+    dyt = _offset_copy(torch.from_numpy(dy).cuda())
+    h0 = torch.from_numpy(inp.h0).cuda()
+    L_ = ssm.lib()
+    ws = torch.empty(L_.ssm_scan_bwd_workspace_bytes(batch, dim, L, N), dtype=torch.uint8,
+                     device="cuda")
+    p = lambda t: None if t is None else t.data_ptr()
+    bias, skip = to_dev(inp, "dt_bias"), to_dev(inp, "Dskip")  # kept alive across the call
+    st = L_.ssm_scan_bwd(batch, dim, L, N, 1, 0, p(args[0]), p(args[1]), p(bias),
+                         p(args[2]), p(args[3]), p(args[4]), p(skip), p(z), p(h0),
+                         0, p(dyt), None, p(outs["dx"]), p(outs["ddt"]), p(outs["dz"]),
+                         p(outs["dBm"]), p(outs["dCm"]), p(outs["dA"]), p(outs["dDskip"]),
+                         p(outs["ddt_bias"]), p(outs["dh0"]), p(ws), ws.numel(), None)
+    assert st == 0
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(inp.values("x"), inp.values("dt"), inp.A, inp.values("Bm"),
+                        inp.values("Cm"), dy.astype(np.float64), dt_bias=inp.dt_bias,
+                        Dskip=inp.Dskip, z=inp.values("z"), h0=inp.h0)
+    g = {k: v.cpu().numpy() for k, v in outs.items()}
+    _check(_errors(g, r), torch.float32, "unaligned")
+    for k, (big, lo, n) in bigs.items():
+        bits = big.view(torch.int32).cpu().numpy()
+        assert (bits[:lo] == 0x7FC0DEAD).all() and (bits[lo + n:] == 0x7FC0DEAD).all(), k

@@ -148,3 +148,37 @@ def test_conv_feeds_scan():
                              dt_bias=inp.dt_bias, Dskip=inp.Dskip, z=inp.values("z"))
     assert rel_err(y.cpu().numpy(), ry) <= TOL_F32
     assert rel_err(hL.cpu().numpy(), rh) <= TOL_F32
+
+
+def _offset_copy(t, off=1):
+    """A contiguous copy of t whose data starts `off` elements into a larger
+    buffer: element-aligned but not 16-byte aligned."""
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+    v = buf[off:off + t.numel()].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def test_conv_unaligned_pointers_and_guard_bands():
+    """x and y one element off a 16-byte boundary (every run takes the
+    element path) at a shape whose rows would otherwise be vector-aligned;
+    NaN guard bands around y and the final state stay untouched."""
+    inp, w, b, s0 = _conv_inputs(2, 37, 2048, 4, "bf16")
+    x = _offset_copy(to_dev(inp, "x"))
+    G = 64
+    nan_bits = torch.tensor([0x7FC0DEAD], dtype=torch.int32).view(torch.float32).item()
+    n_y, n_s = 2 * 37 * 2048, 2 * 37 * 3
+    ybig = torch.full((n_y + 2 * G + 1,), nan_bits, device="cuda")
+    sbig = torch.full((n_s + 2 * G,), nan_bits, device="cuda")
+    y = ybig[G + 1:G + 1 + n_y].view(2, 37, 2048)
+    sL = sbig[G:G + n_s].view(2, 37, 3)
+    ssm.ssm_conv1d_fwd(x, torch.from_numpy(w).cuda(), bias=torch.from_numpy(b).cuda(),
+                       state0=torch.from_numpy(s0).cuda(), y=y, stateL=sL,
+                       out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ry, rs = oracle.conv1d(inp.values("x"), w, bias=b, state0=s0)
+    assert rel_err(y.cpu().numpy(), ry) <= TOL_F32
+    assert np.array_equal(sL.cpu().numpy(), rs.astype(np.float32))
+    for big, lo, n in ((ybig, G + 1, n_y), (sbig, G, n_s)):
+        bits = big.view(torch.int32).cpu().numpy()
+        assert (bits[:lo] == 0x7FC0DEAD).all() and (bits[lo + n:] == 0x7FC0DEAD).all()
