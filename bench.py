@@ -133,6 +133,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="before the W warm-up steps, run the step for at least this long "
+                         "(untimed): the GPU's clocks ramp up under sustained load, and a "
+                         "cold first second reads 10-20%% slower than steady state")
     ap.add_argument("--workload", type=int, default=2, help="index into synth.WORKLOADS")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -392,6 +396,11 @@ def main():
         ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
                          Dskip=t["Dskip"], z=t["z"], y=y, hL=hL)
 
+    t_end = time.perf_counter() + args.warmup_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
