@@ -326,8 +326,10 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
     stream = torch.cuda.current_stream()
     ptr = lambda k: t[k].data_ptr()
 
-    def call():
-        st = L.ssm_scan_bwd(wl.batch, wl.dim, wl.seqlen, wl.dstate, 1 if wl.dtype == "bf16" else 0, 0, ptr("x"), ptr("dt"),
+    ind = 1 if wl.dtype == "bf16" else 0
+
+    def call(flags=0):
+        st = L.ssm_scan_bwd(wl.batch, wl.dim, wl.seqlen, wl.dstate, ind, flags, ptr("x"), ptr("dt"),
                             ptr("dt_bias"), ptr("A"), ptr("Bm"), ptr("Cm"), ptr("Dskip"), ptr("z"),
                             None, 0, dy.data_ptr(), None, g["dx"].data_ptr(), g["ddt"].data_ptr(),
                             g["dz"].data_ptr(), g["dBm"].data_ptr(), g["dCm"].data_ptr(),
@@ -336,16 +338,34 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
         if st != 0:
             raise RuntimeError("ssm_scan_bwd failed with status %d" % st)
 
-    for _ in range(2):
-        call()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(launches)]
-    for e0, e1 in evs:
-        e0.record(stream)
-        call()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(launches)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    ms = timed(call)
+    # training order: the forward writes the checkpoints (SSM_FLAG_CHECKPOINTS)
+    # into the backward's workspace, the backward reads them
+    y = torch.empty((wl.batch, wl.dim, wl.seqlen), device="cuda")
+
+    def fwd_ckpt():
+        st = L.ssm_scan_fwd(wl.batch, wl.dim, wl.seqlen, wl.dstate, ind, 2, ptr("x"), ptr("dt"),
+                            ptr("dt_bias"), ptr("A"), ptr("Bm"), ptr("Cm"), ptr("Dskip"), ptr("z"),
+                            None, 0, y.data_ptr(), None, ws.data_ptr(), ws.numel(),
+                            stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError("ssm_scan_fwd failed with status %d" % st)
+
+    fwd_ckpt_ms = timed(fwd_ckpt)
+    fwd_ckpt()
+    bwd_ckpt_ms = timed(lambda: call(2))
     elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
     slots = elems * BWD_SLOTS_PER_ELEM + wl.batch * wl.dim * wl.seqlen * BWD_SLOTS_PER_ROW_STEP
     achieved = slots / (ms * 1e-3) / 1e12
@@ -355,7 +375,10 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
                          "unit": "TOP/s", "frac": achieved / (PEAK_SLOTS / 1e12), "traffic": None,
                          "model": "fp32 VALU issue slots (transcendental = 4), %.2f slots/element"
                                   % (slots / elems)},
-            "note": "zero-fill + chunk-state recompute + reverse pass + partial-copy sum"}
+            "with_forward_checkpoints": {"forward_ms": fwd_ckpt_ms, "backward_ms": bwd_ckpt_ms},
+            "note": "zero-fill + chunk-state recompute + reverse pass + partial-copy sum; "
+                    "with_forward_checkpoints: the forward writes the checkpoints and the "
+                    "backward skips its recomputation pass"}
 
 
 def main():

@@ -72,9 +72,19 @@ typedef enum {
 } ssm_status_t;
 
 /* flags bit 0: use the exact zero-order-hold B-bar of the "Method" section,
- * B-bar = (Delta A)^-1 (exp(Delta A) - 1) Delta B, instead of Delta B.
- * Every other bit must be zero (SSM_ERR_UNSUPPORTED otherwise). */
+ * B-bar = (Delta A)^-1 (exp(Delta A) - 1) Delta B, instead of Delta B. */
 #define SSM_FLAG_ZOH_B 0x1u
+
+/* flags bit 1 (ssm_scan_fwd with the Delta B form only, and ssm_scan_bwd):
+ * checkpoints for the backward pass.  The backward recomputes the scan's
+ * states from the state entering every 64-step chunk ("Hardware-aware state
+ * expansion": states are recomputed, not stored).  With this bit,
+ * ssm_scan_fwd writes those checkpoints into `workspace`, which must then be
+ * at least ssm_scan_bwd_workspace_bytes(...) bytes (see ssm_bwd.h), and
+ * ssm_scan_bwd given the same workspace reads them instead of running its own
+ * recomputation pass.  The forward's other outputs are unchanged bit for bit.
+ * Any other flag bit is SSM_ERR_UNSUPPORTED. */
+#define SSM_FLAG_CHECKPOINTS 0x2u
 
 /* SSM_ABI_VERSION of the loaded library. */
 int ssm_abi_version(void);
@@ -102,7 +112,10 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
  *            may be exactly h0 (each channel reads its h0 before writing hL)
  *            but must not otherwise overlap an input or y
  *   workspace, workspace_bytes: device scratch of at least
- *            ssm_scan_fwd_workspace_bytes(...) bytes (NULL allowed when 0)
+ *            ssm_scan_fwd_workspace_bytes(...) bytes (NULL allowed when 0);
+ *            with SSM_FLAG_CHECKPOINTS, the backward pass's workspace (at
+ *            least ssm_scan_bwd_workspace_bytes(...) bytes), which receives
+ *            the checkpoints and must not overlap any input or output
  * Supported sizes: batch <= 65535, seqlen <= 2^28 - 4096, dstate in {1, 2, 4, 8, 16}.
  */
 ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,

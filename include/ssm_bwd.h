@@ -7,8 +7,11 @@
  * in and read back from HBM.  ssm_scan_bwd returns the gradients of
  *     l = sum(dy * y) + sum(dhL * hL)
  * with respect to every input of ssm_scan_fwd (see ssm.h for the forward map
- * and layouts), for the Delta * B form of B-bar (flags must be 0: the exact
- * zero-order-hold form has no backward here).
+ * and layouts), for the Delta * B form of B-bar (the exact zero-order-hold
+ * form has no backward here: SSM_FLAG_ZOH_B is SSM_ERR_UNSUPPORTED).  flags
+ * may hold SSM_FLAG_CHECKPOINTS: `workspace` then already holds the
+ * checkpoints that ssm_scan_fwd wrote with that flag for the same x, dt,
+ * dt_bias, A, Bm and h0, and the recomputation pass is skipped.
  *
  * Per (b, d), with u_t = dt_t + dt_bias, Delta_t = softplus(u_t),
  * A-bar_t = exp(Delta_t A), s_t = C_t . h_t + Dskip x_t, ds_t = dy_t silu(z_t):
@@ -36,8 +39,9 @@
 extern "C" {
 #endif
 
-/* Device workspace ssm_scan_bwd needs: the recomputed state entering every
- * 128-step chunk, batch * dim * ceil(seqlen / 128) * dstate fp32 values. */
+/* Device workspace ssm_scan_bwd needs: the state entering every 64-step
+ * chunk (batch * dim * ceil(seqlen / 64) * dstate fp32 values, first) and 8
+ * partial copies of dBm and dCm (8 * 2 * batch * dstate * seqlen fp32). */
 size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
 
 /*

@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libssm.so")
 
 SSM_F32, SSM_BF16 = 0, 1
 SSM_FLAG_ZOH_B = 0x1
+SSM_FLAG_CHECKPOINTS = 0x2
 SSM_CONV_SILU = 0x1
 STATUS = {
     0: "SSM_OK", 1: "SSM_ERR_NULL_ARG", 2: "SSM_ERR_BAD_SHAPE", 3: "SSM_ERR_BAD_DTYPE",
@@ -112,9 +113,12 @@ def _stream(stream, device):
 
 def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
                  out_dtype=torch.float32, return_final_state=True, y=None, hL=None,
-                 zoh=False, stream=None):
+                 zoh=False, checkpoints=None, stream=None):
     """Fused selective scan; returns (y, hL) (hL is None unless requested).
-    zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B)."""
+    zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B).
+    checkpoints: a device buffer of ssm_scan_bwd_workspace_bytes(...) bytes
+    that receives the backward pass's checkpoints (SSM_FLAG_CHECKPOINTS); pass
+    it to ssm_scan_bwd with checkpoints_in_workspace=True."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -135,8 +139,12 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     yp = _ptr(y, "y", (batch, dim, L), out_dtype)
     hp = _ptr(hL, "hL", (batch, dim, N), f32)
     flags = SSM_FLAG_ZOH_B if zoh else 0
+    wp, wb = None, 0
+    if checkpoints is not None:
+        flags |= SSM_FLAG_CHECKPOINTS
+        wp, wb = _ptr(checkpoints, "checkpoints"), checkpoints.numel() * checkpoints.element_size()
     st = lib().ssm_scan_fwd(batch, dim, L, N, _dtype_code(ind), flags, *args, _dtype_code(y.dtype),
-                            yp, hp, None, 0, _stream(stream, x.device))
+                            yp, hp, wp, wb, _stream(stream, x.device))
     _check(st)
     return y, hL
 
@@ -166,11 +174,13 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
 
 
 def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=None, dhL=None,
-                 grad_dtype=torch.float32, workspace=None, stream=None):
+                 grad_dtype=torch.float32, workspace=None, checkpoints_in_workspace=False,
+                 stream=None):
     """Gradients of sum(dy * y) + sum(dhL * hL) through ssm_scan_fwd (Delta*B
     form).  Returns a dict: dx, ddt, dz (None without z) in grad_dtype; dBm,
     dCm, dA, dDskip, ddt_bias, dh0 in fp32 (dDskip / ddt_bias / dh0 are
-    computed for every call)."""
+    computed for every call).  checkpoints_in_workspace=True: `workspace`
+    holds the checkpoints a forward call wrote (SSM_FLAG_CHECKPOINTS)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -189,6 +199,8 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
     }
     need = lib().ssm_scan_bwd_workspace_bytes(batch, dim, L, N)
     if workspace is None:
+        if checkpoints_in_workspace:
+            raise ValueError("checkpoints_in_workspace needs the forward's workspace")
         workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
     args = [
         _ptr(x, "x", (batch, dim, L), ind), _ptr(dt, "dt", (batch, dim, L), ind),
@@ -203,7 +215,8 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
         _ptr(g["dCm"], "dCm"), _ptr(g["dA"], "dA"), _ptr(g["dDskip"], "dDskip"),
         _ptr(g["ddt_bias"], "ddt_bias"), _ptr(g["dh0"], "dh0"),
     ]
-    st = lib().ssm_scan_bwd(batch, dim, L, N, _dtype_code(ind), 0, *args, _dtype_code(grad_dtype),
+    flags = SSM_FLAG_CHECKPOINTS if checkpoints_in_workspace else 0
+    st = lib().ssm_scan_bwd(batch, dim, L, N, _dtype_code(ind), flags, *args, _dtype_code(grad_dtype),
                             *gargs, _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                             _stream(stream, dev))
     _check(st)

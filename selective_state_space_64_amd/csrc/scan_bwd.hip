@@ -19,12 +19,13 @@
 //   2. chunk_states_kernel: the forward recurrence once more (8 steps per
 //      lane, 128-step row chunks), keeping only the state entering every
 //      64-step chunk (batch*dim*ceil(L/64)*N floats of workspace);
-//   3. scan_bwd_kernel: 64-step chunks in reverse order.  Per chunk and state
-//      n the workgroup recomputes the chunk's states from its checkpoint with
-//      the forward in-row scan, folds the adjoint of each lane's 4 steps into
-//      an affine map, composes the maps of a row with the mirrored (reverse
-//      time) DPP scan, replays the lane's steps backwards and accumulates the
-//      gradients.  dBm and dCm sum over channels: each lane leaves its terms
+//   3. scan_bwd_kernel: 64-step chunks in reverse order.  Per chunk, for
+//      pairs of states (two independent chains in flight per wave, their DPP
+//      scans interleaved), the workgroup recomputes the chunk's states from
+//      its checkpoint with the forward in-row scan, folds the adjoint of each
+//      lane's 4 steps into an affine map, composes the maps of a row with the
+//      mirrored (reverse time) DPP scan, replays the lane's steps backwards
+//      and accumulates the gradients.  dBm and dCm sum over channels: each lane leaves its terms
 //      in LDS, the workgroup adds its 16 channels, and one atomic add per
 //      (state, step) goes to one of 8 partial copies chosen by workgroup
 //      index, so that the workgroups sharing a copy sit on one XCD (the
@@ -157,6 +158,87 @@ __device__ inline float add_lane_pair(float v)
         "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
         : "+v"(v));
     return v;
+}
+
+// Two independent forward row scans (see row_scan in scan_common.hpp),
+// interleaved so that each one's DPP read hazard is covered by the other's
+// instructions instead of wait states.
+__device__ inline void row_scan_x2(float &a0, float &b0, float &e0, float &h0,
+                                   float &a1, float &b1, float &e1, float &h1)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fma_f32 %2, %0, %3, %1\n\t"
+        "v_fma_f32 %6, %4, %7, %5\n\t"
+        "s_nop 0\n\t"
+        "v_mov_b32_dpp %3, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %7, %6 row_shr:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(a0), "+v"(b0), "=&v"(e0), "+v"(h0), "+v"(a1), "+v"(b1), "=&v"(e1), "+v"(h1));
+}
+
+// Two independent reverse row scans (see row_scan_rev), interleaved.
+__device__ inline void row_scan_rev_x2(float &a0, float &b0, float &e0, float &h0,
+                                       float &a1, float &b1, float &e1, float &h1)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shl:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shl:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shl:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fma_f32 %2, %0, %3, %1\n\t"
+        "v_fma_f32 %6, %4, %7, %5\n\t"
+        "s_nop 0\n\t"
+        "v_mov_b32_dpp %3, %2 row_shl:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %7, %6 row_shl:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(a0), "+v"(b0), "=&v"(e0), "+v"(h0), "+v"(a1), "+v"(b1), "=&v"(e1), "+v"(h1));
+}
+
+// Two row sums (see row_total_last), interleaved.
+__device__ inline void row_total_last_x2(float &v0, float &v1)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 0\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 0\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 0\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_add_f32_dpp %1, %1, %1 row_shr:8 row_mask:0xf bank_mask:0xf"
+        : "+v"(v0), "+v"(v1));
 }
 
 // Bm or Cm of one chunk into LDS as fp32, layout [n][q][lane] of float4 (the
@@ -303,14 +385,15 @@ __global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
     }
 }
 
+// 3 waves per SIMD: the two chains of a state pair need ~150 VGPRs.
 template <typename Tin, typename Tg, int N>
-__global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
+__global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 {
     constexpr int K = kKB, T = kTB, Q = K / 4, NP = N + 1;
     __shared__ float4 sB[N * Q * kRowB];
     __shared__ float4 sC[N * Q * kRowB];
-    // Per-channel dBm / dCm terms of one state, double-buffered by state
-    // parity: [buffer][dBm, dCm][channel][step].
+    // Per-channel dBm / dCm terms of the states in flight:
+    // [state of the pair][dBm, dCm][channel][step].
     __shared__ float4 sP[2][2][kChanB][T / 4];
     __shared__ float sAP[kChanB * NP];  // A * log2(e)
     __shared__ float sH[kChanB * NP];   // forward state entering the chunk
@@ -406,86 +489,120 @@ __global__ __launch_bounds__(kThreadsB, 4) void scan_bwd_kernel(BwdParams p)
         lds_barrier();
 
         const float4 *bp = sB + j, *cp = sC + j;
+        static_assert(N % 2 == 0 || N == 1, "states are processed in pairs");
+        constexpr int G = N >= 2 ? 2 : 1;  // states in flight per iteration
 #pragma unroll 1
-        for (int n = 0; n < N; ++n) {
-            const float a1 = ap[n];
-            const float An = a1 * kLn2;
-            float bv[K], cv[K], da[K], hh[K];
-            lds_run<K>(bp + n * Q * kRowB, bv);
-            lds_run<K>(cp + n * Q * kRowB, cv);
-
-            // forward states of this chunk, from the checkpoint (the input
-            // term Delta x B is recomputed where needed to save registers)
+        for (int n = 0; n < N; n += G) {
+            float a1[G], An[G], bv[G][K], cv[G][K], da[G][K], hh[G][K], ptot[G], hl[G];
 #pragma unroll
-            for (int i = 0; i < K; ++i) da[i] = exp2_hw(delta[i] * a1);
-            float hl = w[0] * bv[0];
+            for (int g = 0; g < G; ++g) {
+                a1[g] = ap[n + g];
+                An[g] = a1[g] * kLn2;
+                lds_run<K>(bp + (n + g) * Q * kRowB, bv[g]);
+                lds_run<K>(cp + (n + g) * Q * kRowB, cv[g]);
 #pragma unroll
-            for (int i = 1; i < K; ++i) hl = __builtin_fmaf(da[i], hl, w[i] * bv[i]);
-            const float ptot = exp2_hw(sumd * a1);
-            float aa = ptot;
-            float hend, h = hs[n];
-            row_scan(aa, hl, hend, h);
+                for (int i = 0; i < K; ++i) da[g][i] = exp2_hw(delta[i] * a1[g]);
+                hl[g] = w[0] * bv[g][0];
 #pragma unroll
-            for (int i = 0; i < K; ++i) {
-                h = __builtin_fmaf(da[i], h, w[i] * bv[i]);
-                hh[i] = h;
-                sacc[i] = __builtin_fmaf(cv[i], h, sacc[i]);
+                for (int i = 1; i < K; ++i) hl[g] = __builtin_fmaf(da[g][i], hl[g], w[i] * bv[g][i]);
+                ptot[g] = exp2_hw(sumd * a1[g]);
+            }
+            // forward states of this chunk, from the checkpoint
+            float aa[G], hend[G], h[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                aa[g] = ptot[g];
+                h[g] = hs[n + g];
+            }
+            if constexpr (G == 2) {
+                row_scan_x2(aa[0], hl[0], hend[0], h[0], aa[1], hl[1], hend[1], h[1]);
+            } else {
+                row_scan(aa[0], hl[0], hend[0], h[0]);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+#pragma unroll
+                for (int i = 0; i < K; ++i) {
+                    h[g] = __builtin_fmaf(da[g][i], h[g], w[i] * bv[g][i]);
+                    hh[g][i] = h[g];
+                    sacc[i] = __builtin_fmaf(cv[g][i], h[g], sacc[i]);
+                }
             }
 
             // adjoint: lane map mu_out = ptot mu_in + q over the lane's steps,
             // mu = A-bar lambda of the step just after the lane's last one
-            float q = ds[K - 1] * cv[K - 1];
+            float pm[G], qm[G], mend[G], mu[G];
 #pragma unroll
-            for (int i = K - 2; i >= 0; --i) q = __builtin_fmaf(da[i + 1], q, ds[i] * cv[i]);
-            float pm = ptot, qm = da[0] * q;
-            float mend, mu = mus[n];
-            row_scan_rev(pm, qm, mend, mu);
+            for (int g = 0; g < G; ++g) {
+                float q = ds[K - 1] * cv[g][K - 1];
+#pragma unroll
+                for (int i = K - 2; i >= 0; --i) q = __builtin_fmaf(da[g][i + 1], q, ds[i] * cv[g][i]);
+                pm[g] = ptot[g];
+                qm[g] = da[g][0] * q;
+                mu[g] = mus[n + g];
+            }
+            if constexpr (G == 2) {
+                row_scan_rev_x2(pm[0], qm[0], mend[0], mu[0], pm[1], qm[1], mend[1], mu[1]);
+            } else {
+                row_scan_rev(pm[0], qm[0], mend[0], mu[0]);
+            }
             if (j == 0) {
-                mus[n] = mend;
-                if (ch == 0 && live && p.dh0) p.dh0[(size_t(b) * dim + d) * N + n] = mend;
-            }
-            float lam = mu, dap = 0.0f, gbv[K], gcv[K];
 #pragma unroll
-            for (int i = K - 1; i >= 0; --i) {
-                lam = __builtin_fmaf(ds[i], cv[i], lam);
-                const float hpa = __builtin_fmaf(-w[i], bv[i], hh[i]);  // A-bar h_{t-1}
-                const float lh = lam * hpa;
-                sah[i] = __builtin_fmaf(An, lh, sah[i]);
-                dap = __builtin_fmaf(delta[i], lh, dap);
-                sb[i] = __builtin_fmaf(lam, bv[i], sb[i]);
-                gbv[i] = lam * w[i];
-                gcv[i] = ds[i] * hh[i];
-                lam *= da[i];
+                for (int g = 0; g < G; ++g) {
+                    mus[n + g] = mend[g];
+                    if (ch == 0 && live && p.dh0) p.dh0[(size_t(b) * dim + d) * N + n + g] = mend[g];
+                }
             }
-            dap = row_total_last(dap);
-            if (j == kRowB - 1) das[n] += dap;
+            float dap[G];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                float lam = mu[g], gbv[K], gcv[K];
+                dap[g] = 0.0f;
+#pragma unroll
+                for (int i = K - 1; i >= 0; --i) {
+                    lam = __builtin_fmaf(ds[i], cv[g][i], lam);
+                    const float hpa = __builtin_fmaf(-w[i], bv[g][i], hh[g][i]);  // A-bar h_{t-1}
+                    const float lh = lam * hpa;
+                    sah[i] = __builtin_fmaf(An[g], lh, sah[i]);
+                    dap[g] = __builtin_fmaf(delta[i], lh, dap[g]);
+                    sb[i] = __builtin_fmaf(lam, bv[g][i], sb[i]);
+                    gbv[i] = lam * w[i];
+                    gcv[i] = ds[i] * hh[g][i];
+                    lam *= da[g][i];
+                }
+                sP[g][0][c][j] = make_float4(gbv[0], gbv[1], gbv[2], gbv[3]);
+                sP[g][1][c][j] = make_float4(gcv[0], gcv[1], gcv[2], gcv[3]);
+            }
+            if constexpr (G == 2) {
+                row_total_last_x2(dap[0], dap[1]);
+            } else {
+                dap[0] = row_total_last(dap[0]);
+            }
+            if (j == kRowB - 1) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) das[n + g] += dap[g];
+            }
 
-            // dBm[b, n, t] and dCm[b, n, t] sum over channels: each lane
-            // leaves its terms in LDS; neighbouring lanes 2i, 2i + 1 add 8
-            // channels each for one (quantity, step), combine through DPP,
-            // and the even lane issues the atomic add into this workgroup's
-            // copy.
-            const int pb = n & 1;
-#pragma unroll
-            for (int q4 = 0; q4 < K / 4; ++q4) {
-                sP[pb][0][c][j * (K / 4) + q4] =
-                    make_float4(gbv[4 * q4], gbv[4 * q4 + 1], gbv[4 * q4 + 2], gbv[4 * q4 + 3]);
-                sP[pb][1][c][j * (K / 4) + q4] =
-                    make_float4(gcv[4 * q4], gcv[4 * q4 + 1], gcv[4 * q4 + 2], gcv[4 * q4 + 3]);
-            }
+            // dBm[b, n, t] and dCm[b, n, t] sum over channels: lanes 2i, 2i + 1
+            // add 8 channels each for one (state, quantity, step), combine
+            // through DPP, and the even lane issues the atomic add into this
+            // workgroup's copy.
             lds_barrier();
-            {
-                const int pair = tid >> 1;  // 0..127 = (quantity, step)
+#pragma unroll
+            for (int rep = 0; rep < G; ++rep) {
+                const int trip = rep * (kThreadsB / 2) + (tid >> 1);  // (state, quantity, step)
                 const int half = tid & 1;
-                const int qq = pair / T, t = pair % T;
-                const float *col = reinterpret_cast<const float *>(&sP[pb][qq][half * (kChanB / 2)][0]) + t;
+                const int g = trip / (2 * T), qq = (trip / T) & 1, t = trip % T;
+                const float *col = reinterpret_cast<const float *>(&sP[g][qq][half * (kChanB / 2)][0]) + t;
                 float acc = 0.0f;
 #pragma unroll
                 for (int cc = 0; cc < kChanB / 2; ++cc) acc += col[cc * T];
                 acc = add_lane_pair(acc);
                 const int tt = ch * T + t;
-                if (half == 0 && tt < L) atomicAdd(&part[size_t(qq) * bnl + size_t(n) * L + tt], acc);
+                if (half == 0 && tt < L)
+                    atomicAdd(&part[size_t(qq) * bnl + size_t(n + g) * L + tt], acc);
             }
+            lds_barrier();
         }
 
         // per-step gradients of this chunk
@@ -535,7 +652,8 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
                        size_t(kCopies) * 2 * nbc, a.dA, size_t(a.dim) * N, a.dDskip, size_t(a.dim),
                        a.ddt_bias, size_t(a.dim));
     const dim3 grid((a.dim + kChanB - 1) / kChanB, a.batch);
-    hipLaunchKernelGGL((chunk_states_kernel<Tin, N>), grid, dim3(kThreadsB), 0, stream, p);
+    if (!a.ckpt_given)
+        hipLaunchKernelGGL((chunk_states_kernel<Tin, N>), grid, dim3(kThreadsB), 0, stream, p);
     hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, N>), grid, dim3(kThreadsB), 0, stream, p);
     hipLaunchKernelGGL(bwd_sum_kernel, dim3(1024), dim3(256), 0, stream, part, nbc, a.dBm, a.dCm);
     return hipGetLastError();

@@ -71,6 +71,8 @@ struct ScanParams {
     const float *h0;
     void *y;
     float *hL;
+    float *ck;  // optional: state entering every 64-step chunk, [batch][dim][nck][N]
+    int nck;
 };
 
 __device__ inline bool aligned16(const void *p)
@@ -78,7 +80,7 @@ __device__ inline bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-template <typename Tin, typename Tout, int N, int K, bool kZoh>
+template <typename Tin, typename Tout, int N, int K, bool kZoh, bool kCkpt>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kernel(ScanParams p)
 {
     static_assert(K % 8 == 0, "K must be a multiple of 8");
@@ -277,9 +279,18 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
 #pragma unroll
             for (int i = 1; i < K; ++i) hl = __builtin_fmaf(dA[i], hl, bb[i]);
             float aa = exp2_hw(sumd * ap);
+            [[maybe_unused]] const float cin = carry;
             float hend, h = carry;
             row_scan(aa, hl, hend, h);
             if (j == kRow - 1) aptr[NP + n] = hend;
+            if constexpr (kCkpt) {
+                // checkpoints for the backward pass: the state entering each
+                // 64-step half of the chunk (the carry, and lane 7's end)
+                static_assert(kRow * K == 128, "two 64-step checkpoints per chunk");
+                const int half = j == kRow / 2 - 1 ? 1 : 0;
+                if (live && (j == 0 || half) && 2 * ch + half < p.nck)
+                    p.ck[((size_t(b) * dim + d) * p.nck + 2 * ch + half) * N + n] = half ? hend : cin;
+            }
             bp += Q * kRow;
             load_b(bp, bv);          // next state's B (one past the end on the last state)
             ap = aptr[n + 1];
@@ -354,9 +365,17 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
 {
     constexpr int K = kK;
     ScanParams p{a.dim, a.seqlen, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
-                 a.Dskip, a.z, a.h0, a.y, a.hL};
+                 a.Dskip, a.z, a.h0, a.y, a.hL, a.ck, (a.seqlen + 63) / 64};
     dim3 grid((a.dim + kChannels - 1) / kChannels, a.batch);
-    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh>), grid, dim3(kThreads), 0, stream, p);
+    if constexpr (!kZoh) {
+        if (a.ck) {
+            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true>), grid, dim3(kThreads),
+                               0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false>), grid, dim3(kThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 

@@ -63,7 +63,7 @@ const char *ssm_status_string(ssm_status_t s)
     case SSM_ERR_ALIAS: return "an output buffer overlaps an input it must not overlap";
     case SSM_ERR_UNSUPPORTED:
         return "unsupported dstate (1, 2, 4, 8 or 16) or conv width (2, 3 or 4), or an unknown flag bit";
-    case SSM_ERR_WORKSPACE: return "workspace smaller than ssm_scan_fwd_workspace_bytes";
+    case SSM_ERR_WORKSPACE: return "workspace smaller than the documented size for this call";
     case SSM_ERR_HIP: return "the HIP runtime rejected the kernel launch";
     }
     return "unknown status";
@@ -85,12 +85,17 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
         return SSM_ERR_BAD_SHAPE;
-    if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_ZOH_B) != 0) return SSM_ERR_UNSUPPORTED;
+    if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS)) != 0 ||
+        flags == (SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS))
+        return SSM_ERR_UNSUPPORTED;
 
     const size_t seq_elems = mul3(batch, dim, seqlen);
     const size_t bc_elems = mul3(batch, dstate, seqlen);
     const size_t st_elems = mul3(batch, dim, dstate);
     if (!seq_elems || !bc_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+    const bool ckpt = (flags & SSM_FLAG_CHECKPOINTS) != 0;
+    const size_t ck_bytes = ckpt ? ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate) : 0;
+    if (ckpt && !workspace) return SSM_ERR_NULL_ARG;
 
     const size_t in = dsize(in_dtype);
     for (const void *p : {x, dt, Bm, Cm, z})
@@ -99,9 +104,11 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           (const void *)h0, (const void *)hL})
         if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
     if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+    if (ckpt && misaligned(workspace, 4)) return SSM_ERR_MISALIGNED;
 
     const size_t ybytes = seq_elems * dsize(out_dtype);
     const size_t hbytes = st_elems * sizeof(float);
+    if (ckpt && workspace_bytes < ck_bytes) return SSM_ERR_WORKSPACE;
     struct In {
         const void *p;
         size_t bytes;
@@ -114,15 +121,18 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
         // hL may be exactly h0 (read before written per channel), nothing else
         if (hL && !(i.p == h0 && hL == h0) && overlaps(hL, hbytes, i.p, i.bytes))
             return SSM_ERR_ALIAS;
+        if (ckpt && overlaps(workspace, ck_bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
     }
     if (overlaps(y, ybytes, hL, hbytes)) return SSM_ERR_ALIAS;
+    if (ckpt && (overlaps(workspace, ck_bytes, y, ybytes) || overlaps(workspace, ck_bytes, hL, hbytes)))
+        return SSM_ERR_ALIAS;
 
     if (workspace_bytes < ssm_scan_fwd_workspace_bytes(batch, dim, seqlen, dstate))
         return SSM_ERR_WORKSPACE;
-    (void)workspace;
 
     ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
-                    (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL};
+                    (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,
+                    ckpt ? static_cast<float *>(workspace) : nullptr};
     const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
@@ -278,7 +288,7 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
     if (!valid_dtype(in_dtype) || !valid_dtype(grad_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
         return SSM_ERR_BAD_SHAPE;
-    if (!valid_dstate(dstate) || flags != 0) return SSM_ERR_UNSUPPORTED;
+    if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_CHECKPOINTS) != 0) return SSM_ERR_UNSUPPORTED;
 
     const size_t seq_elems = mul3(batch, dim, seqlen);
     const size_t bc_elems = mul3(batch, dstate, seqlen);
@@ -325,7 +335,7 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
     }
     ssm::BwdArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, grad_dtype == SSM_BF16,
                    x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy, dhL, dx, ddt, dz, dBm, dCm, dA,
-                   dDskip, ddt_bias, dh0, workspace};
+                   dDskip, ddt_bias, dh0, workspace, (flags & SSM_FLAG_CHECKPOINTS) != 0};
     const hipError_t e = ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -17,6 +17,7 @@ struct ScanArgs {
     const float *h0;
     void *y;
     float *hL;
+    float *ck;  // optional checkpoint output (state entering each 64-step chunk)
 };
 
 struct UpdateArgs {
@@ -63,6 +64,7 @@ struct BwdArgs {
     void *dx, *ddt, *dz;
     float *dBm, *dCm, *dA, *dDskip, *ddt_bias, *dh0;
     void *workspace;
+    int ckpt_given;  // the workspace already holds the forward's checkpoints
 };
 
 // Device workspace of the backward pass: the state entering every chunk.

@@ -104,8 +104,9 @@ ERRORS = [
     ("batch0", dict(batch=0), 2), ("dim_neg", dict(dim=-1), 2), ("L0", dict(seqlen=0), 2),
     ("batch_huge", dict(batch=70000), 2), ("L_huge", dict(seqlen=(1 << 28) - 4095), 2),
     ("in_dtype", dict(in_dtype=7), 3), ("out_dtype", dict(out_dtype=-1), 3),
-    ("N3", dict(dstate=3), 6), ("N32", dict(dstate=32), 6), ("flag_bit1", dict(flags=2), 6),
-    ("flag_other", dict(flags=0x81), 6),
+    ("N3", dict(dstate=3), 6), ("N32", dict(dstate=32), 6), ("flag_bit2", dict(flags=4), 6),
+    ("flag_other", dict(flags=0x81), 6), ("zoh_with_checkpoints", dict(flags=3), 6),
+    ("checkpoints_without_workspace", dict(flags=2), 1),
 ]
 
 
@@ -216,6 +217,13 @@ def test_validation_alignment_and_alias():
     assert _fake_call(hL=_FAKE["h0"]) == 8                # hL == h0 exactly is allowed
     assert _fake_call(z=None, h0=None, hL=None, Dskip=None, dt_bias=None) == 8
     assert _fake_call(flags=1) == 8  # SSM_FLAG_ZOH_B is accepted
+    # SSM_FLAG_CHECKPOINTS: the backward's workspace size, no overlap, aligned
+    need = ssm.lib().ssm_scan_bwd_workspace_bytes(2, 8, 40, 16)
+    ws = 0x200000000  # clear of every fake buffer above
+    assert _fake_call(flags=2, ws=ws, wsb=need - 4) == 7
+    assert _fake_call(flags=2, ws=ws + 2, wsb=need) == 4
+    assert _fake_call(flags=2, ws=_FAKE["y"], wsb=need) == 5
+    assert _fake_call(flags=2, ws=ws, wsb=need) == 8
 
 
 @no_gpu

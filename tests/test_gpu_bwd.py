@@ -251,3 +251,35 @@ def test_bwd_unaligned_pointers_and_guard_bands():
     for k, (big, lo, n) in bigs.items():
         bits = big.view(torch.int32).cpu().numpy()
         assert (bits[:lo] == 0x7FC0DEAD).all() and (bits[lo + n:] == 0x7FC0DEAD).all(), k
+
+
+@pytest.mark.parametrize("shape", [(2, 48, 16, 2048, "bf16"), (1, 17, 8, 1000, "f32"),
+                                   (2, 5, 1, 777, "f32"), (1, 3, 16, 7, "bf16"),
+                                   (2, 20, 4, 64, "bf16")],
+                         ids=lambda s: "b%d_d%d_N%d_L%d_%s" % s)
+def test_bwd_checkpoints_from_forward(shape):
+    """SSM_FLAG_CHECKPOINTS: the forward writes the state entering every
+    64-step chunk into the backward's workspace without changing its own
+    outputs, and the backward that reads them matches the one that
+    recomputes them (bit for bit where no atomics are involved)."""
+    batch, dim, N, L, dt = shape
+    inp = synth.make_inputs(workload("ckpt", batch, dim, N, L, dt, seed=13), with_h0=True)
+    t = {k: to_dev(inp, k) for k in ("x", "dt", "A", "Bm", "Cm", "dt_bias", "Dskip", "z")}
+    h0 = torch.from_numpy(inp.h0).cuda()
+    kw = dict(dt_bias=t["dt_bias"], Dskip=t["Dskip"], z=t["z"], h0=h0)
+    need = ssm.lib().ssm_scan_bwd_workspace_bytes(batch, dim, L, N)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    y0, hL0 = ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], **kw)
+    y1, hL1 = ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], checkpoints=ws, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(hL0, hL1)
+    dy = torch.from_numpy(np.random.default_rng(13).standard_normal((batch, dim, L),
+                                                                    dtype=np.float32)).cuda()
+    g0 = ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy, **kw)
+    g1 = ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy, workspace=ws,
+                          checkpoints_in_workspace=True, **kw)
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dz", "dh0"):
+        assert torch.equal(g0[k], g1[k]), k
+    for k in ("dBm", "dCm", "dA", "dDskip", "ddt_bias"):
+        assert float((g0[k] - g1[k]).abs().max()) <= 1e-5 * float(g0[k].abs().max()) + 1e-30, k
