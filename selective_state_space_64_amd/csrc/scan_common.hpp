@@ -53,6 +53,7 @@ __device__ inline void row_scan(float &a, float &b, float &hend, float &h)
 template <typename Tout, int K>
 __device__ inline void store_y(Tout *dst, bool vec, int count, const float *v)
 {
+    static_assert(K % (16 / sizeof(Tout)) == 0, "a run must be whole 16-byte vectors");
     if constexpr (sizeof(Tout) == 4) {
         if (vec) {
             f32x4 *q = reinterpret_cast<f32x4 *>(dst);

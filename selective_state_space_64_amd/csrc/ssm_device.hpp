@@ -72,6 +72,7 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi)
 template <typename T, int n>
 __device__ inline void load_run(const T *p, bool vec, int count, float *out)
 {
+    static_assert(n % io<T>::kVec == 0, "a run must be whole 16-byte vectors");
     if (vec) {
         const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
 #pragma unroll
@@ -95,6 +96,7 @@ template <typename T, int n> struct raw_run {
 template <typename T, int n>
 __device__ inline void load_raw(const T *p, bool vec, int count, raw_run<T, n> &r)
 {
+    static_assert(n % io<T>::kVec == 0, "a run must be whole 16-byte vectors");
     if (vec) {
         const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
 #pragma unroll
