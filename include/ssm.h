@@ -4,7 +4,8 @@
  * Two operations, both from the page "Mamba: Linear-Time Sequence Modeling
  * with Selective State Spaces" (reading guide to arXiv 2312.00752):
  *
- *   ssm_scan_fwd      the fused selective scan over a whole sequence.
+ *   ssm_scan_fwd      the fused selective scan over a whole sequence
+ *                     (ssm_scan_fwd_strided: the same on strided views).
  *                     "Method": A-bar = exp(Delta A) by zero-order hold; the
  *                     recurrence h_t = A-bar_t h_{t-1} + B-bar_t x_t; the
  *                     readout y_t = C_t h_t taken after the step-t update.
@@ -26,7 +27,8 @@
  *
  * Conventions for every entry point:
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
- *     densely packed (last index fastest).  The library allocates nothing,
+ *     densely packed (last index fastest), except where a layout argument
+ *     gives strides.  The library allocates nothing,
  *     keeps no state between calls, and is reentrant.
  *   - Layouts: x, dt, z, y      [batch][dim][seqlen]
  *              Bm, Cm           [batch][dstate][seqlen]
@@ -123,6 +125,53 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           const float *A, const void *Bm, const void *Cm, const float *Dskip,
                           const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
                           float *hL, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Strided layouts for ssm_scan_fwd_strided.  The Mamba block (glossary entry
+ * "Mamba Block" of the same reading-guide page) feeds the scan from one input
+ * projection that yields both the SSM branch x and the gate z, so the two
+ * usually arrive as halves of one [batch][2 dim][seqlen] buffer; Bm and Cm
+ * likewise as parts of one projection.  These strides let such views be
+ * passed without a copy.  All strides are in ELEMENTS of the tensor's own
+ * type; time is always the contiguous index (stride 1).
+ *   seq_row        distance between consecutive channels (rows) of x, dt, z
+ *                  and y, shared by the four; >= seqlen; 0 means seqlen
+ *   seq_batch[4]   distance between batch entries of x, dt, z, y (in that
+ *                  order); each >= dim * seq_row; 0 means dim * seq_row
+ *   bc_row         distance between consecutive states of Bm and Cm; >= seqlen;
+ *                  0 means seqlen
+ *   bc_batch[2]    distance between batch entries of Bm, Cm; each >=
+ *                  dstate * bc_row; 0 means dstate * bc_row
+ * Strides of 0 everywhere (or a NULL layout) give the dense layout of
+ * ssm_scan_fwd.  Each row start is aligned like any other element; the
+ * kernels still use 16-byte vector accesses when the strides keep rows on
+ * 16-byte boundaries.  A negative stride, one below its minimum, seq_row or
+ * bc_row above 2^28 - 4096, or a tensor spanning 2^56 elements or more is
+ * SSM_ERR_BAD_SHAPE.
+ */
+typedef struct {
+    long long seq_row;
+    long long seq_batch[4];
+    long long bc_row;
+    long long bc_batch[2];
+} ssm_scan_layout_t;
+
+/*
+ * ssm_scan_fwd on strided inputs and output: the same arguments, flags and
+ * errors, with `layout` (host pointer, read during the call only; NULL means
+ * dense) giving the strides of x, dt, z, y, Bm and Cm.  A, Dskip, dt_bias, h0,
+ * hL and the checkpoints stay dense.  Overlap is judged on address ranges: y
+ * and hL must not overlap the range from the first to the last element of any
+ * input (as laid out by the strides), so y may not be interleaved with an
+ * input even where no element coincides.
+ */
+ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
+                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                                  float *hL, void *workspace, size_t workspace_bytes,
+                                  const ssm_scan_layout_t *layout, void *stream);
 
 /*
  * One decode step (seqlen = 1) on a persistent state.

@@ -35,8 +35,14 @@ STATUS = {
     7: "SSM_ERR_WORKSPACE", 8: "SSM_ERR_HIP",
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
-           "ssm_scan_fwd", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_update",
+           "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_update",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd"]
+
+
+class ScanLayout(ctypes.Structure):
+    """ssm_scan_layout_t: strides in elements, 0 = dense default."""
+    _fields_ = [("seq_row", ctypes.c_longlong), ("seq_batch", ctypes.c_longlong * 4),
+                ("bc_row", ctypes.c_longlong), ("bc_batch", ctypes.c_longlong * 2)]
 
 
 class SSMError(RuntimeError):
@@ -65,6 +71,9 @@ def lib():
         L.ssm_scan_fwd_workspace_bytes.argtypes = [i, i, i, i]
         L.ssm_scan_fwd.restype = i
         L.ssm_scan_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 9 + [i, vp, vp, vp, sz, vp]
+        L.ssm_scan_fwd_strided.restype = i
+        L.ssm_scan_fwd_strided.argtypes = ([i, i, i, i, i, u] + [vp] * 9 +
+                                           [i, vp, vp, vp, sz, ctypes.POINTER(ScanLayout), vp])
         L.ssm_state_update.restype = i
         L.ssm_state_update.argtypes = [i, i, i, i, u] + [vp] * 9 + [i, vp, vp]
         L.ssm_scan_bwd_workspace_bytes.restype = sz
@@ -106,6 +115,38 @@ def _ptr(t, name, shape=None, dtype=None):
     return t.data_ptr()
 
 
+def _rows(ts, names, shape, dtype):
+    """Pointers, shared row stride and batch strides of [batch, rows, L]
+    tensors whose time index is contiguous (views such as halves of one
+    projection output).  Strides of size-1 dimensions are free and read as the
+    dense default (0)."""
+    batch, rows, L = shape
+    ptrs, bstrides, rstride = [], [], None
+    for t, name in zip(ts, names):
+        if t is None:
+            ptrs.append(None)
+            bstrides.append(0)
+            continue
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        want = dtype[name] if isinstance(dtype, dict) else dtype
+        if t.dtype != want:
+            raise TypeError("%s must be %s, got %s" % (name, want, t.dtype))
+        if L > 1 and t.stride(2) != 1:
+            raise ValueError("%s must have a contiguous time index (stride 1)" % name)
+        if rows > 1:
+            if rstride is None:
+                rstride = t.stride(1)
+            elif t.stride(1) != rstride:
+                raise ValueError("%s must share the row stride of %s (%d, got %d)"
+                                 % (name, "/".join(names), rstride, t.stride(1)))
+        ptrs.append(t.data_ptr())
+        bstrides.append(t.stride(0) if batch > 1 else 0)
+    return ptrs, (rstride if rstride is not None else 0), bstrides
+
+
 def _stream(stream, device):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return s.cuda_stream
@@ -115,6 +156,9 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
                  out_dtype=torch.float32, return_final_state=True, y=None, hL=None,
                  zoh=False, checkpoints=None, stream=None):
     """Fused selective scan; returns (y, hL) (hL is None unless requested).
+    x, dt, z, y (and Bm, Cm) may be strided views with a contiguous time
+    index and one row stride shared among them, e.g. x and z as the two
+    halves of one [batch, 2 dim, L] projection output.
     zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B).
     checkpoints: a device buffer of ssm_scan_bwd_workspace_bytes(...) bytes
     that receives the backward pass's checkpoints (SSM_FLAG_CHECKPOINTS); pass
@@ -129,22 +173,25 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     if hL is None and return_final_state:
         hL = torch.empty((batch, dim, N), dtype=torch.float32, device=x.device)
     f32 = torch.float32
+    (xp, dtp, zp, yp), row, seq_b = _rows(
+        (x, dt, z, y), ("x", "dt", "z", "y"), (batch, dim, L),
+        {"x": ind, "dt": ind, "z": ind, "y": out_dtype})
+    (Bp, Cp), bc_row, bc_b = _rows((Bm, Cm), ("Bm", "Cm"), (batch, N, L), ind)
+    layout = ScanLayout(row, (ctypes.c_longlong * 4)(*seq_b), bc_row,
+                        (ctypes.c_longlong * 2)(*bc_b))
     args = [
-        _ptr(x, "x", (batch, dim, L), ind), _ptr(dt, "dt", (batch, dim, L), ind),
-        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
-        _ptr(Bm, "Bm", (batch, N, L), ind), _ptr(Cm, "Cm", (batch, N, L), ind),
-        _ptr(Dskip, "Dskip", (dim,), f32), _ptr(z, "z", (batch, dim, L), ind),
-        _ptr(h0, "h0", (batch, dim, N), f32),
+        xp, dtp, _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
+        Bp, Cp, _ptr(Dskip, "Dskip", (dim,), f32), zp, _ptr(h0, "h0", (batch, dim, N), f32),
     ]
-    yp = _ptr(y, "y", (batch, dim, L), out_dtype)
     hp = _ptr(hL, "hL", (batch, dim, N), f32)
     flags = SSM_FLAG_ZOH_B if zoh else 0
     wp, wb = None, 0
     if checkpoints is not None:
         flags |= SSM_FLAG_CHECKPOINTS
         wp, wb = _ptr(checkpoints, "checkpoints"), checkpoints.numel() * checkpoints.element_size()
-    st = lib().ssm_scan_fwd(batch, dim, L, N, _dtype_code(ind), flags, *args, _dtype_code(y.dtype),
-                            yp, hp, wp, wb, _stream(stream, x.device))
+    st = lib().ssm_scan_fwd_strided(batch, dim, L, N, _dtype_code(ind), flags, *args,
+                                    _dtype_code(y.dtype), yp, hp, wp, wb, ctypes.byref(layout),
+                                    _stream(stream, x.device))
     _check(st)
     return y, hL
 

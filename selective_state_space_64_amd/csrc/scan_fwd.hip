@@ -63,6 +63,10 @@ constexpr int kMinWavesPerSimd = sizeof(Tin) == 2 ? SSM_SCAN_MINW_BF16 : SSM_SCA
 
 struct ScanParams {
     int dim, seqlen;
+    // Layout in elements: every row of x, dt, z, y (one channel) and of Bm,
+    // Cm (one state) holds seqlen contiguous steps; rows of a batch entry are
+    // `row` apart (x, dt, z, y share it), batch entries are `*_b` apart.
+    long long row, x_b, dt_b, z_b, y_b, bc_row, B_b, C_b;
     const void *x, *dt;
     const float *dt_bias, *A;
     const void *Bm, *Cm;
@@ -113,20 +117,22 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     // Wave-uniform row base (its first channel, clamped) and per-lane offset.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int d0 = min(int(blockIdx.x) * kChannels + wave * 4, dim - 1);
-    const size_t row0 = (size_t(b) * dim + d0) * size_t(L);
-    const Tin *xw = static_cast<const Tin *>(p.x) + row0;
-    const Tin *dtw = static_cast<const Tin *>(p.dt) + row0;
-    const Tin *zw = p.z ? static_cast<const Tin *>(p.z) + row0 : nullptr;
-    Tout *yw = static_cast<Tout *>(p.y) + row0;
-    const uint32_t lane_row = uint32_t(dc - d0) * uint32_t(L);  // elements
-    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * N * L;
-    const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * N * L;
+    const size_t row0 = size_t(d0) * size_t(p.row);
+    const Tin *xw = static_cast<const Tin *>(p.x) + size_t(b) * size_t(p.x_b) + row0;
+    const Tin *dtw = static_cast<const Tin *>(p.dt) + size_t(b) * size_t(p.dt_b) + row0;
+    const Tin *zw = p.z ? static_cast<const Tin *>(p.z) + size_t(b) * size_t(p.z_b) + row0 : nullptr;
+    Tout *yw = static_cast<Tout *>(p.y) + size_t(b) * size_t(p.y_b) + row0;
+    const uint32_t lane_row = uint32_t(dc - d0) * uint32_t(p.row);  // elements
+    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * size_t(p.B_b);
+    const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * size_t(p.C_b);
     // Wave-uniform: every row of every streamed tensor starts on a 16-byte
     // boundary, so all runs of a chunk that lies inside the sequence can use
     // unguarded 16-byte vector accesses.
-    const bool rows_vec = aligned16(p.x) && aligned16(p.dt) && (!p.z || aligned16(p.z)) &&
-                          aligned16(p.y) && aligned16(p.Bm) && aligned16(p.Cm) &&
-                          (size_t(L) * sizeof(Tin)) % 16 == 0 && (size_t(L) * sizeof(Tout)) % 16 == 0;
+    const bool rows_vec = aligned16(xw) && aligned16(dtw) && (!zw || aligned16(zw)) &&
+                          aligned16(yw) && aligned16(Bb) && aligned16(Cb) &&
+                          (size_t(p.row) * sizeof(Tin)) % 16 == 0 &&
+                          (size_t(p.row) * sizeof(Tout)) % 16 == 0 &&
+                          (size_t(p.bc_row) * sizeof(Tin)) % 16 == 0;
     auto chunk_full = [&](int chunk) { return rows_vec && (chunk + 1) * T <= L; };
 
     for (int s = tid; s < kChannels * NP; s += kThreads) {
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     raw_run<Tin, K> stB, stC;
     auto stage_load = [&](const Tin *src, int chunk, raw_run<Tin, K> &st) {
         const int l = chunk * T + sj * K;
-        const Tin *q = src + size_t(sn) * size_t(L) + l;
+        const Tin *q = src + size_t(sn) * size_t(p.bc_row) + l;
         if (chunk_full(chunk)) {
             load_raw<Tin, K>(q, true, K, st);
         } else {
@@ -364,7 +370,8 @@ template <typename Tin, typename Tout, int N, bool kZoh>
 hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
 {
     constexpr int K = kK;
-    ScanParams p{a.dim, a.seqlen, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
+    ScanParams p{a.dim, a.seqlen, a.row, a.x_b, a.dt_b, a.z_b, a.y_b, a.bc_row, a.B_b, a.C_b,
+                 a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
                  a.Dskip, a.z, a.h0, a.y, a.hL, a.ck, (a.seqlen + 63) / 64};
     dim3 grid((a.dim + kChannels - 1) / kChannels, a.batch);
     if constexpr (!kZoh) {

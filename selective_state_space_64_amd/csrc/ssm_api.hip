@@ -81,6 +81,19 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
                           float *hL, void *workspace, size_t workspace_bytes, void *stream)
 {
+    return ssm_scan_fwd_strided(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A,
+                                Bm, Cm, Dskip, z, h0, out_dtype, y, hL, workspace,
+                                workspace_bytes, nullptr, stream);
+}
+
+ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
+                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                                  float *hL, void *workspace, size_t workspace_bytes,
+                                  const ssm_scan_layout_t *layout, void *stream)
+{
     if (!x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
@@ -89,10 +102,30 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
         flags == (SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS))
         return SSM_ERR_UNSUPPORTED;
 
-    const size_t seq_elems = mul3(batch, dim, seqlen);
-    const size_t bc_elems = mul3(batch, dstate, seqlen);
     const size_t st_elems = mul3(batch, dim, dstate);
-    if (!seq_elems || !bc_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+    if (!mul3(batch, dim, seqlen) || !mul3(batch, dstate, seqlen) || !st_elems)
+        return SSM_ERR_BAD_SHAPE;
+    const ssm_scan_layout_t dense{};
+    const ssm_scan_layout_t &lay = layout ? *layout : dense;
+    // Strides with defaults filled in, and each tensor's span in elements.
+    const long long row = lay.seq_row ? lay.seq_row : seqlen;
+    const long long bc_row = lay.bc_row ? lay.bc_row : seqlen;
+    if (row < seqlen || row > ssm::kMaxSeqlen || bc_row < seqlen || bc_row > ssm::kMaxSeqlen)
+        return SSM_ERR_BAD_SHAPE;
+    long long seq_b[4], bc_b[2];
+    size_t seq_span[4], bc_span[2];
+    auto strided = [&](long long given, int rows, long long rs, long long &sb, size_t &sp) {
+        sb = given ? given : rows * rs;
+        if (sb < rows * rs) return false;
+        const __int128 n = (__int128)(batch - 1) * sb + (__int128)(rows - 1) * rs + seqlen;
+        if (n >= ((__int128)1 << 56)) return false;
+        sp = size_t(n);
+        return true;
+    };
+    for (int i = 0; i < 4; ++i)
+        if (!strided(lay.seq_batch[i], dim, row, seq_b[i], seq_span[i])) return SSM_ERR_BAD_SHAPE;
+    for (int i = 0; i < 2; ++i)
+        if (!strided(lay.bc_batch[i], dstate, bc_row, bc_b[i], bc_span[i])) return SSM_ERR_BAD_SHAPE;
     const bool ckpt = (flags & SSM_FLAG_CHECKPOINTS) != 0;
     const size_t ck_bytes = ckpt ? ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate) : 0;
     if (ckpt && !workspace) return SSM_ERR_NULL_ARG;
@@ -106,16 +139,16 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
     if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
     if (ckpt && misaligned(workspace, 4)) return SSM_ERR_MISALIGNED;
 
-    const size_t ybytes = seq_elems * dsize(out_dtype);
+    const size_t ybytes = seq_span[3] * dsize(out_dtype);
     const size_t hbytes = st_elems * sizeof(float);
     if (ckpt && workspace_bytes < ck_bytes) return SSM_ERR_WORKSPACE;
     struct In {
         const void *p;
         size_t bytes;
-    } inputs[] = {{x, seq_elems * in},  {dt, seq_elems * in},       {dt_bias, dim * sizeof(float)},
+    } inputs[] = {{x, seq_span[0] * in}, {dt, seq_span[1] * in},    {dt_bias, dim * sizeof(float)},
                   {A, size_t(dim) * dstate * sizeof(float)},
-                  {Bm, bc_elems * in},  {Cm, bc_elems * in},        {Dskip, dim * sizeof(float)},
-                  {z, seq_elems * in},  {h0, hbytes}};
+                  {Bm, bc_span[0] * in}, {Cm, bc_span[1] * in},     {Dskip, dim * sizeof(float)},
+                  {z, seq_span[2] * in}, {h0, hbytes}};
     for (const In &i : inputs) {
         if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
         // hL may be exactly h0 (read before written per channel), nothing else
@@ -132,7 +165,8 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
 
     ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
                     (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,
-                    ckpt ? static_cast<float *>(workspace) : nullptr};
+                    ckpt ? static_cast<float *>(workspace) : nullptr,
+                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], bc_row, bc_b[0], bc_b[1]};
     const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

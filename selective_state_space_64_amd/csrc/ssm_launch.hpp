@@ -18,6 +18,9 @@ struct ScanArgs {
     void *y;
     float *hL;
     float *ck;  // optional checkpoint output (state entering each 64-step chunk)
+    // Strides in elements (time stride is 1): rows of x, dt, z, y are `row`
+    // apart, rows of Bm, Cm `bc_row` apart; batch entries `*_b` apart.
+    long long row, x_b, dt_b, z_b, y_b, bc_row, B_b, C_b;
 };
 
 struct UpdateArgs {

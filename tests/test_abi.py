@@ -57,7 +57,9 @@ def test_binding_argtypes_match_prototypes():
         argtypes = getattr(L, name).argtypes
         assert len(argtypes) == len(params), (name, len(argtypes), len(params))
         for decl, at in zip(params, argtypes):
-            if "*" in decl:
+            if "ssm_scan_layout_t" in decl:
+                assert at == ctypes.POINTER(ssm.ScanLayout), (name, decl, at)
+            elif "*" in decl:
                 assert at in (ctypes.c_void_p, ctypes.c_char_p), (name, decl, at)
             elif decl.startswith("size_t"):
                 assert at == ctypes.c_size_t, (name, decl, at)
@@ -224,6 +226,66 @@ def test_validation_alignment_and_alias():
     assert _fake_call(flags=2, ws=ws + 2, wsb=need) == 4
     assert _fake_call(flags=2, ws=_FAKE["y"], wsb=need) == 5
     assert _fake_call(flags=2, ws=ws, wsb=need) == 8
+
+
+def _strided_call(layout, **over):
+    a = dict(batch=2, dim=8, seqlen=40, dstate=16, in_dtype=1, flags=0, out_dtype=0,
+             ws=None, wsb=0, **_FAKE)
+    a.update(over)
+    lay = None
+    if layout is not None:
+        lay = ssm.ScanLayout(layout.get("seq_row", 0),
+                             (ctypes.c_longlong * 4)(*layout.get("seq_batch", (0, 0, 0, 0))),
+                             layout.get("bc_row", 0),
+                             (ctypes.c_longlong * 2)(*layout.get("bc_batch", (0, 0))))
+    return ssm.lib().ssm_scan_fwd_strided(
+        a["batch"], a["dim"], a["seqlen"], a["dstate"], a["in_dtype"], a["flags"], a["x"], a["dt"],
+        a["dt_bias"], a["A"], a["Bm"], a["Cm"], a["Dskip"], a["z"], a["h0"], a["out_dtype"], a["y"],
+        a["hL"], a["ws"], a["wsb"], ctypes.byref(lay) if lay is not None else None, None)
+
+
+STRIDE_ERRORS = [
+    ("row_below_L", dict(seq_row=39)), ("row_negative", dict(seq_row=-40)),
+    ("row_huge", dict(seq_row=(1 << 28) - 4095)),
+    ("x_batch_below", dict(seq_row=48, seq_batch=(8 * 48 - 1, 0, 0, 0))),
+    ("y_batch_below", dict(seq_batch=(0, 0, 0, 8 * 40 - 1))),
+    ("batch_negative", dict(seq_batch=(0, -1, 0, 0))),
+    ("bc_row_below_L", dict(bc_row=39)), ("bc_row_huge", dict(bc_row=1 << 28)),
+    ("Cm_batch_below", dict(bc_batch=(0, 16 * 40 - 1))),
+    ("span_2_56", dict(seq_batch=(1 << 56, 0, 0, 0))),
+]
+
+
+@no_gpu
+@pytest.mark.parametrize("name,layout", STRIDE_ERRORS, ids=[e[0] for e in STRIDE_ERRORS])
+def test_strided_validation_rejects_bad_strides(name, layout):
+    assert _strided_call(layout) == 2
+
+
+@no_gpu
+def test_strided_validation_spans_and_defaults():
+    # a NULL layout, or all strides 0, is the dense call (reaches the launch)
+    assert _strided_call(None) == 8
+    assert _strided_call({}) == 8
+    assert _strided_call(None, flags=1) == 8
+    assert _strided_call(None, batch=0) == 2
+    # strides equal to the dense ones, given explicitly
+    assert _strided_call(dict(seq_row=40, seq_batch=(320,) * 4, bc_row=40, bc_batch=(640, 640))) == 8
+    # x and z as halves of one [2, 16, 40] bf16 buffer: batch stride 640, and
+    # x's span runs to the end of its second batch entry (640 + 320 elements)
+    xz = dict(seq_batch=(640, 0, 640, 0))
+    assert _strided_call(xz, z=_FAKE["x"] + 320 * 2) == 8          # inputs may interleave
+    assert _strided_call(xz, y=_FAKE["x"] + 1280) == 5             # dense-free byte, inside the span
+    assert _strided_call(xz, y=_FAKE["x"] + 960 * 2) == 8          # just past x's span
+    # y strided: its span (fp32) is what hL must avoid
+    assert _strided_call(dict(seq_batch=(0, 0, 0, 1000)), hL=_FAKE["y"] + (1000 + 320) * 4 - 4) == 5
+    assert _strided_call(dict(seq_batch=(0, 0, 0, 1000)), hL=_FAKE["y"] + (1000 + 320) * 4) == 8
+    # padded rows: every row 48 apart
+    assert _strided_call(dict(seq_row=48, bc_row=41)) == 8
+    # Bm/Cm spans follow bc strides
+    bc = dict(bc_batch=(2 * 640, 2 * 640))
+    assert _strided_call(bc, y=_FAKE["Bm"] + (640 + 640) * 2 - 4) == 5
+    assert _strided_call(bc, y=_FAKE["Bm"] + (1280 + 640) * 2) == 8
 
 
 @no_gpu
