@@ -95,7 +95,18 @@ int ssm_abi_version(void);
 const char *ssm_status_string(ssm_status_t status);
 
 /* Device workspace ssm_scan_fwd needs for these sizes, in bytes (0: none;
- * the workspace argument may then be NULL). */
+ * the workspace argument may then be NULL).  It is non-zero when the
+ * sequence is split into segments scanned in parallel, which the library
+ * does when batch x ceil(dim / 16) is small (under 256) and seqlen long
+ * (segments of at least 1024 steps).  The recurrence is affine in the state,
+ * so each segment but the last first runs from a zero state (h0 for the
+ * first) to get its end state and Delta sum; the main pass then enters
+ * segment s with the earlier segments composed,
+ *     h <- exp(A sum_s Delta) h + (end state of s),
+ * the composition of the scan's associative operator over whole segments
+ * (the "Parallel Associative Scan" glossary entry of the reading-guide page).
+ * The workspace holds, per segment and (batch, channel), dstate + 1 floats.
+ * A function of the sizes only; invalid sizes give 0. */
 size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
 
 /*
@@ -114,7 +125,9 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
  *            may be exactly h0 (each channel reads its h0 before writing hL)
  *            but must not otherwise overlap an input or y
  *   workspace, workspace_bytes: device scratch of at least
- *            ssm_scan_fwd_workspace_bytes(...) bytes (NULL allowed when 0);
+ *            ssm_scan_fwd_workspace_bytes(...) bytes (NULL allowed when 0),
+ *            4-byte aligned, overlapping no input or output; its contents
+ *            are scratch before and after the call;
  *            with SSM_FLAG_CHECKPOINTS, the backward pass's workspace (at
  *            least ssm_scan_bwd_workspace_bytes(...) bytes), which receives
  *            the checkpoints and must not overlap any input or output

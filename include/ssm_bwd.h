@@ -41,7 +41,10 @@ extern "C" {
 
 /* Device workspace ssm_scan_bwd needs: the state entering every 64-step
  * chunk (batch * dim * ceil(seqlen / 64) * dstate fp32 values, first) and 8
- * partial copies of dBm and dCm (8 * 2 * batch * dstate * seqlen fp32). */
+ * partial copies of dBm and dCm (8 * 2 * batch * dstate * seqlen fp32), or,
+ * if larger, the forward's sequence-split workspace
+ * (ssm_scan_fwd_workspace_bytes), which a forward with SSM_FLAG_CHECKPOINTS
+ * keeps after the checkpoints. */
 size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
 
 /*

@@ -154,7 +154,7 @@ def _stream(stream, device):
 
 def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
                  out_dtype=torch.float32, return_final_state=True, y=None, hL=None,
-                 zoh=False, checkpoints=None, stream=None):
+                 zoh=False, checkpoints=None, workspace=None, stream=None):
     """Fused selective scan; returns (y, hL) (hL is None unless requested).
     x, dt, z, y (and Bm, Cm) may be strided views with a contiguous time
     index and one row stride shared among them, e.g. x and z as the two
@@ -162,7 +162,10 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B).
     checkpoints: a device buffer of ssm_scan_bwd_workspace_bytes(...) bytes
     that receives the backward pass's checkpoints (SSM_FLAG_CHECKPOINTS); pass
-    it to ssm_scan_bwd with checkpoints_in_workspace=True."""
+    it to ssm_scan_bwd with checkpoints_in_workspace=True.
+    workspace: device scratch of ssm_scan_fwd_workspace_bytes(...) bytes for
+    shapes whose sequence the library splits across workgroups (few batch
+    rows and channels, long L); allocated here when not given."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -189,6 +192,12 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     if checkpoints is not None:
         flags |= SSM_FLAG_CHECKPOINTS
         wp, wb = _ptr(checkpoints, "checkpoints"), checkpoints.numel() * checkpoints.element_size()
+    else:
+        need = lib().ssm_scan_fwd_workspace_bytes(batch, dim, L, N)
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        if workspace is not None:
+            wp, wb = _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
     st = lib().ssm_scan_fwd_strided(batch, dim, L, N, _dtype_code(ind), flags, *args,
                                     _dtype_code(y.dtype), yp, hp, wp, wb, ctypes.byref(layout),
                                     _stream(stream, x.device))

@@ -34,6 +34,8 @@
 //   4. bwd_sum_kernel: dBm, dCm = the sum of the 8 copies.
 // The layout and lane mapping follow the forward kernel: a workgroup owns one
 // batch row and 16 channels, each 16-lane DPP row one channel.
+#include <algorithm>
+
 #include "scan_common.hpp"
 #include "ssm_device.hpp"
 #include "ssm_launch.hpp"
@@ -679,7 +681,10 @@ size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
     const size_t nchunks = (size_t(seqlen) + kTB - 1) / kTB;
     const size_t checkpoints = size_t(batch) * size_t(dim) * nchunks * size_t(dstate);
     const size_t partials = size_t(kCopies) * 2 * size_t(batch) * size_t(dstate) * size_t(seqlen);
-    return (checkpoints + partials) * sizeof(float);
+    // A forward pass that writes the checkpoints keeps its sequence-split
+    // planes where the partial sums go later.
+    return checkpoints * sizeof(float) +
+           std::max(partials * sizeof(float), scan_fwd_split_bytes(batch, dim, seqlen, dstate));
 }
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream)

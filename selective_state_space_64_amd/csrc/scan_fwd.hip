@@ -30,6 +30,8 @@
 // Bm and Cm chunks (shared by every channel of the batch row) are staged once
 // per workgroup into LDS as fp32, double-buffered, one barrier per chunk.
 // No MFMA: the recurrence is not a dense contraction.
+#include <algorithm>
+
 #include "scan_common.hpp"
 #include "ssm_device.hpp"
 #include "ssm_launch.hpp"
@@ -55,6 +57,24 @@ constexpr int kWaves = SSM_SCAN_WAVES;      // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChannels = kThreads / kRow;  // channels per workgroup
 constexpr int kK = SSM_SCAN_K;              // consecutive timesteps per lane
+// Sequence split (see scan_fwd_split): used when the batch rows and channel
+// blocks give fewer than SSM_SPLIT_BELOW_WGS workgroups; aims at
+// SSM_SPLIT_TARGET_WGS workgroups with segments of at least
+// SSM_SPLIT_MIN_STEPS steps.  The aggregate pass costs about 0.8 of a
+// forward pass, so a split pays where the unsplit launch runs the chip at
+// under about half its rate: measured, fewer than ~300 workgroups (a 2x to 4x
+// gain at 48 to 128 workgroups, a loss at 320 with two segments).  Many
+// segments (~16 workgroups per CU) keep the last wave's tail short.
+#ifndef SSM_SPLIT_BELOW_WGS
+#define SSM_SPLIT_BELOW_WGS 256
+#endif
+#ifndef SSM_SPLIT_TARGET_WGS
+#define SSM_SPLIT_TARGET_WGS 4096
+#endif
+#ifndef SSM_SPLIT_MIN_STEPS
+#define SSM_SPLIT_MIN_STEPS 1024
+#endif
+constexpr int kMaxSegments = 1024;
 // Occupancy target (waves per SIMD): 4, which is also what the ~36 KB of LDS
 // per 4-wave workgroup allows (4 workgroups per CU).  More resident waves
 // were measured not to help: the state loop runs near the VALU issue limit.
@@ -77,6 +97,11 @@ struct ScanParams {
     float *hL;
     float *ck;  // optional: state entering every 64-step chunk, [batch][dim][nck][N]
     int nck;
+    // Sequence split: segment blockIdx.z covers steps [z seg_len, (z+1) seg_len).
+    // agg[s][b][d][0..N-1]: state at the end of segment s (from h0 for s = 0,
+    // from zero otherwise); agg[s][b][d][N]: sum of Delta over segment s.
+    int seg_len, nseg;
+    float *agg;
 };
 
 __device__ inline bool aligned16(const void *p)
@@ -84,10 +109,11 @@ __device__ inline bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-template <typename Tin, typename Tout, int N, int K, bool kZoh, bool kCkpt>
+template <typename Tin, typename Tout, int N, int K, bool kZoh, bool kCkpt, bool kAgg>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kernel(ScanParams p)
 {
     static_assert(K % 8 == 0, "K must be a multiple of 8");
+    static_assert(!(kCkpt && kAgg), "the aggregate pass writes no checkpoints");
     static_assert(N * kRow <= kThreads, "one staging slot per thread");
     constexpr int T = kRow * K;  // timesteps per chunk
     constexpr int Q = K / 4;     // float4 per lane per state
@@ -109,7 +135,9 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     const int cw = c & 3;                     // channel within the wave
     const int b = blockIdx.y;
     const int dim = p.dim;
-    const int L = p.seqlen;
+    const int seg = blockIdx.z;
+    const int lseg = seg * p.seg_len;              // first step of this segment
+    const int L = min(p.seqlen - lseg, p.seg_len);  // steps in this segment
     const int d = blockIdx.x * kChannels + c;
     const bool live = d < dim;
     const int dc = live ? d : dim - 1;
@@ -117,14 +145,14 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     // Wave-uniform row base (its first channel, clamped) and per-lane offset.
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int d0 = min(int(blockIdx.x) * kChannels + wave * 4, dim - 1);
-    const size_t row0 = size_t(d0) * size_t(p.row);
+    const size_t row0 = size_t(d0) * size_t(p.row) + size_t(lseg);
     const Tin *xw = static_cast<const Tin *>(p.x) + size_t(b) * size_t(p.x_b) + row0;
     const Tin *dtw = static_cast<const Tin *>(p.dt) + size_t(b) * size_t(p.dt_b) + row0;
     const Tin *zw = p.z ? static_cast<const Tin *>(p.z) + size_t(b) * size_t(p.z_b) + row0 : nullptr;
     Tout *yw = static_cast<Tout *>(p.y) + size_t(b) * size_t(p.y_b) + row0;
     const uint32_t lane_row = uint32_t(dc - d0) * uint32_t(p.row);  // elements
-    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * size_t(p.B_b);
-    const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * size_t(p.C_b);
+    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * size_t(p.B_b) + size_t(lseg);
+    const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * size_t(p.C_b) + size_t(lseg);
     // Wave-uniform: every row of every streamed tensor starts on a 16-byte
     // boundary, so all runs of a chunk that lies inside the sequence can use
     // unguarded 16-byte vector accesses.
@@ -141,10 +169,40 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         sAC[cc * 2 * NP + n] = (n < N) ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
     }
     if (j == 0) {
+        // State entering the segment: h0 for the first; otherwise the
+        // segments before it composed in order, h <- exp(A sum Delta) h + end
+        // state (each segment's map is affine in its entering state).
+        // With a split, the aggregate pass copies h0 into the last plane of
+        // agg and the main pass reads that copy, so that hL may overwrite h0
+        // while other segments of the same channel are still running.
+        float *hin = sAC + c * 2 * NP + NP;
+        float *h0copy = p.nseg > 1 ? p.agg + ((size_t(p.nseg - 1) * gridDim.y + b) * dim + dc) * NP
+                                   : nullptr;
+        if (seg == 0 || kAgg) {
+            const bool copy = !kAgg && h0copy;
 #pragma unroll
-        for (int n = 0; n < N; ++n)
-            sAC[c * 2 * NP + NP + n] = p.h0 ? p.h0[(size_t(b) * dim + dc) * N + n] : 0.0f;
-        sAC[c * 2 * NP + NP + N] = 0.0f;
+            for (int n = 0; n < N; ++n) {
+                const float v = (p.h0 && seg == 0)
+                                    ? (copy ? h0copy[n] : p.h0[(size_t(b) * dim + dc) * N + n])
+                                    : 0.0f;
+                hin[n] = v;
+                if (kAgg && seg == 0 && p.h0 && live) h0copy[n] = v;
+            }
+        } else {
+            float h[N];
+#pragma unroll
+            for (int n = 0; n < N; ++n) h[n] = 0.0f;
+            for (int s = 0; s < seg; ++s) {
+                const float *ag = p.agg + ((size_t(s) * gridDim.y + b) * dim + dc) * NP;
+                const float sd = ag[N];
+#pragma unroll
+                for (int n = 0; n < N; ++n)
+                    h[n] = __builtin_fmaf(exp2_hw(p.A[size_t(dc) * N + n] * kLog2e * sd), h[n], ag[n]);
+            }
+#pragma unroll
+            for (int n = 0; n < N; ++n) hin[n] = h[n];
+        }
+        hin[N] = 0.0f;
     }
 
     // Staging slot of this thread: state sn, lane block sj (threads < N*16).
@@ -197,14 +255,15 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     const int nchunks = (L + T - 1) / T;
     if (stager) {
         stage_load(Bb, 0, stB);
-        stage_load(Cb, 0, stC);
+        if constexpr (!kAgg) stage_load(Cb, 0, stC);
         stage_store(sB[0], stB);
-        stage_store(sC[0], stC);
+        if constexpr (!kAgg) stage_store(sC[0], stC);
     }
     xd_load(0);
     lds_barrier();
 
     float *aptr = sAC + c * 2 * NP;  // A' at aptr[n], carry at aptr[NP + n]
+    [[maybe_unused]] float dtot = 0.0f;  // this lane's Delta sum (aggregate pass)
 
     for (int ch = 0; ch < nchunks; ++ch) {
         const int buf = ch & 1;
@@ -262,8 +321,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         // One state: local fold, row scan, carry update and replay.
         auto state_step = [&](int n) {
             float cv[K];
-            load_b(cp, cv);
-            cp += Q * kRow;
+            if constexpr (!kAgg) {
+                load_b(cp, cv);
+                cp += Q * kRow;
+            }
             float dA[K], bb[K];
             if constexpr (kZoh) {
                 // exact zero-order hold: B-bar x = phi(Delta A) Delta B x
@@ -294,17 +355,20 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
                 // 64-step half of the chunk (the carry, and lane 7's end)
                 static_assert(kRow * K == 128, "two 64-step checkpoints per chunk");
                 const int half = j == kRow / 2 - 1 ? 1 : 0;
-                if (live && (j == 0 || half) && 2 * ch + half < p.nck)
-                    p.ck[((size_t(b) * dim + d) * p.nck + 2 * ch + half) * N + n] = half ? hend : cin;
+                const int ck = 2 * (ch + lseg / T) + half;  // global 64-step chunk
+                if (live && (j == 0 || half) && ck < p.nck)
+                    p.ck[((size_t(b) * dim + d) * p.nck + ck) * N + n] = half ? hend : cin;
             }
             bp += Q * kRow;
             load_b(bp, bv);          // next state's B (one past the end on the last state)
             ap = aptr[n + 1];
             carry = aptr[NP + n + 1];
+            if constexpr (!kAgg) {
 #pragma unroll
-            for (int i = 0; i < K; ++i) {
-                h = __builtin_fmaf(dA[i], h, bb[i]);
-                yv[i] = __builtin_fmaf(cv[i], h, yv[i]);
+                for (int i = 0; i < K; ++i) {
+                    h = __builtin_fmaf(dA[i], h, bb[i]);
+                    yv[i] = __builtin_fmaf(cv[i], h, yv[i]);
+                }
             }
         };
 
@@ -316,17 +380,17 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             constexpr int N1 = (N + 2) / 3, N2 = N - (N + 2) / 3;
             if (more && stager) {
                 stage_load(Bb, ch + 1, stB);
-                stage_load(Cb, ch + 1, stC);
+                if constexpr (!kAgg) stage_load(Cb, ch + 1, stC);
             }
 #pragma unroll 1
             for (int n = 0; n < N1; ++n) state_step(n);
             if (more && stager) {
                 stage_store(sB[buf ^ 1], stB);
-                stage_store(sC[buf ^ 1], stC);
+                if constexpr (!kAgg) stage_store(sC[buf ^ 1], stC);
             }
 #pragma unroll 1
             for (int n = N1; n < N2; ++n) state_step(n);
-            if (zw) z_load(ch, yoff);
+            if (!kAgg && zw) z_load(ch, yoff);
             if (more) xd_load(ch + 1);
 #pragma unroll 1
             for (int n = N2; n < N; ++n) state_step(n);
@@ -334,23 +398,24 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             // few states: everything is fetched up front
             if (more && stager) {
                 stage_load(Bb, ch + 1, stB);
-                stage_load(Cb, ch + 1, stC);
+                if constexpr (!kAgg) stage_load(Cb, ch + 1, stC);
             }
-            if (zw) z_load(ch, yoff);
+            if (!kAgg && zw) z_load(ch, yoff);
             if (more) xd_load(ch + 1);
 #pragma unroll 1
             for (int n = 0; n < N; ++n) state_step(n);
             if (more && stager) {
                 stage_store(sB[buf ^ 1], stB);
-                stage_store(sC[buf ^ 1], stC);
+                if constexpr (!kAgg) stage_store(sC[buf ^ 1], stC);
             }
         }
 
-        if (zw) {
+        if constexpr (kAgg) dtot += sumd;
+        if (!kAgg && zw) {
 #pragma unroll
             for (int i = 0; i < K; ++i) yv[i] *= silu(decode_raw_at<Tin, K>(rz, i));
         }
-        if (live) {
+        if (!kAgg && live) {
             Tout *yr = at(yw, uint32_t((lane_row + uint32_t(l0)) * sizeof(Tout)));
             if (full)
                 store_y<Tout, K>(yr, true, K, yv);
@@ -360,7 +425,17 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         lds_barrier();
     }
 
-    if (p.hL && live && j == 0) {
+    if constexpr (kAgg) {
+        // the segment's Delta sum over the row's 16 lanes
+#pragma unroll
+        for (int m = 1; m < kRow; m <<= 1) dtot += __shfl_xor(dtot, m, kRow);
+        if (live && j == 0) {
+            float *ag = p.agg + ((size_t(seg) * gridDim.y + b) * dim + d) * NP;
+#pragma unroll
+            for (int n = 0; n < N; ++n) ag[n] = aptr[NP + n];
+            ag[N] = dtot;
+        }
+    } else if (p.hL && live && j == 0 && seg == int(gridDim.z) - 1) {
 #pragma unroll
         for (int n = 0; n < N; ++n) p.hL[(size_t(b) * dim + d) * N + n] = aptr[NP + n];
     }
@@ -370,19 +445,29 @@ template <typename Tin, typename Tout, int N, bool kZoh>
 hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
 {
     constexpr int K = kK;
+    const ScanSplit sp = scan_fwd_split(a.batch, a.dim, a.seqlen);
     ScanParams p{a.dim, a.seqlen, a.row, a.x_b, a.dt_b, a.z_b, a.y_b, a.bc_row, a.B_b, a.C_b,
                  a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
-                 a.Dskip, a.z, a.h0, a.y, a.hL, a.ck, (a.seqlen + 63) / 64};
-    dim3 grid((a.dim + kChannels - 1) / kChannels, a.batch);
+                 a.Dskip, a.z, a.h0, a.y, a.hL, a.ck, (a.seqlen + 63) / 64,
+                 sp.seg_len, sp.nseg, a.agg};
+    const unsigned gx = (a.dim + kChannels - 1) / kChannels;
+    if (sp.nseg > 1) {
+        // every segment but the last: its end state and Delta sum
+        hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, true>),
+                           dim3(gx, a.batch, sp.nseg - 1), dim3(kThreads), 0, stream, p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid(gx, a.batch, sp.nseg);
     if constexpr (!kZoh) {
         if (a.ck) {
-            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true>), grid, dim3(kThreads),
-                               0, stream, p);
+            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true, false>), grid,
+                               dim3(kThreads), 0, stream, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false>), grid, dim3(kThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, false>), grid, dim3(kThreads),
+                       0, stream, p);
     return hipGetLastError();
 }
 
@@ -406,6 +491,30 @@ hipError_t launch_mode(const ScanArgs &a, hipStream_t stream)
 }
 
 }  // namespace
+
+ScanSplit scan_fwd_split(int batch, int dim, int seqlen)
+{
+    constexpr int T = kRow * kK;
+    const long long wgs = (long long)batch * ((dim + kChannels - 1) / kChannels);
+    ScanSplit sp{1, seqlen};
+    if (wgs >= SSM_SPLIT_BELOW_WGS) return sp;
+    long long nseg = SSM_SPLIT_TARGET_WGS / wgs;  // whole waves of workgroups
+    nseg = std::min<long long>(nseg, seqlen / SSM_SPLIT_MIN_STEPS);
+    nseg = std::min<long long>(nseg, kMaxSegments);
+    if (nseg < 2) return sp;
+    const long long per = (seqlen + nseg - 1) / nseg;
+    sp.seg_len = int((per + T - 1) / T * T);
+    sp.nseg = int((seqlen + sp.seg_len - 1) / sp.seg_len);
+    if (sp.nseg < 2) sp = {1, seqlen};
+    return sp;
+}
+
+size_t scan_fwd_split_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    const ScanSplit sp = scan_fwd_split(batch, dim, seqlen);
+    if (sp.nseg < 2) return 0;
+    return size_t(sp.nseg) * size_t(batch) * size_t(dim) * size_t(dstate + 1) * sizeof(float);
+}
 
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t stream)
 {

@@ -71,8 +71,10 @@ const char *ssm_status_string(ssm_status_t s)
 
 size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 {
-    (void)batch; (void)dim; (void)seqlen; (void)dstate;
-    return 0;
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen ||
+        !valid_dstate(dstate))
+        return 0;
+    return ssm::scan_fwd_split_bytes(batch, dim, seqlen, dstate);
 }
 
 ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
@@ -127,7 +129,12 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
     for (int i = 0; i < 2; ++i)
         if (!strided(lay.bc_batch[i], dstate, bc_row, bc_b[i], bc_span[i])) return SSM_ERR_BAD_SHAPE;
     const bool ckpt = (flags & SSM_FLAG_CHECKPOINTS) != 0;
-    const size_t ck_bytes = ckpt ? ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate) : 0;
+    const size_t split_bytes = ssm::scan_fwd_split_bytes(batch, dim, seqlen, dstate);
+    // Bytes of the workspace this call uses: the backward pass's workspace
+    // with checkpoints (the split's planes then follow the checkpoints),
+    // otherwise the split's planes, if any.
+    const size_t ws_bytes = ckpt ? ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate)
+                                 : split_bytes;
     if (ckpt && !workspace) return SSM_ERR_NULL_ARG;
 
     const size_t in = dsize(in_dtype);
@@ -137,11 +144,11 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
                           (const void *)h0, (const void *)hL})
         if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
     if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
-    if (ckpt && misaligned(workspace, 4)) return SSM_ERR_MISALIGNED;
+    if (ws_bytes && misaligned(workspace, 4)) return SSM_ERR_MISALIGNED;
 
     const size_t ybytes = seq_span[3] * dsize(out_dtype);
     const size_t hbytes = st_elems * sizeof(float);
-    if (ckpt && workspace_bytes < ck_bytes) return SSM_ERR_WORKSPACE;
+    if (workspace_bytes < ws_bytes || (ws_bytes && !workspace)) return SSM_ERR_WORKSPACE;
     struct In {
         const void *p;
         size_t bytes;
@@ -154,19 +161,19 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
         // hL may be exactly h0 (read before written per channel), nothing else
         if (hL && !(i.p == h0 && hL == h0) && overlaps(hL, hbytes, i.p, i.bytes))
             return SSM_ERR_ALIAS;
-        if (ckpt && overlaps(workspace, ck_bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        if (overlaps(workspace, ws_bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
     }
     if (overlaps(y, ybytes, hL, hbytes)) return SSM_ERR_ALIAS;
-    if (ckpt && (overlaps(workspace, ck_bytes, y, ybytes) || overlaps(workspace, ck_bytes, hL, hbytes)))
+    if (overlaps(workspace, ws_bytes, y, ybytes) || overlaps(workspace, ws_bytes, hL, hbytes))
         return SSM_ERR_ALIAS;
 
-    if (workspace_bytes < ssm_scan_fwd_workspace_bytes(batch, dim, seqlen, dstate))
-        return SSM_ERR_WORKSPACE;
-
+    float *ws = static_cast<float *>(workspace);
+    const size_t ck_floats = size_t(batch) * dim * ((size_t(seqlen) + 63) / 64) * dstate;
+    float *agg = split_bytes ? (ckpt ? ws + ck_floats : ws) : nullptr;
     ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
                     (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,
-                    ckpt ? static_cast<float *>(workspace) : nullptr,
-                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], bc_row, bc_b[0], bc_b[1]};
+                    ckpt ? ws : nullptr,
+                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], bc_row, bc_b[0], bc_b[1], agg};
     const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -21,7 +21,21 @@ struct ScanArgs {
     // Strides in elements (time stride is 1): rows of x, dt, z, y are `row`
     // apart, rows of Bm, Cm `bc_row` apart; batch entries `*_b` apart.
     long long row, x_b, dt_b, z_b, y_b, bc_row, B_b, C_b;
+    // Workspace of the sequence split (scan_fwd_split_bytes), or NULL when
+    // the shape is not split.
+    float *agg;
 };
+
+// Sequence split of the forward scan: segments of seg_len steps (a multiple
+// of the 128-step chunk) scanned by separate workgroups.  A function of the
+// shape only, so that the workspace size is known before the call.
+struct ScanSplit {
+    int nseg, seg_len;
+};
+ScanSplit scan_fwd_split(int batch, int dim, int seqlen);
+// Bytes of the split's workspace: one plane of (dstate + 1) floats per
+// (batch, channel) for every segment; 0 when the shape is not split.
+size_t scan_fwd_split_bytes(int batch, int dim, int seqlen, int dstate);
 
 struct UpdateArgs {
     int batch, dim, dstate;

@@ -288,6 +288,64 @@ def test_strided_validation_spans_and_defaults():
     assert _strided_call(bc, y=_FAKE["Bm"] + (1280 + 640) * 2) == 8
 
 
+def _split_bytes(batch, dim, L, N):
+    """The documented split rule, restated: split when batch * ceil(dim / 16)
+    < 256, into whole multiples of that many workgroups up to 4096, segments
+    >= 1024 steps and a multiple of 128, at most 1024 segments."""
+    wgs = batch * ((dim + 15) // 16)
+    if wgs >= 256:
+        return 0
+    nseg = min(4096 // wgs, L // 1024, 1024)
+    if nseg < 2:
+        return 0
+    seg = -(-(-(-L // nseg)) // 128) * 128
+    nseg = -(-L // seg)
+    return 0 if nseg < 2 else nseg * batch * dim * (N + 1) * 4
+
+
+@pytest.mark.parametrize("shape", [(4, 5120, 2048, 16), (8, 1536, 2048, 16), (1, 1536, 1 << 20, 16),
+                                   (1, 16, 2048, 16), (1, 16, 2047, 16), (2, 20, 5000, 8),
+                                   (1, 1, 1 << 20, 1), (256, 16, 4096, 4), (255, 16, 4096, 4),
+                                   (1, 8185, 4096, 16)])
+def test_fwd_workspace_bytes_follow_the_split_rule(shape):
+    assert ssm.lib().ssm_scan_fwd_workspace_bytes(*shape) == _split_bytes(*shape)
+
+
+def test_fwd_workspace_bytes_examples():
+    L = ssm.lib()
+    assert L.ssm_scan_fwd_workspace_bytes(4, 5120, 2048, 16) == 0      # 1280 workgroups
+    assert L.ssm_scan_fwd_workspace_bytes(1, 16, 2048, 16) == 2 * 16 * 17 * 4
+    # the long sequence: 96 workgroups -> 42 segments of 24 992 steps
+    assert L.ssm_scan_fwd_workspace_bytes(1, 1536, 1 << 20, 16) == 42 * 1536 * 17 * 4
+    assert L.ssm_scan_fwd_workspace_bytes(2, 2560, 2048, 16) == 0      # 320 workgroups
+    assert L.ssm_scan_fwd_workspace_bytes(0, 16, 4096, 16) == 0
+    assert L.ssm_scan_fwd_workspace_bytes(1, 16, 4096, 3) == 0
+    # the backward's workspace also covers the forward's split planes
+    for shape in [(1, 16, 4096, 16), (1, 4096, 1 << 14, 16), (1, 8, 1 << 20, 1)]:
+        bw = L.ssm_scan_bwd_workspace_bytes(*shape)
+        b, d, n_l, n = shape
+        ck = b * d * (-(-n_l // 64)) * n * 4
+        assert bw == ck + max(8 * 2 * b * n * n_l * 4, _split_bytes(*shape))
+
+
+@no_gpu
+def test_split_workspace_validation():
+    shape = dict(batch=1, dim=16, seqlen=4096, dstate=16)
+    need = _split_bytes(1, 16, 4096, 16)
+    assert need > 0
+    ws = 0x200000000
+    assert _fake_call(**shape) == 7                                  # no workspace
+    assert _fake_call(**shape, ws=ws, wsb=need - 4) == 7
+    assert _fake_call(**shape, ws=ws + 2, wsb=need) == 4
+    assert _fake_call(**shape, ws=_FAKE["dt"] + 16, wsb=need) == 5   # inside dt
+    assert _fake_call(**shape, ws=_FAKE["hL"] - need + 4, wsb=need) == 5
+    assert _fake_call(**shape, ws=ws, wsb=need) == 8
+    # with checkpoints the backward's workspace is what is checked
+    bw = ssm.lib().ssm_scan_bwd_workspace_bytes(1, 16, 4096, 16)
+    assert _fake_call(**shape, flags=2, ws=ws, wsb=bw - 4) == 7
+    assert _fake_call(**shape, flags=2, ws=ws, wsb=bw) == 8
+
+
 @no_gpu
 def test_state_update_validation():
     L = ssm.lib()
