@@ -71,6 +71,46 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           float *dBm, float *dCm, float *dA, float *dDskip, float *ddt_bias,
                           float *dh0, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Strided layouts for ssm_scan_bwd_strided, in the manner of
+ * ssm_scan_layout_t (ssm.h): strides in ELEMENTS of each tensor's own type,
+ * time contiguous.  In training, z comes from the same input projection as
+ * x, and its gradient dz goes back into that projection's gradient buffer,
+ * so both are usually halves of one [batch][2 dim][seqlen] buffer.
+ *   seq_row        distance between rows (channels) of x, dt, z, dy, dx,
+ *                  ddt and dz, shared by the seven; >= seqlen; 0 means seqlen
+ *   seq_batch[7]   distance between batch entries of x, dt, z, dy, dx, ddt,
+ *                  dz (in that order); each >= dim * seq_row; 0 means
+ *                  dim * seq_row
+ *   bc_row, bc_batch[2]  as in ssm_scan_layout_t, for Bm and Cm
+ * dBm, dCm and every other argument stay dense.  The limits and errors are
+ * those of ssm_scan_layout_t; overlap is judged on each tensor's address
+ * range from its first to its last element, so two outputs (dx and dz, say)
+ * may not be interleaved halves of one buffer, while dz alone may be written
+ * into half of one.
+ */
+typedef struct {
+    long long seq_row;
+    long long seq_batch[7];
+    long long bc_row;
+    long long bc_batch[2];
+} ssm_scan_bwd_layout_t;
+
+/*
+ * ssm_scan_bwd on strided views: the same arguments, flags and errors, with
+ * `layout` (host pointer, read during the call only; NULL means dense).
+ */
+ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
+                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, ssm_dtype_t grad_dtype,
+                                  const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                                  float *dBm, float *dCm, float *dA, float *dDskip,
+                                  float *ddt_bias, float *dh0, void *workspace,
+                                  size_t workspace_bytes, const ssm_scan_bwd_layout_t *layout,
+                                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

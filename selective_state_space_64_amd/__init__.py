@@ -36,12 +36,18 @@ STATUS = {
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
            "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_update",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd"]
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_strided"]
 
 
 class ScanLayout(ctypes.Structure):
     """ssm_scan_layout_t: strides in elements, 0 = dense default."""
     _fields_ = [("seq_row", ctypes.c_longlong), ("seq_batch", ctypes.c_longlong * 4),
+                ("bc_row", ctypes.c_longlong), ("bc_batch", ctypes.c_longlong * 2)]
+
+
+class BwdLayout(ctypes.Structure):
+    """ssm_scan_bwd_layout_t: strides in elements, 0 = dense default."""
+    _fields_ = [("seq_row", ctypes.c_longlong), ("seq_batch", ctypes.c_longlong * 7),
                 ("bc_row", ctypes.c_longlong), ("bc_batch", ctypes.c_longlong * 2)]
 
 
@@ -80,6 +86,9 @@ def lib():
         L.ssm_scan_bwd_workspace_bytes.argtypes = [i, i, i, i]
         L.ssm_scan_bwd.restype = i
         L.ssm_scan_bwd.argtypes = [i, i, i, i, i, u] + [vp] * 9 + [i] + [vp] * 12 + [sz, vp]
+        L.ssm_scan_bwd_strided.restype = i
+        L.ssm_scan_bwd_strided.argtypes = ([i, i, i, i, i, u] + [vp] * 9 + [i] + [vp] * 12 +
+                                           [sz, ctypes.POINTER(BwdLayout), vp])
         L.ssm_conv1d_fwd.restype = i
         L.ssm_conv1d_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 4 + [i, vp, vp, vp]
         L.ssm_conv1d_update.restype = i
@@ -231,21 +240,27 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
 
 def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=None, dhL=None,
                  grad_dtype=torch.float32, workspace=None, checkpoints_in_workspace=False,
-                 stream=None):
+                 dx=None, ddt=None, dz=None, stream=None):
     """Gradients of sum(dy * y) + sum(dhL * hL) through ssm_scan_fwd (Delta*B
     form).  Returns a dict: dx, ddt, dz (None without z) in grad_dtype; dBm,
     dCm, dA, dDskip, ddt_bias, dh0 in fp32 (dDskip / ddt_bias / dh0 are
     computed for every call).  checkpoints_in_workspace=True: `workspace`
-    holds the checkpoints a forward call wrote (SSM_FLAG_CHECKPOINTS)."""
+    holds the checkpoints a forward call wrote (SSM_FLAG_CHECKPOINTS).
+    x, dt, z, dy and the outputs dx, ddt, dz (given here, else allocated
+    dense) may be strided views with a contiguous time index and one shared
+    row stride, e.g. z and dz as halves of the projection's buffers; Bm and
+    Cm likewise with their own row stride."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
     N = A.shape[-1]
     ind, dev, f32 = x.dtype, x.device, torch.float32
+    shape = (batch, dim, L)
     g = {
-        "dx": torch.empty((batch, dim, L), dtype=grad_dtype, device=dev),
-        "ddt": torch.empty((batch, dim, L), dtype=grad_dtype, device=dev),
-        "dz": torch.empty((batch, dim, L), dtype=grad_dtype, device=dev) if z is not None else None,
+        "dx": dx if dx is not None else torch.empty(shape, dtype=grad_dtype, device=dev),
+        "ddt": ddt if ddt is not None else torch.empty(shape, dtype=grad_dtype, device=dev),
+        "dz": (dz if dz is not None else torch.empty(shape, dtype=grad_dtype, device=dev))
+              if z is not None else None,
         "dBm": torch.empty((batch, N, L), dtype=f32, device=dev),
         "dCm": torch.empty((batch, N, L), dtype=f32, device=dev),
         "dA": torch.empty((dim, N), dtype=f32, device=dev),
@@ -258,23 +273,28 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
         if checkpoints_in_workspace:
             raise ValueError("checkpoints_in_workspace needs the forward's workspace")
         workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+    names = ("x", "dt", "z", "dy", "dx", "ddt", "dz")
+    (xp, dtp, zp, dyp, dxp, ddtp, dzp), row, seq_b = _rows(
+        (x, dt, z, dy, g["dx"], g["ddt"], g["dz"]), names, shape,
+        {"x": ind, "dt": ind, "z": ind, "dy": grad_dtype, "dx": grad_dtype, "ddt": grad_dtype,
+         "dz": grad_dtype})
+    (Bp, Cp), bc_row, bc_b = _rows((Bm, Cm), ("Bm", "Cm"), (batch, N, L), ind)
+    layout = BwdLayout(row, (ctypes.c_longlong * 7)(*seq_b), bc_row,
+                       (ctypes.c_longlong * 2)(*bc_b))
     args = [
-        _ptr(x, "x", (batch, dim, L), ind), _ptr(dt, "dt", (batch, dim, L), ind),
-        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
-        _ptr(Bm, "Bm", (batch, N, L), ind), _ptr(Cm, "Cm", (batch, N, L), ind),
-        _ptr(Dskip, "Dskip", (dim,), f32), _ptr(z, "z", (batch, dim, L), ind),
-        _ptr(h0, "h0", (batch, dim, N), f32),
+        xp, dtp, _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
+        Bp, Cp, _ptr(Dskip, "Dskip", (dim,), f32), zp, _ptr(h0, "h0", (batch, dim, N), f32),
     ]
     gargs = [
-        _ptr(dy, "dy", (batch, dim, L), grad_dtype), _ptr(dhL, "dhL", (batch, dim, N), f32),
-        _ptr(g["dx"], "dx"), _ptr(g["ddt"], "ddt"), _ptr(g["dz"], "dz"), _ptr(g["dBm"], "dBm"),
+        dyp, _ptr(dhL, "dhL", (batch, dim, N), f32), dxp, ddtp, dzp, _ptr(g["dBm"], "dBm"),
         _ptr(g["dCm"], "dCm"), _ptr(g["dA"], "dA"), _ptr(g["dDskip"], "dDskip"),
         _ptr(g["ddt_bias"], "ddt_bias"), _ptr(g["dh0"], "dh0"),
     ]
     flags = SSM_FLAG_CHECKPOINTS if checkpoints_in_workspace else 0
-    st = lib().ssm_scan_bwd(batch, dim, L, N, _dtype_code(ind), flags, *args, _dtype_code(grad_dtype),
-                            *gargs, _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-                            _stream(stream, dev))
+    st = lib().ssm_scan_bwd_strided(batch, dim, L, N, _dtype_code(ind), flags, *args,
+                                    _dtype_code(grad_dtype), *gargs, _ptr(workspace, "workspace"),
+                                    workspace.numel() * workspace.element_size(),
+                                    ctypes.byref(layout), _stream(stream, dev))
     _check(st)
     return g
 

@@ -54,6 +54,9 @@ constexpr int kCopies = 8;                 // partial dBm / dCm copies (one per 
 
 struct BwdParams {
     int batch, dim, seqlen, nchunks;
+    // Layout in elements (time contiguous): rows of x, dt, z, dy, dx, ddt, dz
+    // are `row` apart, rows of Bm, Cm `bc_row` apart, batch entries `*_b`.
+    long long row, x_b, dt_b, z_b, dy_b, dx_b, ddt_b, dz_b, bc_row, B_b, C_b;
     const void *x, *dt;
     const float *dt_bias, *A;
     const void *Bm, *Cm;
@@ -246,12 +249,13 @@ __device__ inline void row_total_last_x2(float &v0, float &v1)
 // Bm or Cm of one chunk into LDS as fp32, layout [n][q][lane] of float4 (the
 // forward kernel's layout): thread (sn, sj) stages the K steps of lane sj.
 template <typename Tin, int K>
-__device__ inline void stage_chunk(float4 *dst, const Tin *src, int L, int chunk, int sn, int sj)
+__device__ inline void stage_chunk(float4 *dst, const Tin *src, int L, long long srow, int chunk,
+                                   int sn, int sj)
 {
     constexpr int T = kRowB * K, Q = K / 4;
     const int l = chunk * T + sj * K;
     const int cnt = max(0, min(K, L - l));
-    const Tin *q = src + size_t(sn) * size_t(L) + l;
+    const Tin *q = src + size_t(sn) * size_t(srow) + l;
     float v[K];
     load4<Tin>(q, cnt, v);
 #pragma unroll
@@ -317,10 +321,10 @@ __global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
     const int d = int(blockIdx.x) * kChanB + c;
     const bool live = d < dim;
     const int dc = live ? d : dim - 1;
-    const size_t rowo = (size_t(b) * dim + dc) * size_t(L);
-    const Tin *xr = static_cast<const Tin *>(p.x) + rowo;
-    const Tin *dtr = static_cast<const Tin *>(p.dt) + rowo;
-    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * N * L;
+    const size_t rowo = size_t(dc) * size_t(p.row);
+    const Tin *xr = static_cast<const Tin *>(p.x) + size_t(b) * size_t(p.x_b) + rowo;
+    const Tin *dtr = static_cast<const Tin *>(p.dt) + size_t(b) * size_t(p.dt_b) + rowo;
+    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * size_t(p.B_b);
 
     for (int s = tid; s < kChanB * NP; s += kThreadsB) {
         const int cc = s / NP, n = s % NP;
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
         if (stager) {
             const int l = ch * T + sj * K;
             const int cnt = max(0, min(K, L - l));
-            const Tin *q = Bb + size_t(sn) * size_t(L) + l;
+            const Tin *q = Bb + size_t(sn) * size_t(p.bc_row) + l;
             float v[K];
             load_run<Tin, K>(q, cnt == K && (reinterpret_cast<uintptr_t>(q) & 15u) == 0, cnt, v);
 #pragma unroll
@@ -394,9 +398,9 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
     constexpr int K = kKB, T = kTB, Q = K / 4, NP = N + 1;
     __shared__ float4 sB[N * Q * kRowB];
     __shared__ float4 sC[N * Q * kRowB];
-    // Per-channel dBm / dCm terms of the states in flight:
-    // [state of the pair][dBm, dCm][channel][step].
-    __shared__ float4 sP[2][2][kChanB][T / 4];
+    // Per-channel dBm / dCm terms of the states in flight, double-buffered
+    // by pair parity: [buffer][state of the pair][dBm, dCm][channel][step].
+    __shared__ float4 sP[2][2][2][kChanB][T / 4];
     __shared__ float sAP[kChanB * NP];  // A * log2(e)
     __shared__ float sH[kChanB * NP];   // forward state entering the chunk
     __shared__ float sMu[kChanB * NP];  // adjoint entering the chunk from its right
@@ -407,16 +411,17 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
     const int d = int(blockIdx.x) * kChanB + c;
     const bool live = d < dim;
     const int dc = live ? d : dim - 1;
-    const size_t rowo = (size_t(b) * dim + dc) * size_t(L);
-    const Tin *xr = static_cast<const Tin *>(p.x) + rowo;
-    const Tin *dtr = static_cast<const Tin *>(p.dt) + rowo;
-    const Tin *zr = p.z ? static_cast<const Tin *>(p.z) + rowo : nullptr;
-    const Tg *dyr = static_cast<const Tg *>(p.dy) + rowo;
-    Tg *dxr = static_cast<Tg *>(p.dx) + rowo;
-    Tg *ddtr = static_cast<Tg *>(p.ddt) + rowo;
-    Tg *dzr = p.dz ? static_cast<Tg *>(p.dz) + rowo : nullptr;
-    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * N * L;
-    const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * N * L;
+    const size_t rowo = size_t(dc) * size_t(p.row);
+    const size_t bb = size_t(b);
+    const Tin *xr = static_cast<const Tin *>(p.x) + bb * size_t(p.x_b) + rowo;
+    const Tin *dtr = static_cast<const Tin *>(p.dt) + bb * size_t(p.dt_b) + rowo;
+    const Tin *zr = p.z ? static_cast<const Tin *>(p.z) + bb * size_t(p.z_b) + rowo : nullptr;
+    const Tg *dyr = static_cast<const Tg *>(p.dy) + bb * size_t(p.dy_b) + rowo;
+    Tg *dxr = static_cast<Tg *>(p.dx) + bb * size_t(p.dx_b) + rowo;
+    Tg *ddtr = static_cast<Tg *>(p.ddt) + bb * size_t(p.ddt_b) + rowo;
+    Tg *dzr = p.dz ? static_cast<Tg *>(p.dz) + bb * size_t(p.dz_b) + rowo : nullptr;
+    const Tin *Bb = static_cast<const Tin *>(p.Bm) + bb * size_t(p.B_b);
+    const Tin *Cb = static_cast<const Tin *>(p.Cm) + bb * size_t(p.C_b);
 
     for (int s = tid; s < kChanB * NP; s += kThreadsB) {
         const int cc = s / NP, n = s % NP;
@@ -442,8 +447,8 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
     for (int ch = p.nchunks - 1; ch >= 0; --ch) {
         lds_barrier();
         if (stager) {
-            stage_chunk<Tin, K>(sB, Bb, L, ch, sn, sj);
-            stage_chunk<Tin, K>(sC, Cb, L, ch, sn, sj);
+            stage_chunk<Tin, K>(sB, Bb, L, p.bc_row, ch, sn, sj);
+            stage_chunk<Tin, K>(sC, Cb, L, p.bc_row, ch, sn, sj);
         }
         for (int s = tid; s < kChanB * N; s += kThreadsB) {
             const int cc = s / N, n = s % N;
@@ -495,6 +500,7 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
         constexpr int G = N >= 2 ? 2 : 1;  // states in flight per iteration
 #pragma unroll 1
         for (int n = 0; n < N; n += G) {
+            const int pb = (n / G) & 1;  // sP buffer of this pair
             float a1[G], An[G], bv[G][K], cv[G][K], da[G][K], hh[G][K], ptot[G], hl[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -572,8 +578,8 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
                     gcv[i] = ds[i] * hh[g][i];
                     lam *= da[g][i];
                 }
-                sP[g][0][c][j] = make_float4(gbv[0], gbv[1], gbv[2], gbv[3]);
-                sP[g][1][c][j] = make_float4(gcv[0], gcv[1], gcv[2], gcv[3]);
+                sP[pb][g][0][c][j] = make_float4(gbv[0], gbv[1], gbv[2], gbv[3]);
+                sP[pb][g][1][c][j] = make_float4(gcv[0], gcv[1], gcv[2], gcv[3]);
             }
             if constexpr (G == 2) {
                 row_total_last_x2(dap[0], dap[1]);
@@ -588,14 +594,17 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
             // dBm[b, n, t] and dCm[b, n, t] sum over channels: lanes 2i, 2i + 1
             // add 8 channels each for one (state, quantity, step), combine
             // through DPP, and the even lane issues the atomic add into this
-            // workgroup's copy.
+            // workgroup's copy.  One barrier per pair: the terms alternate
+            // between two buffers, and a thread writes a buffer again only
+            // after the next pair's barrier, which every thread reaches after
+            // finishing its sums over that buffer.
             lds_barrier();
 #pragma unroll
             for (int rep = 0; rep < G; ++rep) {
                 const int trip = rep * (kThreadsB / 2) + (tid >> 1);  // (state, quantity, step)
                 const int half = tid & 1;
                 const int g = trip / (2 * T), qq = (trip / T) & 1, t = trip % T;
-                const float *col = reinterpret_cast<const float *>(&sP[g][qq][half * (kChanB / 2)][0]) + t;
+                const float *col = reinterpret_cast<const float *>(&sP[pb][g][qq][half * (kChanB / 2)][0]) + t;
                 float acc = 0.0f;
 #pragma unroll
                 for (int cc = 0; cc < kChanB / 2; ++cc) acc += col[cc * T];
@@ -604,7 +613,6 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
                 if (half == 0 && tt < L)
                     atomicAdd(&part[size_t(qq) * bnl + size_t(n + g) * L + tt], acc);
             }
-            lds_barrier();
         }
 
         // per-step gradients of this chunk
@@ -646,7 +654,9 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
     const int nchunks = (a.seqlen + kTB - 1) / kTB;
     float *ck = static_cast<float *>(a.workspace);
     float *part = ck + size_t(a.batch) * a.dim * nchunks * N;
-    BwdParams p{a.batch, a.dim, a.seqlen, nchunks, a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
+    BwdParams p{a.batch, a.dim, a.seqlen, nchunks,
+                a.row, a.x_b, a.dt_b, a.z_b, a.dy_b, a.dx_b, a.ddt_b, a.dz_b, a.bc_row, a.B_b, a.C_b,
+                a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
                 a.Dskip, a.z, a.h0, a.dy, a.dhL, a.dx, a.ddt, a.dz, a.dBm, a.dCm, a.dA,
                 a.dDskip, a.ddt_bias, a.dh0, ck, part};
     const size_t nbc = size_t(a.batch) * N * a.seqlen;

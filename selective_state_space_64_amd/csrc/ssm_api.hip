@@ -46,6 +46,29 @@ size_t mul3(long long a, long long b, long long c)
     return size_t(r);
 }
 
+// Row stride of strided [batch][rows][seqlen] tensors: 0 means seqlen;
+// false when below seqlen or beyond the kernels' 32-bit in-wave offsets.
+bool row_stride(long long given, int seqlen, long long &rs)
+{
+    rs = given ? given : seqlen;
+    return rs >= seqlen && rs <= ssm::kMaxSeqlen;
+}
+
+// Batch stride (0 means rows * rs) and span in elements, from the first to
+// one past the last element, of a [batch][rows][seqlen] tensor whose rows
+// are rs apart; false when the stride is negative or below rows * rs, or the
+// span reaches 2^56 elements.
+bool batch_span(long long given, int batch, int rows, long long rs, int seqlen, long long &sb,
+                size_t &sp)
+{
+    sb = given ? given : rows * rs;
+    if (sb < rows * rs) return false;
+    const __int128 n = (__int128)(batch - 1) * sb + (__int128)(rows - 1) * rs + seqlen;
+    if (n >= ((__int128)1 << 56)) return false;
+    sp = size_t(n);
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,24 +133,16 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
     const ssm_scan_layout_t dense{};
     const ssm_scan_layout_t &lay = layout ? *layout : dense;
     // Strides with defaults filled in, and each tensor's span in elements.
-    const long long row = lay.seq_row ? lay.seq_row : seqlen;
-    const long long bc_row = lay.bc_row ? lay.bc_row : seqlen;
-    if (row < seqlen || row > ssm::kMaxSeqlen || bc_row < seqlen || bc_row > ssm::kMaxSeqlen)
-        return SSM_ERR_BAD_SHAPE;
-    long long seq_b[4], bc_b[2];
+    long long row, bc_row, seq_b[4], bc_b[2];
     size_t seq_span[4], bc_span[2];
-    auto strided = [&](long long given, int rows, long long rs, long long &sb, size_t &sp) {
-        sb = given ? given : rows * rs;
-        if (sb < rows * rs) return false;
-        const __int128 n = (__int128)(batch - 1) * sb + (__int128)(rows - 1) * rs + seqlen;
-        if (n >= ((__int128)1 << 56)) return false;
-        sp = size_t(n);
-        return true;
-    };
+    if (!row_stride(lay.seq_row, seqlen, row) || !row_stride(lay.bc_row, seqlen, bc_row))
+        return SSM_ERR_BAD_SHAPE;
     for (int i = 0; i < 4; ++i)
-        if (!strided(lay.seq_batch[i], dim, row, seq_b[i], seq_span[i])) return SSM_ERR_BAD_SHAPE;
+        if (!batch_span(lay.seq_batch[i], batch, dim, row, seqlen, seq_b[i], seq_span[i]))
+            return SSM_ERR_BAD_SHAPE;
     for (int i = 0; i < 2; ++i)
-        if (!strided(lay.bc_batch[i], dstate, bc_row, bc_b[i], bc_span[i])) return SSM_ERR_BAD_SHAPE;
+        if (!batch_span(lay.bc_batch[i], batch, dstate, bc_row, seqlen, bc_b[i], bc_span[i]))
+            return SSM_ERR_BAD_SHAPE;
     const bool ckpt = (flags & SSM_FLAG_CHECKPOINTS) != 0;
     const size_t split_bytes = ssm::scan_fwd_split_bytes(batch, dim, seqlen, dstate);
     // Bytes of the workspace this call uses: the backward pass's workspace
@@ -322,6 +337,22 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           float *dBm, float *dCm, float *dA, float *dDskip, float *ddt_bias,
                           float *dh0, void *workspace, size_t workspace_bytes, void *stream)
 {
+    return ssm_scan_bwd_strided(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A, Bm,
+                                Cm, Dskip, z, h0, grad_dtype, dy, dhL, dx, ddt, dz, dBm, dCm, dA,
+                                dDskip, ddt_bias, dh0, workspace, workspace_bytes, nullptr, stream);
+}
+
+ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
+                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, ssm_dtype_t grad_dtype,
+                                  const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                                  float *dBm, float *dCm, float *dA, float *dDskip,
+                                  float *ddt_bias, float *dh0, void *workspace,
+                                  size_t workspace_bytes, const ssm_scan_bwd_layout_t *layout,
+                                  void *stream)
+{
     if (!x || !dt || !A || !Bm || !Cm || !dy || !dx || !ddt || !dBm || !dCm || !dA)
         return SSM_ERR_NULL_ARG;
     if (z && !dz) return SSM_ERR_NULL_ARG;
@@ -331,10 +362,22 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
         return SSM_ERR_BAD_SHAPE;
     if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_CHECKPOINTS) != 0) return SSM_ERR_UNSUPPORTED;
 
-    const size_t seq_elems = mul3(batch, dim, seqlen);
     const size_t bc_elems = mul3(batch, dstate, seqlen);
     const size_t st_elems = mul3(batch, dim, dstate);
-    if (!seq_elems || !bc_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+    if (!mul3(batch, dim, seqlen) || !bc_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+    const ssm_scan_bwd_layout_t dense{};
+    const ssm_scan_bwd_layout_t &lay = layout ? *layout : dense;
+    // x, dt, z, dy, dx, ddt, dz: strides and spans in elements; Bm, Cm likewise
+    long long row, bc_row, seq_b[7], bc_b[2];
+    size_t sp[7], bc_span[2];
+    if (!row_stride(lay.seq_row, seqlen, row) || !row_stride(lay.bc_row, seqlen, bc_row))
+        return SSM_ERR_BAD_SHAPE;
+    for (int i = 0; i < 7; ++i)
+        if (!batch_span(lay.seq_batch[i], batch, dim, row, seqlen, seq_b[i], sp[i]))
+            return SSM_ERR_BAD_SHAPE;
+    for (int i = 0; i < 2; ++i)
+        if (!batch_span(lay.bc_batch[i], batch, dstate, bc_row, seqlen, bc_b[i], bc_span[i]))
+            return SSM_ERR_BAD_SHAPE;
     const size_t ws_need = ssm_scan_bwd_workspace_bytes(batch, dim, seqlen, dstate);
     if (!workspace && ws_need) return SSM_ERR_NULL_ARG;
 
@@ -356,12 +399,12 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
         size_t bytes;
     };
     const size_t fb = sizeof(float);
-    const Buf inputs[] = {{x, seq_elems * in},  {dt, seq_elems * in},  {dt_bias, dim * fb},
+    const Buf inputs[] = {{x, sp[0] * in},  {dt, sp[1] * in},  {dt_bias, dim * fb},
                           {A, size_t(dim) * dstate * fb},
-                          {Bm, bc_elems * in},  {Cm, bc_elems * in},  {Dskip, dim * fb},
-                          {z, seq_elems * in},  {h0, st_elems * fb},  {dy, seq_elems * gs},
+                          {Bm, bc_span[0] * in},  {Cm, bc_span[1] * in},  {Dskip, dim * fb},
+                          {z, sp[2] * in},  {h0, st_elems * fb},  {dy, sp[3] * gs},
                           {dhL, st_elems * fb}};
-    const Buf outputs[] = {{dx, seq_elems * gs},     {ddt, seq_elems * gs},   {dz, seq_elems * gs},
+    const Buf outputs[] = {{dx, sp[4] * gs},         {ddt, sp[5] * gs},       {dz, sp[6] * gs},
                            {dBm, bc_elems * fb},     {dCm, bc_elems * fb},
                            {dA, size_t(dim) * dstate * fb},
                            {dDskip, dim * fb},       {ddt_bias, dim * fb},    {dh0, st_elems * fb},
@@ -376,7 +419,9 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
     }
     ssm::BwdArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, grad_dtype == SSM_BF16,
                    x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy, dhL, dx, ddt, dz, dBm, dCm, dA,
-                   dDskip, ddt_bias, dh0, workspace, (flags & SSM_FLAG_CHECKPOINTS) != 0};
+                   dDskip, ddt_bias, dh0, workspace, (flags & SSM_FLAG_CHECKPOINTS) != 0,
+                   row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], seq_b[4], seq_b[5], seq_b[6],
+                   bc_row, bc_b[0], bc_b[1]};
     const hipError_t e = ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -82,6 +82,9 @@ struct BwdArgs {
     float *dBm, *dCm, *dA, *dDskip, *ddt_bias, *dh0;
     void *workspace;
     int ckpt_given;  // the workspace already holds the forward's checkpoints
+    // Strides in elements (time stride 1): rows of x, dt, z, dy, dx, ddt, dz
+    // `row` apart, rows of Bm, Cm `bc_row` apart, batch entries `*_b` apart.
+    long long row, x_b, dt_b, z_b, dy_b, dx_b, ddt_b, dz_b, bc_row, B_b, C_b;
 };
 
 // Device workspace of the backward pass: the state entering every chunk.

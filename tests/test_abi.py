@@ -59,6 +59,8 @@ def test_binding_argtypes_match_prototypes():
         for decl, at in zip(params, argtypes):
             if "ssm_scan_layout_t" in decl:
                 assert at == ctypes.POINTER(ssm.ScanLayout), (name, decl, at)
+            elif "ssm_scan_bwd_layout_t" in decl:
+                assert at == ctypes.POINTER(ssm.BwdLayout), (name, decl, at)
             elif "*" in decl:
                 assert at in (ctypes.c_void_p, ctypes.c_char_p), (name, decl, at)
             elif decl.startswith("size_t"):
@@ -344,6 +346,54 @@ def test_split_workspace_validation():
     bw = ssm.lib().ssm_scan_bwd_workspace_bytes(1, 16, 4096, 16)
     assert _fake_call(**shape, flags=2, ws=ws, wsb=bw - 4) == 7
     assert _fake_call(**shape, flags=2, ws=ws, wsb=bw) == 8
+
+
+_BWD_FAKE = {k: 0x10000000 * (i + 20) for i, k in enumerate(
+    ["dy", "dx", "ddt", "dz", "dBm", "dCm", "dA", "dDskip", "ddt_bias", "dh0", "dhL"])}
+
+
+def _bwd_call(layout=None, **over):
+    """ssm_scan_bwd_strided on fake, never dereferenced addresses."""
+    a = dict(batch=2, dim=8, seqlen=40, dstate=16, in_dtype=1, flags=0, grad_dtype=0,
+             ws=0x300000000, wsb=None, **_FAKE, **_BWD_FAKE)
+    a.update(over)
+    if a["wsb"] is None:
+        a["wsb"] = ssm.lib().ssm_scan_bwd_workspace_bytes(a["batch"], a["dim"], a["seqlen"],
+                                                          a["dstate"])
+    lay = None
+    if layout is not None:
+        lay = ssm.BwdLayout(layout.get("seq_row", 0),
+                            (ctypes.c_longlong * 7)(*layout.get("seq_batch", (0,) * 7)),
+                            layout.get("bc_row", 0),
+                            (ctypes.c_longlong * 2)(*layout.get("bc_batch", (0, 0))))
+    return ssm.lib().ssm_scan_bwd_strided(
+        a["batch"], a["dim"], a["seqlen"], a["dstate"], a["in_dtype"], a["flags"], a["x"], a["dt"],
+        a["dt_bias"], a["A"], a["Bm"], a["Cm"], a["Dskip"], a["z"], a["h0"], a["grad_dtype"],
+        a["dy"], a["dhL"], a["dx"], a["ddt"], a["dz"], a["dBm"], a["dCm"], a["dA"], a["dDskip"],
+        a["ddt_bias"], a["dh0"], a["ws"], a["wsb"], ctypes.byref(lay) if lay is not None else None,
+        None)
+
+
+@no_gpu
+def test_bwd_strided_validation():
+    assert _bwd_call() == 8                                        # dense: reaches the launch
+    assert _bwd_call({}) == 8
+    assert _bwd_call({"seq_row": 39}) == 2
+    assert _bwd_call({"seq_row": -1}) == 2
+    assert _bwd_call({"seq_batch": (0, 0, 0, 0, 0, 8 * 40 - 1, 0)}) == 2   # ddt batch too small
+    assert _bwd_call({"bc_row": 39}) == 2
+    assert _bwd_call({"bc_batch": (0, 16 * 40 - 1)}) == 2
+    # z and dz as halves of [2, 16, 40] fp32 / bf16 buffers
+    half = dict(seq_batch=(0, 0, 640, 0, 0, 0, 640))
+    assert _bwd_call(half) == 8
+    # dz's span (fp32, 960 elements) now reaches past the dense 320 * 2 ...
+    assert _bwd_call(half, dCm=_BWD_FAKE["dz"] + 2 * 320 * 4) == 5
+    assert _bwd_call(half, dCm=_BWD_FAKE["dz"] + 960 * 4) == 8
+    # an input's span: z (bf16) spans 960 elements
+    assert _bwd_call(half, dh0=_FAKE["z"] + 900 * 2) == 5
+    assert _bwd_call(half, dh0=_FAKE["z"] + 960 * 2) == 8
+    # outputs may not interleave with each other either
+    assert _bwd_call(dict(seq_batch=(0, 0, 0, 0, 640, 640, 0)), ddt=_BWD_FAKE["dx"] + 320 * 4) == 5
 
 
 @no_gpu

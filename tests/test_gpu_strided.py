@@ -221,3 +221,92 @@ def test_binding_rejects_unsupported_views():
         _scan(s, y=y)
     assert e.value.status == 2
     del xb, big
+
+
+# ------------------------------------------------------------ backward pass
+BWD_PER_ROW = ("dx", "ddt", "dz", "dh0")  # no atomics: bit-identical between calls
+
+
+def _bwd_dense(t, dy, **kw):
+    return ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy, dt_bias=t["dt_bias"],
+                            Dskip=t["Dskip"], z=t["z"], h0=t["h0"], **kw)
+
+
+@pytest.mark.parametrize("shape", [(2, 24, 16, 517, "bf16"), (3, 17, 8, 1024, "f32"),
+                                   (1, 40, 16, 2048, "bf16")],
+                         ids=lambda s: "b%d_d%d_N%d_L%d_%s" % s)
+def test_bwd_projection_halves(shape):
+    """Training layout: x and z halves of one xz buffer, Bm and Cm halves of
+    one buffer, dz written into the second half of the projection's dxz
+    gradient buffer (whose first half, the conv's input gradient, is left
+    alone), dt, dy and ddt as halves of buffers of their own (one shared row
+    stride).  The per-row gradients equal the dense call bit for bit, the
+    summed ones within rounding, and all match the oracle."""
+    import oracle
+    batch, dim, N, L, dt = shape
+    print("strided bwd", shape, flush=True)
+    inp = synth.make_inputs(workload("strided_bwd", batch, dim, N, L, dt, seed=31), with_h0=True)
+    d = _dense(inp)
+    rng = np.random.default_rng(4)
+    dyv = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    dy = torch.from_numpy(dyv).cuda()
+    g0 = _bwd_dense(d, dy)
+    s = dict(d)
+    s["x"], s["z"], xz = _halves(d["x"], d["z"])
+    s["Bm"], s["Cm"], bc = _halves(d["Bm"], d["Cm"])
+    # x and z have rows L apart (halves of xz); dt and dy need the same row
+    # stride, so they are halves of buffers of their own
+    s["dt"], _, dtb = _halves(d["dt"], torch.zeros_like(d["dt"]))
+    dys, _, dyb = _halves(dy, torch.zeros_like(dy))
+    dxz = _nan_fill((batch, 2 * dim, L), torch.float32)
+    ddtb = _nan_fill((batch, 2 * dim, L), torch.float32)
+    g1 = ssm.ssm_scan_bwd(s["x"], s["dt"], s["A"], s["Bm"], s["Cm"], dys, dt_bias=s["dt_bias"],
+                          Dskip=s["Dskip"], z=s["z"], h0=s["h0"], dz=dxz[:, dim:],
+                          ddt=ddtb[:, dim:])
+    torch.cuda.synchronize()
+    assert g1["dz"].data_ptr() == dxz[:, dim:].data_ptr()
+    assert _untouched(dxz[:, :dim])
+    for k in BWD_PER_ROW:
+        assert torch.equal(g1[k], g0[k]), k
+    for k in ("dBm", "dCm", "dA", "dDskip", "ddt_bias"):
+        assert rel_err(g1[k].cpu().numpy(), g0[k].cpu().numpy()) <= 1e-5, k
+    assert _untouched(ddtb[:, :dim])
+    r = oracle.scan_bwd(inp.values("x"), inp.values("dt"), inp.A.astype(np.float64),
+                        inp.values("Bm"), inp.values("Cm"), dyv.astype(np.float64),
+                        dt_bias=inp.dt_bias.astype(np.float64), Dskip=inp.Dskip.astype(np.float64),
+                        z=inp.values("z"), h0=inp.h0.astype(np.float64))
+    for k in ("dx", "ddt", "dz", "dBm", "dCm", "dA", "dh0"):
+        e = rel_err(g1[k].cpu().numpy(), r[k])
+        assert e <= 1e-4, (k, e)
+    del xz, bc, dtb, dyb
+
+
+def test_bwd_padded_rows_element_path():
+    """Rows L + 3 apart (bf16 runs then never sit on 8-byte boundaries): the
+    element path, against the dense call."""
+    batch, dim, N, L = 2, 20, 16, 400
+    inp = synth.make_inputs(workload("strided_bwd_pad", batch, dim, N, L, "bf16", seed=32),
+                            with_h0=True)
+    d = _dense(inp)
+    dy = torch.randn(batch, dim, L, device="cuda")
+    g0 = _bwd_dense(d, dy)
+    s, keep = dict(d), []
+    for k in ("x", "dt", "z"):
+        s[k], b = _padded(d[k], 3)
+        keep.append(b)
+    dys, b = _padded(dy, 3)
+    keep.append(b)
+    outs = {}
+    for k in ("dx", "ddt", "dz"):
+        outs[k], b = _padded(torch.empty((batch, dim, L), device="cuda"), 3)
+        b.view(torch.int32).fill_(NAN_BITS)
+        keep.append(b)
+    g1 = ssm.ssm_scan_bwd(s["x"], s["dt"], s["A"], s["Bm"], s["Cm"], dys, dt_bias=s["dt_bias"],
+                          Dskip=s["Dskip"], z=s["z"], h0=s["h0"], **outs)
+    torch.cuda.synchronize()
+    for k in BWD_PER_ROW:
+        assert torch.equal(g1[k], g0[k]), k
+    for k in ("dBm", "dCm", "dA"):
+        assert rel_err(g1[k].cpu().numpy(), g0[k].cpu().numpy()) <= 1e-5, k
+    for b in keep[-3:]:
+        assert _untouched(b[:, :, L:])
