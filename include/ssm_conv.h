@@ -58,6 +58,33 @@ ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype
                             void *y, float *stateL, void *stream);
 
 /*
+ * Strided layouts for ssm_conv1d_fwd_strided: strides in ELEMENTS, time
+ * contiguous.  The block's conv reads the SSM branch x, one half of the
+ * input projection's [batch][2 dim][seqlen] output (glossary entry "Mamba
+ * Block"), so x usually arrives as a view with rows seqlen apart and batch
+ * entries 2 dim seqlen apart.
+ *   x_row, y_row      distance between channel rows; >= seqlen; 0 means seqlen
+ *   x_batch, y_batch  distance between batch entries; >= dim * row stride;
+ *                     0 means dim * row stride
+ * A stride below its minimum, a negative one, or a tensor spanning 2^56
+ * elements or more is SSM_ERR_BAD_SHAPE.  Overlap is judged on each tensor's
+ * address range from its first to its last element.  weight, bias and the
+ * conv states stay dense.
+ */
+typedef struct {
+    long long x_row, x_batch;
+    long long y_row, y_batch;
+} ssm_conv_layout_t;
+
+/* ssm_conv1d_fwd on strided x and y: the same arguments and errors, with
+ * `layout` (host pointer, read during the call only; NULL means dense). */
+ssm_status_t ssm_conv1d_fwd_strided(int batch, int dim, int seqlen, int width,
+                                    ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                    const float *weight, const float *bias, const float *state0,
+                                    ssm_dtype_t out_dtype, void *y, float *stateL,
+                                    const ssm_conv_layout_t *layout, void *stream);
+
+/*
  * One decode step: the same operation at seqlen = 1 on a persistent state.
  *   state    [batch][dim][width-1] fp32, read and overwritten in place with
  *            the window shifted by one (the new input last)

@@ -35,7 +35,8 @@ STATUS = {
     7: "SSM_ERR_WORKSPACE", 8: "SSM_ERR_HIP",
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
-           "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_update",
+           "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided",
+           "ssm_conv1d_update",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_strided"]
 
 
@@ -49,6 +50,12 @@ class BwdLayout(ctypes.Structure):
     """ssm_scan_bwd_layout_t: strides in elements, 0 = dense default."""
     _fields_ = [("seq_row", ctypes.c_longlong), ("seq_batch", ctypes.c_longlong * 7),
                 ("bc_row", ctypes.c_longlong), ("bc_batch", ctypes.c_longlong * 2)]
+
+
+class ConvLayout(ctypes.Structure):
+    """ssm_conv_layout_t: strides in elements, 0 = dense default."""
+    _fields_ = [("x_row", ctypes.c_longlong), ("x_batch", ctypes.c_longlong),
+                ("y_row", ctypes.c_longlong), ("y_batch", ctypes.c_longlong)]
 
 
 class SSMError(RuntimeError):
@@ -91,6 +98,9 @@ def lib():
                                            [sz, ctypes.POINTER(BwdLayout), vp])
         L.ssm_conv1d_fwd.restype = i
         L.ssm_conv1d_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 4 + [i, vp, vp, vp]
+        L.ssm_conv1d_fwd_strided.restype = i
+        L.ssm_conv1d_fwd_strided.argtypes = ([i, i, i, i, i, u] + [vp] * 4 +
+                                             [i, vp, vp, ctypes.POINTER(ConvLayout), vp])
         L.ssm_conv1d_update.restype = i
         L.ssm_conv1d_update.argtypes = [i, i, i, i, u] + [vp] * 4 + [i, vp, vp]
         _lib = L
@@ -302,7 +312,9 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
 def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=None,
                    return_final_state=True, y=None, stateL=None, stream=None):
     """Causal depthwise conv over [batch, dim, L]; returns (y, stateL).
-    out_dtype defaults to x's dtype (the conv output feeds the scan's x)."""
+    out_dtype defaults to x's dtype (the conv output feeds the scan's x).
+    x and y may be strided views with a contiguous time index (x as the
+    first half of the input projection's [batch, 2 dim, L] output)."""
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -313,12 +325,15 @@ def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=No
     if stateL is None and return_final_state:
         stateL = torch.empty((batch, dim, W - 1), dtype=torch.float32, device=x.device)
     f32 = torch.float32
-    args = [_ptr(x, "x", (batch, dim, L), x.dtype), _ptr(weight, "weight", (dim, W), f32),
+    (xp,), x_row, (x_b,) = _rows((x,), ("x",), (batch, dim, L), x.dtype)
+    (yp,), y_row, (y_b,) = _rows((y,), ("y",), (batch, dim, L), out_dtype)
+    layout = ConvLayout(x_row, x_b, y_row, y_b)
+    args = [xp, _ptr(weight, "weight", (dim, W), f32),
             _ptr(bias, "bias", (dim,), f32), _ptr(state0, "state0", (batch, dim, W - 1), f32)]
-    yp = _ptr(y, "y", (batch, dim, L), y.dtype)
     sp = _ptr(stateL, "stateL", (batch, dim, W - 1), f32)
-    st = lib().ssm_conv1d_fwd(batch, dim, L, W, _dtype_code(x.dtype), SSM_CONV_SILU if silu else 0,
-                              *args, _dtype_code(y.dtype), yp, sp, _stream(stream, x.device))
+    st = lib().ssm_conv1d_fwd_strided(batch, dim, L, W, _dtype_code(x.dtype),
+                                      SSM_CONV_SILU if silu else 0, *args, _dtype_code(y.dtype), yp,
+                                      sp, ctypes.byref(layout), _stream(stream, x.device))
     _check(st)
     return y, stateL
 

@@ -33,7 +33,10 @@ constexpr int kConvThreads = 256;
 struct ConvParams {
     int dim, seqlen, runs_per_row;
     unsigned div_mul, div_shift;  // g / runs_per_row == (umulhi(g, mul) + g) >> shift
+    unsigned dim_mul, dim_shift;  // row / dim likewise
     long long total_runs;
+    // element strides (time contiguous): channel rows and batch entries
+    long long x_row, x_b, y_row, y_b;
     const void *x;
     const float *weight, *bias, *state0;
     void *y;
@@ -107,21 +110,24 @@ conv1d_fwd_kernel(ConvParams p, bool vec_in, bool vec_out, bool act)
     constexpr int H = W - 1;
     const long long g = (long long)blockIdx.x * kConvThreads + threadIdx.x;
     const bool live = g < p.total_runs;
-    long long row;
+    long long row, bi;  // row = bi * dim + d
     int j;
     if constexpr (kWide) {
         row = g / p.runs_per_row;
         j = int(g - row * p.runs_per_row);
+        bi = row / p.dim;
     } else {
         const unsigned q = div_magic(unsigned(g), p.div_mul, p.div_shift);
         row = q;
         j = int(unsigned(g) - q * unsigned(p.runs_per_row));
+        bi = div_magic(q, p.dim_mul, p.dim_shift);
     }
+    const int d = int(row - bi * p.dim);
     const int L = p.seqlen;
     const int t0 = j * kRun;
     const int count = live ? min(kRun, L - t0) : 0;
 
-    const Tin *xr = static_cast<const Tin *>(p.x) + row * L;
+    const Tin *xr = static_cast<const Tin *>(p.x) + bi * p.x_b + d * p.x_row;
     float e[H + kRun];  // e[H + i] = x[t0 + i]; e[0..H) the inputs before the run
     if (live) {
         load_run<Tin, kRun>(xr + t0, vec_in && count == kRun, count, e + H);
@@ -142,8 +148,6 @@ conv1d_fwd_kernel(ConvParams p, bool vec_in, bool vec_out, bool act)
 #pragma unroll
         for (int k = 0; k < H; ++k) e[k] = io<Tin>::load1(xr + t0 - H + k);
     }
-    const int d = int(row % p.dim);
-
     float taps[W];
     load_taps<W>(p.weight + (size_t)d * W, taps);
     const float b = p.bias ? p.bias[d] : 0.0f;
@@ -155,8 +159,8 @@ conv1d_fwd_kernel(ConvParams p, bool vec_in, bool vec_out, bool act)
         for (int k = 0; k < W; ++k) s = __builtin_fmaf(taps[k], e[i + k], s);
         out[i] = act ? silu(s) : s;
     }
-    store_run<Tout>(static_cast<Tout *>(p.y) + row * L + t0, vec_out && count == kRun, count,
-                    out);
+    store_run<Tout>(static_cast<Tout *>(p.y) + bi * p.y_b + d * p.y_row + t0,
+                    vec_out && count == kRun, count, out);
 
     if (j == 0 && p.stateL) {
         // Final state = the last H entries of (state0, x).  This lane already
@@ -225,12 +229,22 @@ hipError_t launch_conv_typed(const ConvArgs &a, hipStream_t stream)
     p.state0 = a.state0;
     p.y = a.y;
     p.stateL = a.stateL;
-    // Every run starts at element row * L + 8 j; 16-byte vectors need that
-    // offset times the element size to be a multiple of 16 on a 16-byte base.
-    const bool vec_in = aligned16(a.x) && (size_t(a.seqlen) * sizeof(Tin)) % 16 == 0 &&
-                        (kRun * sizeof(Tin)) % 16 == 0;
-    const bool vec_out = aligned16(a.y) && (size_t(a.seqlen) * sizeof(Tout)) % 16 == 0 &&
-                         (kRun * sizeof(Tout)) % 16 == 0;
+    p.x_row = a.x_row;
+    p.x_b = a.x_b;
+    p.y_row = a.y_row;
+    p.y_b = a.y_b;
+    const MagicDiv md = magic_div(unsigned(a.dim));
+    p.dim_mul = md.mul;
+    p.dim_shift = md.shift;
+    // Every run starts at element b * batch stride + d * row stride + 8 j;
+    // 16-byte vectors need each term times the element size to be a multiple
+    // of 16 on a 16-byte base.
+    auto vec16 = [](const void *base, size_t esize, long long row, long long bs) {
+        return aligned16(base) && (size_t(row) * esize) % 16 == 0 && (size_t(bs) * esize) % 16 == 0 &&
+               (kRun * esize) % 16 == 0;
+    };
+    const bool vec_in = vec16(a.x, sizeof(Tin), a.x_row, a.x_b);
+    const bool vec_out = vec16(a.y, sizeof(Tout), a.y_row, a.y_b);
     const long long blocks = (p.total_runs + kConvThreads - 1) / kConvThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.total_runs + kConvThreads <= (1ll << 32)) {

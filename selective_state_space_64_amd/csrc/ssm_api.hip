@@ -247,13 +247,31 @@ ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype
                             const float *bias, const float *state0, ssm_dtype_t out_dtype,
                             void *y, float *stateL, void *stream)
 {
+    return ssm_conv1d_fwd_strided(batch, dim, seqlen, width, in_dtype, flags, x, weight, bias,
+                                  state0, out_dtype, y, stateL, nullptr, stream);
+}
+
+ssm_status_t ssm_conv1d_fwd_strided(int batch, int dim, int seqlen, int width,
+                                    ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                    const float *weight, const float *bias, const float *state0,
+                                    ssm_dtype_t out_dtype, void *y, float *stateL,
+                                    const ssm_conv_layout_t *layout, void *stream)
+{
     if (!x || !weight || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1 || seqlen < 1) return SSM_ERR_BAD_SHAPE;
     if (width < 2 || width > 4 || (flags & ~SSM_CONV_SILU) != 0) return SSM_ERR_UNSUPPORTED;
-    const size_t seq_elems = mul3(batch, dim, seqlen);
     const size_t st_elems = mul3(batch, dim, width - 1);
-    if (!seq_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+    if (!mul3(batch, dim, seqlen) || !st_elems) return SSM_ERR_BAD_SHAPE;
+    const ssm_conv_layout_t dense{};
+    const ssm_conv_layout_t &lay = layout ? *layout : dense;
+    long long x_row = lay.x_row ? lay.x_row : seqlen, y_row = lay.y_row ? lay.y_row : seqlen;
+    long long x_b, y_b;
+    size_t x_span, y_span;
+    if (x_row < seqlen || y_row < seqlen ||
+        !batch_span(lay.x_batch, batch, dim, x_row, seqlen, x_b, x_span) ||
+        !batch_span(lay.y_batch, batch, dim, y_row, seqlen, y_b, y_span))
+        return SSM_ERR_BAD_SHAPE;
 
     const size_t in = dsize(in_dtype);
     if (misaligned(x, in)) return SSM_ERR_MISALIGNED;
@@ -262,12 +280,12 @@ ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype
         if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
     if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
 
-    const size_t ybytes = seq_elems * dsize(out_dtype);
+    const size_t ybytes = y_span * dsize(out_dtype);
     const size_t sbytes = st_elems * sizeof(float);
     struct In {
         const void *p;
         size_t bytes;
-    } inputs[] = {{x, seq_elems * in},
+    } inputs[] = {{x, x_span * in},
                   {weight, size_t(dim) * width * sizeof(float)},
                   {bias, dim * sizeof(float)},
                   {state0, sbytes}};
@@ -280,7 +298,8 @@ ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype
     if (overlaps(y, ybytes, stateL, sbytes)) return SSM_ERR_ALIAS;
 
     ssm::ConvArgs a{batch, dim, seqlen, width, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
-                    (flags & SSM_CONV_SILU) != 0, x, weight, bias, state0, y, stateL};
+                    (flags & SSM_CONV_SILU) != 0, x, weight, bias, state0, y, stateL,
+                    x_row, x_b, y_row, y_b};
     const hipError_t e = ssm::launch_conv1d_fwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

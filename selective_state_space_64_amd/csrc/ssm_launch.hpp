@@ -56,6 +56,8 @@ struct ConvArgs {
     const float *weight, *bias, *state0;
     void *y;
     float *stateL;
+    // element strides of x and y (time contiguous): rows, batch entries
+    long long x_row, x_b, y_row, y_b;
 };
 
 struct ConvUpdateArgs {

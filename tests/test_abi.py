@@ -61,6 +61,8 @@ def test_binding_argtypes_match_prototypes():
                 assert at == ctypes.POINTER(ssm.ScanLayout), (name, decl, at)
             elif "ssm_scan_bwd_layout_t" in decl:
                 assert at == ctypes.POINTER(ssm.BwdLayout), (name, decl, at)
+            elif "ssm_conv_layout_t" in decl:
+                assert at == ctypes.POINTER(ssm.ConvLayout), (name, decl, at)
             elif "*" in decl:
                 assert at in (ctypes.c_void_p, ctypes.c_char_p), (name, decl, at)
             elif decl.startswith("size_t"):
@@ -434,6 +436,36 @@ def _conv_call(L, **over):
     a.update(over)
     return L.ssm_conv1d_fwd(a["batch"], a["dim"], a["seqlen"], a["width"], a["ind"], a["flags"],
                             a["x"], a["w"], a["bias"], a["s0"], a["outd"], a["y"], a["sL"], None)
+
+
+def _conv_strided_call(layout, **over):
+    a = dict(batch=2, dim=8, seqlen=40, width=4, ind=1, flags=1, outd=1, **_CFAKE)
+    a.update(over)
+    lay = None if layout is None else ssm.ConvLayout(*layout)
+    return ssm.lib().ssm_conv1d_fwd_strided(
+        a["batch"], a["dim"], a["seqlen"], a["width"], a["ind"], a["flags"], a["x"], a["w"],
+        a["bias"], a["s0"], a["outd"], a["y"], a["sL"],
+        ctypes.byref(lay) if lay is not None else None, None)
+
+
+@no_gpu
+def test_conv_strided_validation():
+    assert _conv_strided_call(None) == 8
+    assert _conv_strided_call((0, 0, 0, 0)) == 8
+    assert _conv_strided_call((40, 320, 40, 320)) == 8       # the dense strides, explicit
+    assert _conv_strided_call((39, 0, 0, 0)) == 2
+    assert _conv_strided_call((0, 0, -40, 0)) == 2
+    assert _conv_strided_call((0, 319, 0, 0)) == 2
+    assert _conv_strided_call((48, 8 * 48 - 1, 0, 0)) == 2
+    assert _conv_strided_call((0, 1 << 56, 0, 0)) == 2
+    # x as the first half of a [2, 16, 40] bf16 projection output: its span is
+    # 640 + 320 elements, so y (bf16) may start right after it but not before
+    xz = (0, 640, 0, 0)
+    assert _conv_strided_call(xz, y=_CFAKE["x"] + 900 * 2) == 5
+    assert _conv_strided_call(xz, y=_CFAKE["x"] + 960 * 2) == 8
+    # y strided: stateL must avoid y's span
+    assert _conv_strided_call((0, 0, 50, 1000), sL=_CFAKE["y"] + (1000 + 7 * 50 + 40) * 2 - 4) == 5
+    assert _conv_strided_call((0, 0, 50, 1000), sL=_CFAKE["y"] + (1000 + 7 * 50 + 40) * 2) == 8
 
 
 def _conv_update_call(L, **over):

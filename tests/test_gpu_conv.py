@@ -182,3 +182,53 @@ def test_conv_unaligned_pointers_and_guard_bands():
     for big, lo, n in ((ybig, G + 1, n_y), (sbig, G, n_s)):
         bits = big.view(torch.int32).cpu().numpy()
         assert (bits[:lo] == 0x7FC0DEAD).all() and (bits[lo + n:] == 0x7FC0DEAD).all()
+
+
+def test_conv_strided_x_from_projection_halves():
+    """x as the first half of the input projection's [batch, 2 dim, L]
+    output (vector path), and again with rows padded by 3 elements and y
+    written into a padded view (element path): both equal to the dense call
+    bit for bit, the padding of y untouched."""
+    batch, dim, L = 2, 37, 2048
+    inp, w, b, s0 = _conv_inputs(batch, dim, L, 4, "bf16")
+    x = to_dev(inp, "x")
+    wt, bt, st = torch.from_numpy(w).cuda(), torch.from_numpy(b).cuda(), torch.from_numpy(s0).cuda()
+    y0, s0d = ssm.ssm_conv1d_fwd(x, wt, bias=bt, state0=st, out_dtype=torch.float32)
+    xz = torch.cat([x, torch.randn(batch, dim, L, device="cuda").to(torch.bfloat16)], dim=1)
+    y1, s1 = ssm.ssm_conv1d_fwd(xz[:, :dim], wt, bias=bt, state0=st, out_dtype=torch.float32)
+    xp = torch.zeros(batch, dim, L + 3, dtype=torch.bfloat16, device="cuda")
+    xp[:, :, :L] = x
+    ybuf = torch.full((batch, dim + 1, L + 3), 777.0, device="cuda")
+    y2, s2 = ssm.ssm_conv1d_fwd(xp[:, :, :L], wt, bias=bt, state0=st, out_dtype=torch.float32,
+                                y=ybuf[:, 1:, :L])
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0) and torch.equal(s1, s0d)
+    assert torch.equal(y2, y0) and torch.equal(s2, s0d)
+    assert bool((ybuf[:, 0] == 777.0).all()) and bool((ybuf[:, :, L:] == 777.0).all())
+    ry, rs = oracle.conv1d(inp.values("x"), w, bias=b, state0=s0)
+    assert rel_err(y1.cpu().numpy(), ry) <= TOL_F32
+
+
+def test_block_order_on_projection_halves():
+    """The Mamba block's order on one bf16 projection buffer xz: the conv
+    reads the x half and writes bf16, the scan reads that output and the z
+    half in place.  The conv output against the oracle conv (bf16 output
+    gate); the scan against the oracle scan run on the conv output the GPU
+    produced."""
+    wl = workload("block_xz", 2, 40, 16, 900, "bf16", seed=10)
+    inp = synth.make_inputs(wl)
+    w, b = synth.conv_parameters(wl, 4)
+    xz = torch.cat([to_dev(inp, "x"), to_dev(inp, "z")], dim=1)
+    xc, _ = ssm.ssm_conv1d_fwd(xz[:, :40], torch.from_numpy(w).cuda(),
+                               bias=torch.from_numpy(b).cuda(), out_dtype=torch.bfloat16)
+    y, hL = ssm.ssm_scan_fwd(xc, to_dev(inp, "dt"), to_dev(inp, "A"), to_dev(inp, "Bm"),
+                             to_dev(inp, "Cm"), dt_bias=to_dev(inp, "dt_bias"),
+                             Dskip=to_dev(inp, "Dskip"), z=xz[:, 40:])
+    torch.cuda.synchronize()
+    xcv = xc.float().cpu().numpy().astype(np.float64)
+    rc, _ = oracle.conv1d(inp.values("x"), w, bias=b)
+    assert rel_err(xcv, rc) <= TOL_BF16_OUT
+    ry, rh = oracle.scan_fwd(xcv, inp.values("dt"), inp.A, inp.values("Bm"), inp.values("Cm"),
+                             dt_bias=inp.dt_bias, Dskip=inp.Dskip, z=inp.values("z"))
+    assert rel_err(y.cpu().numpy(), ry) <= 2e-3
+    assert rel_err(hL.cpu().numpy(), rh) <= 2e-3
