@@ -202,6 +202,31 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
                               const void *Cm, const float *Dskip, const void *z,
                               ssm_dtype_t out_dtype, void *y, void *stream);
 
+/*
+ * Per-token inputs of the decode step usually arrive as slices of the
+ * step's projection outputs: x and z as the halves of one [batch][2 dim]
+ * row (glossary entry "Mamba Block"), Bm and Cm as parts of one
+ * [batch][dt_rank + 2 dstate] row.  Batch strides in ELEMENTS (0 means
+ * dense: dim for x, dt, z, y; dstate for Bm, Cm); each at least that dense
+ * value.  A negative stride, one below its minimum, or a tensor spanning 2^56
+ * elements or more is SSM_ERR_BAD_SHAPE; overlap is judged on address
+ * ranges from first to last element.
+ */
+typedef struct {
+    long long x_batch, dt_batch, z_batch, y_batch;
+    long long B_batch, C_batch;
+} ssm_update_layout_t;
+
+/* ssm_state_update on batch-strided inputs and output: the same arguments
+ * and errors, with `layout` (host pointer, read during the call only; NULL
+ * means dense).  The state stays dense. */
+ssm_status_t ssm_state_update_strided(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
+                                      unsigned flags, float *state, const void *x,
+                                      const void *dt, const float *dt_bias, const float *A,
+                                      const void *Bm, const void *Cm, const float *Dskip,
+                                      const void *z, ssm_dtype_t out_dtype, void *y,
+                                      const ssm_update_layout_t *layout, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

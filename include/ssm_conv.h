@@ -95,6 +95,15 @@ ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dty
                                unsigned flags, float *state, const void *x, const float *weight,
                                const float *bias, ssm_dtype_t out_dtype, void *y, void *stream);
 
+/* ssm_conv1d_update with batch strides in ELEMENTS for x (the x half of
+ * the step's [batch][2 dim] projection row, say) and y: 0 means dim, else
+ * at least dim.  Errors as for ssm_conv1d_fwd_strided; the state is dense. */
+ssm_status_t ssm_conv1d_update_strided(int batch, int dim, int width, ssm_dtype_t in_dtype,
+                                       unsigned flags, float *state, const void *x,
+                                       const float *weight, const float *bias,
+                                       ssm_dtype_t out_dtype, void *y, long long x_batch,
+                                       long long y_batch, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,8 +35,9 @@ STATUS = {
     7: "SSM_ERR_WORKSPACE", 8: "SSM_ERR_HIP",
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
-           "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_state_update", "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided",
-           "ssm_conv1d_update",
+           "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_state_update", "ssm_state_update_strided",
+           "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided", "ssm_conv1d_update",
+           "ssm_conv1d_update_strided",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_strided"]
 
 
@@ -56,6 +57,13 @@ class ConvLayout(ctypes.Structure):
     """ssm_conv_layout_t: strides in elements, 0 = dense default."""
     _fields_ = [("x_row", ctypes.c_longlong), ("x_batch", ctypes.c_longlong),
                 ("y_row", ctypes.c_longlong), ("y_batch", ctypes.c_longlong)]
+
+
+class UpdateLayout(ctypes.Structure):
+    """ssm_update_layout_t: batch strides in elements, 0 = dense default."""
+    _fields_ = [("x_batch", ctypes.c_longlong), ("dt_batch", ctypes.c_longlong),
+                ("z_batch", ctypes.c_longlong), ("y_batch", ctypes.c_longlong),
+                ("B_batch", ctypes.c_longlong), ("C_batch", ctypes.c_longlong)]
 
 
 class SSMError(RuntimeError):
@@ -87,6 +95,12 @@ def lib():
         L.ssm_scan_fwd_strided.restype = i
         L.ssm_scan_fwd_strided.argtypes = ([i, i, i, i, i, u] + [vp] * 9 +
                                            [i, vp, vp, vp, sz, ctypes.POINTER(ScanLayout), vp])
+        L.ssm_state_update_strided.restype = i
+        L.ssm_state_update_strided.argtypes = ([i, i, i, i, u] + [vp] * 9 +
+                                               [i, vp, ctypes.POINTER(UpdateLayout), vp])
+        L.ssm_conv1d_update_strided.restype = i
+        L.ssm_conv1d_update_strided.argtypes = ([i, i, i, i, u] + [vp] * 4 +
+                                                [i, vp, ctypes.c_longlong, ctypes.c_longlong, vp])
         L.ssm_state_update.restype = i
         L.ssm_state_update.argtypes = [i, i, i, i, u] + [vp] * 9 + [i, vp, vp]
         L.ssm_scan_bwd_workspace_bytes.restype = sz
@@ -166,6 +180,23 @@ def _rows(ts, names, shape, dtype):
     return ptrs, (rstride if rstride is not None else 0), bstrides
 
 
+def _bptr(t, name, shape, dtype):
+    """Pointer and batch stride (elements; 0 = dense) of a [batch, n] tensor
+    whose last index is contiguous, e.g. one half of a projection row."""
+    if t is None:
+        return None, 0
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have a contiguous last index" % name)
+    sb = t.stride(0)
+    return t.data_ptr(), (sb if shape[0] > 1 and sb != shape[1] else 0)
+
+
 def _stream(stream, device):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return s.cuda_stream
@@ -227,23 +258,32 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
 def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None,
                      out_dtype=torch.float32, y=None, zoh=False, stream=None):
     """One decode step; updates `state` in place and returns y [batch, dim].
-    zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B)."""
+    zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B).
+    x, dt, z, y, Bm and Cm may be batch-strided views with a contiguous last
+    index (x and z as halves of the step's [batch, 2 dim] projection row)."""
     batch, dim, N = state.shape
     ind = x.dtype
     if y is None:
         y = torch.empty((batch, dim), dtype=out_dtype, device=x.device)
     f32 = torch.float32
+    xp, xb = _bptr(x, "x", (batch, dim), ind)
+    dtp, dtb = _bptr(dt, "dt", (batch, dim), ind)
+    zp, zb = _bptr(z, "z", (batch, dim), ind)
+    yp, yb = _bptr(y, "y", (batch, dim), out_dtype)
+    Bp, Bb = _bptr(Bm, "Bm", (batch, N), ind)
+    Cp, Cb = _bptr(Cm, "Cm", (batch, N), ind)
+    # a layout only when some tensor is strided (keeps the per-token call lean)
+    layout = UpdateLayout(xb, dtb, zb, yb, Bb, Cb) if (xb or dtb or zb or yb or Bb or Cb) else None
     args = [
-        _ptr(state, "state", (batch, dim, N), f32),
-        _ptr(x, "x", (batch, dim), ind), _ptr(dt, "dt", (batch, dim), ind),
-        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
-        _ptr(Bm, "Bm", (batch, N), ind), _ptr(Cm, "Cm", (batch, N), ind),
-        _ptr(Dskip, "Dskip", (dim,), f32), _ptr(z, "z", (batch, dim), ind),
+        _ptr(state, "state", (batch, dim, N), f32), xp, dtp,
+        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32), Bp, Cp,
+        _ptr(Dskip, "Dskip", (dim,), f32), zp,
     ]
-    yp = _ptr(y, "y", (batch, dim), out_dtype)
     flags = SSM_FLAG_ZOH_B if zoh else 0
-    st = lib().ssm_state_update(batch, dim, N, _dtype_code(ind), flags, *args, _dtype_code(y.dtype),
-                                yp, _stream(stream, x.device))
+    st = lib().ssm_state_update_strided(batch, dim, N, _dtype_code(ind), flags, *args,
+                                        _dtype_code(y.dtype), yp,
+                                        None if layout is None else ctypes.byref(layout),
+                                        _stream(stream, x.device))
     _check(st)
     return y
 
@@ -341,18 +381,20 @@ def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=No
 def ssm_conv1d_update(state, x, weight, *, bias=None, silu=True, out_dtype=None, y=None,
                       stream=None):
     """One decode step of the conv; shifts `state` [batch, dim, W-1] in place
-    and returns y [batch, dim]."""
+    and returns y [batch, dim].  x and y may be batch-strided views with a
+    contiguous last index (x as the first half of the step's projection row)."""
     batch, dim, H = state.shape
     out_dtype = out_dtype or x.dtype
     if y is None:
         y = torch.empty((batch, dim), dtype=out_dtype, device=x.device)
     f32 = torch.float32
-    args = [_ptr(state, "state", (batch, dim, H), f32), _ptr(x, "x", (batch, dim), x.dtype),
+    xp, xb = _bptr(x, "x", (batch, dim), x.dtype)
+    yp, yb = _bptr(y, "y", (batch, dim), out_dtype)
+    args = [_ptr(state, "state", (batch, dim, H), f32), xp,
             _ptr(weight, "weight", (dim, H + 1), f32), _ptr(bias, "bias", (dim,), f32)]
-    yp = _ptr(y, "y", (batch, dim), y.dtype)
-    st = lib().ssm_conv1d_update(batch, dim, H + 1, _dtype_code(x.dtype),
-                                 SSM_CONV_SILU if silu else 0, *args, _dtype_code(y.dtype), yp,
-                                 _stream(stream, x.device))
+    st = lib().ssm_conv1d_update_strided(batch, dim, H + 1, _dtype_code(x.dtype),
+                                         SSM_CONV_SILU if silu else 0, *args, _dtype_code(y.dtype),
+                                         yp, xb, yb, _stream(stream, x.device))
     _check(st)
     return y
 

@@ -182,6 +182,7 @@ struct ConvUpdateParams {
     const void *x;
     const float *weight, *bias;
     void *y;
+    long long x_b, y_b;  // batch strides in elements
 };
 
 // One lane per (batch, channel): y = act(bias + sum_k w[k] e[k]) over
@@ -193,21 +194,23 @@ conv1d_update_kernel(ConvUpdateParams p, bool act)
     constexpr int H = W - 1;
     const long long row = (long long)blockIdx.x * kConvThreads + threadIdx.x;
     if (row >= (long long)p.batch * p.dim) return;
-    const int d = int(row % p.dim);
+    const long long bi = row / p.dim;
+    const int d = int(row - bi * p.dim);
     float e[W];
 #pragma unroll
     for (int k = 0; k < H; ++k) e[k] = p.state[row * H + k];
-    e[H] = io<Tin>::load1(static_cast<const Tin *>(p.x) + row);
+    e[H] = io<Tin>::load1(static_cast<const Tin *>(p.x) + bi * p.x_b + d);
     float taps[W];
     load_taps<W>(p.weight + (size_t)d * W, taps);
     float s = p.bias ? p.bias[d] : 0.0f;
 #pragma unroll
     for (int k = 0; k < W; ++k) s = __builtin_fmaf(taps[k], e[k], s);
     const float v = act ? silu(s) : s;
+    const long long yi = bi * p.y_b + d;
     if constexpr (sizeof(Tout) == 4) {
-        static_cast<float *>(p.y)[row] = v;
+        static_cast<float *>(p.y)[yi] = v;
     } else {
-        static_cast<bf16_t *>(p.y)[row].bits = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu);
+        static_cast<bf16_t *>(p.y)[yi].bits = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu);
     }
 #pragma unroll
     for (int k = 0; k < H; ++k) p.state[row * H + k] = e[k + 1];
@@ -263,7 +266,7 @@ hipError_t launch_conv_typed(const ConvArgs &a, hipStream_t stream)
 template <typename Tin, typename Tout, int W>
 hipError_t launch_update_typed(const ConvUpdateArgs &a, hipStream_t stream)
 {
-    ConvUpdateParams p{a.batch, a.dim, a.state, a.x, a.weight, a.bias, a.y};
+    ConvUpdateParams p{a.batch, a.dim, a.state, a.x, a.weight, a.bias, a.y, a.x_b, a.y_b};
     const long long rows = (long long)a.batch * a.dim;
     const long long blocks = (rows + kConvThreads - 1) / kConvThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;

@@ -199,6 +199,17 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
                               const void *Cm, const float *Dskip, const void *z,
                               ssm_dtype_t out_dtype, void *y, void *stream)
 {
+    return ssm_state_update_strided(batch, dim, dstate, in_dtype, flags, state, x, dt, dt_bias, A,
+                                    Bm, Cm, Dskip, z, out_dtype, y, nullptr, stream);
+}
+
+ssm_status_t ssm_state_update_strided(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
+                                      unsigned flags, float *state, const void *x,
+                                      const void *dt, const float *dt_bias, const float *A,
+                                      const void *Bm, const void *Cm, const float *Dskip,
+                                      const void *z, ssm_dtype_t out_dtype, void *y,
+                                      const ssm_update_layout_t *layout, void *stream)
+{
     if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1) return SSM_ERR_BAD_SHAPE;
@@ -208,6 +219,17 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
     if (batch > ssm::kMaxBatch) return SSM_ERR_BAD_SHAPE;
     const size_t st_elems = mul3(batch, dim, dstate);
     if (!rows || !st_elems) return SSM_ERR_BAD_SHAPE;
+    const ssm_update_layout_t dense{};
+    const ssm_update_layout_t &lay = layout ? *layout : dense;
+    // batch strides and spans: x, dt, z, y (rows of dim), Bm, Cm (rows of dstate)
+    long long sb[6];
+    size_t sp[6];
+    const long long given[6] = {lay.x_batch, lay.dt_batch, lay.z_batch, lay.y_batch, lay.B_batch,
+                                lay.C_batch};
+    for (int i = 0; i < 6; ++i) {
+        const int n = i < 4 ? dim : dstate;
+        if (!batch_span(given[i], batch, 1, n, n, sb[i], sp[i])) return SSM_ERR_BAD_SHAPE;
+    }
 
     const size_t in = dsize(in_dtype);
     if (misaligned(state, 16)) return SSM_ERR_MISALIGNED;
@@ -217,19 +239,19 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
         if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
     if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
 
-    const size_t ybytes = rows * dsize(out_dtype);
+    const size_t ybytes = sp[3] * dsize(out_dtype);
     const size_t sbytes = st_elems * sizeof(float);
     struct In {
         const void *p;
         size_t bytes;
-    } inputs[] = {{x, rows * in},
-                  {dt, rows * in},
+    } inputs[] = {{x, sp[0] * in},
+                  {dt, sp[1] * in},
                   {dt_bias, dim * sizeof(float)},
                   {A, size_t(dim) * dstate * sizeof(float)},
-                  {Bm, size_t(batch) * dstate * in},
-                  {Cm, size_t(batch) * dstate * in},
+                  {Bm, sp[4] * in},
+                  {Cm, sp[5] * in},
                   {Dskip, dim * sizeof(float)},
-                  {z, rows * in}};
+                  {z, sp[2] * in}};
     for (const In &i : inputs) {
         if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
         if (overlaps(state, sbytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
@@ -237,7 +259,8 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
     if (overlaps(y, ybytes, state, sbytes)) return SSM_ERR_ALIAS;
 
     ssm::UpdateArgs a{batch, dim, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
-                      (flags & SSM_FLAG_ZOH_B) != 0, state, x, dt, dt_bias, A, Bm, Cm, Dskip, z, y};
+                      (flags & SSM_FLAG_ZOH_B) != 0, state, x, dt, dt_bias, A, Bm, Cm, Dskip, z, y,
+                      sb[0], sb[1], sb[2], sb[3], sb[4], sb[5]};
     const hipError_t e = ssm::launch_state_update(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
@@ -308,6 +331,16 @@ ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dty
                                unsigned flags, float *state, const void *x, const float *weight,
                                const float *bias, ssm_dtype_t out_dtype, void *y, void *stream)
 {
+    return ssm_conv1d_update_strided(batch, dim, width, in_dtype, flags, state, x, weight, bias,
+                                     out_dtype, y, 0, 0, stream);
+}
+
+ssm_status_t ssm_conv1d_update_strided(int batch, int dim, int width, ssm_dtype_t in_dtype,
+                                       unsigned flags, float *state, const void *x,
+                                       const float *weight, const float *bias,
+                                       ssm_dtype_t out_dtype, void *y, long long x_batch,
+                                       long long y_batch, void *stream)
+{
     if (!state || !x || !weight || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1) return SSM_ERR_BAD_SHAPE;
@@ -315,6 +348,11 @@ ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dty
     const size_t rows = mul3(batch, dim, 1);
     const size_t st_elems = mul3(batch, dim, width - 1);
     if (!rows || !st_elems) return SSM_ERR_BAD_SHAPE;
+    long long x_b, y_b;
+    size_t x_span, y_span;
+    if (!batch_span(x_batch, batch, 1, dim, dim, x_b, x_span) ||
+        !batch_span(y_batch, batch, 1, dim, dim, y_b, y_span))
+        return SSM_ERR_BAD_SHAPE;
 
     const size_t in = dsize(in_dtype);
     if (misaligned(x, in)) return SSM_ERR_MISALIGNED;
@@ -322,12 +360,12 @@ ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dty
         if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
     if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
 
-    const size_t ybytes = rows * dsize(out_dtype);
+    const size_t ybytes = y_span * dsize(out_dtype);
     const size_t sbytes = st_elems * sizeof(float);
     struct In {
         const void *p;
         size_t bytes;
-    } inputs[] = {{x, rows * in},
+    } inputs[] = {{x, x_span * in},
                   {weight, size_t(dim) * width * sizeof(float)},
                   {bias, dim * sizeof(float)}};
     for (const In &i : inputs) {
@@ -337,7 +375,7 @@ ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dty
     if (overlaps(y, ybytes, state, sbytes)) return SSM_ERR_ALIAS;
 
     ssm::ConvUpdateArgs a{batch, dim, width, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
-                          (flags & SSM_CONV_SILU) != 0, state, x, weight, bias, y};
+                          (flags & SSM_CONV_SILU) != 0, state, x, weight, bias, y, x_b, y_b};
     const hipError_t e = ssm::launch_conv1d_update(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -47,6 +47,8 @@ struct UpdateArgs {
     const float *Dskip;
     const void *z;
     void *y;
+    // batch strides in elements: x, dt, z, y (rows of dim), Bm, Cm (rows of dstate)
+    long long x_b, dt_b, z_b, y_b, B_b, C_b;
 };
 
 struct ConvArgs {
@@ -67,6 +69,7 @@ struct ConvUpdateArgs {
     const void *x;
     const float *weight, *bias;
     void *y;
+    long long x_b, y_b;  // batch strides of x and y in elements
 };
 
 struct BwdArgs {

@@ -33,6 +33,8 @@ struct UpdateParams {
     const float *Dskip;
     const void *z;
     void *y;
+    // batch strides in elements of x, dt, z, y (rows of dim) and Bm, Cm (rows of N)
+    long long x_b, dt_b, z_b, y_b, B_b, C_b;
 };
 
 template <int N>
@@ -84,8 +86,8 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
     const size_t idx = size_t(b) * p.dim + d;
     const int n0 = r * S;
 
-    const Tin *Bp = static_cast<const Tin *>(p.Bm) + size_t(b) * N + n0;
-    const Tin *Cp = static_cast<const Tin *>(p.Cm) + size_t(b) * N + n0;
+    const Tin *Bp = static_cast<const Tin *>(p.Bm) + size_t(b) * size_t(p.B_b) + n0;
+    const Tin *Cp = static_cast<const Tin *>(p.Cm) + size_t(b) * size_t(p.C_b) + n0;
     float bm[S], cm[S];
 #pragma unroll
     for (int n = 0; n < S; ++n) {
@@ -103,8 +105,8 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
 #pragma unroll
         for (int n = 0; n < S; ++n) a[n] = Ap[n];
     }
-    const float xv = io<Tin>::load1(static_cast<const Tin *>(p.x) + idx);
-    const float dtv = io<Tin>::load1(static_cast<const Tin *>(p.dt) + idx);
+    const float xv = io<Tin>::load1(static_cast<const Tin *>(p.x) + size_t(b) * size_t(p.x_b) + d);
+    const float dtv = io<Tin>::load1(static_cast<const Tin *>(p.dt) + size_t(b) * size_t(p.dt_b) + d);
     const float bias = p.dt_bias ? p.dt_bias[d] : 0.0f;
     const float skip = p.Dskip ? p.Dskip[d] : 0.0f;
 
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
         acc = __builtin_fmaf(cm[n], h[n], acc);
     }
     acc = group_sum<R>(acc) + skip * xv;
-    if (p.z) acc *= silu(io<Tin>::load1(static_cast<const Tin *>(p.z) + idx));
+    if (p.z) acc *= silu(io<Tin>::load1(static_cast<const Tin *>(p.z) + size_t(b) * size_t(p.z_b) + d));
     if (!live) return;
 
     if constexpr (S == 4) {
@@ -133,10 +135,11 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
         for (int i = 0; i < S; ++i) st[i] = h[i];
     }
     if (r == 0) {
+        const size_t yi = size_t(b) * size_t(p.y_b) + d;
         if constexpr (sizeof(Tout) == 4) {
-            static_cast<float *>(p.y)[idx] = acc;
+            static_cast<float *>(p.y)[yi] = acc;
         } else {
-            static_cast<uint16_t *>(p.y)[idx] = uint16_t(pack_bf16x2(acc, 0.0f) & 0xffffu);
+            static_cast<uint16_t *>(p.y)[yi] = uint16_t(pack_bf16x2(acc, 0.0f) & 0xffffu);
         }
     }
 }
@@ -145,7 +148,7 @@ template <typename Tin, typename Tout, int N, bool kZoh>
 hipError_t launch_typed(const UpdateArgs &a, hipStream_t stream)
 {
     UpdateParams p{a.batch, a.dim, a.state, a.x, a.dt, a.dt_bias, a.A,
-                   a.Bm, a.Cm, a.Dskip, a.z, a.y};
+                   a.Bm, a.Cm, a.Dskip, a.z, a.y, a.x_b, a.dt_b, a.z_b, a.y_b, a.B_b, a.C_b};
     constexpr int R = N < 4 ? 1 : N / 4;
     dim3 grid(unsigned((size_t(a.dim) * R + kThreads - 1) / kThreads), a.batch);
     hipLaunchKernelGGL((state_update_kernel<Tin, Tout, N, kZoh>), grid, dim3(kThreads), 0, stream, p);

@@ -63,10 +63,14 @@ def test_binding_argtypes_match_prototypes():
                 assert at == ctypes.POINTER(ssm.BwdLayout), (name, decl, at)
             elif "ssm_conv_layout_t" in decl:
                 assert at == ctypes.POINTER(ssm.ConvLayout), (name, decl, at)
+            elif "ssm_update_layout_t" in decl:
+                assert at == ctypes.POINTER(ssm.UpdateLayout), (name, decl, at)
             elif "*" in decl:
                 assert at in (ctypes.c_void_p, ctypes.c_char_p), (name, decl, at)
             elif decl.startswith("size_t"):
                 assert at == ctypes.c_size_t, (name, decl, at)
+            elif decl.startswith("long long"):
+                assert at == ctypes.c_longlong, (name, decl, at)
             else:
                 assert at in (ctypes.c_int, ctypes.c_uint), (name, decl, at)
 
@@ -396,6 +400,44 @@ def test_bwd_strided_validation():
     assert _bwd_call(half, dh0=_FAKE["z"] + 960 * 2) == 8
     # outputs may not interleave with each other either
     assert _bwd_call(dict(seq_batch=(0, 0, 0, 0, 640, 640, 0)), ddt=_BWD_FAKE["dx"] + 320 * 4) == 5
+
+
+@no_gpu
+def test_decode_strided_validation():
+    L = ssm.lib()
+
+    def upd(layout, **o):
+        a = dict(batch=2, dim=8, N=16, state=_FAKE["h0"], x=_FAKE["x"], dt=_FAKE["dt"],
+                 z=_FAKE["z"], B=_FAKE["Bm"], C=_FAKE["Cm"], y=_FAKE["y"])
+        a.update(o)
+        lay = None if layout is None else ssm.UpdateLayout(*layout)
+        return L.ssm_state_update_strided(a["batch"], a["dim"], a["N"], 1, 0, a["state"], a["x"],
+                                          a["dt"], _FAKE["dt_bias"], _FAKE["A"], a["B"], a["C"],
+                                          _FAKE["Dskip"], a["z"], 0, a["y"],
+                                          ctypes.byref(lay) if lay is not None else None, None)
+
+    assert upd(None) == 8
+    assert upd((0,) * 6) == 8
+    assert upd((16, 0, 16, 0, 44, 44)) == 8                # x/z halves, Bm/Cm parts of x_dbl
+    assert upd((7, 0, 0, 0, 0, 0)) == 2                    # below dim
+    assert upd((0, 0, 0, 0, 15, 0)) == 2                   # below dstate
+    assert upd((0, 0, 0, -8, 0, 0)) == 2
+    # y (fp32) with batch stride 16 spans 16 + 8 elements; the state must avoid it
+    assert upd((0, 0, 0, 16, 0, 0), state=_FAKE["y"] + 96 - 16) == 5
+    assert upd((0, 0, 0, 16, 0, 0), state=_FAKE["y"] + 96) == 8
+
+    def cupd(xb, yb, **o):
+        a = dict(state=_CFAKE["s0"], x=_CFAKE["x"], y=_CFAKE["y"])
+        a.update(o)
+        return L.ssm_conv1d_update_strided(2, 8, 4, 1, 1, a["state"], a["x"], _CFAKE["w"],
+                                           _CFAKE["bias"], 0, a["y"], xb, yb, None)
+
+    assert cupd(0, 0) == 8
+    assert cupd(16, 0) == 8
+    assert cupd(7, 0) == 2
+    assert cupd(0, -1) == 2
+    assert cupd(16, 0, y=_CFAKE["x"] + 2 * 20) == 5         # y inside x's strided span
+    assert cupd(16, 0, y=_CFAKE["x"] + 2 * 24) == 8
 
 
 @no_gpu

@@ -130,3 +130,48 @@ def test_decode_steps_in_hip_graph():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(ys, ref_y) and torch.equal(state, ref_state)
+
+
+def test_decode_on_projection_slices():
+    """The decode step's inputs as slices of its projection rows: x and z
+    halves of one [batch, 2 dim] row per step, Bm and Cm parts of one
+    [batch, r + 2N] row per step, y into half of a [batch, 2 dim] buffer,
+    and the conv's decode step reading the same x half.  Equal bit for bit
+    to the dense calls, y's other half untouched, and against the oracle."""
+    batch, dim, N, steps, r = 5, 70, 16, 6, 12
+    inp = synth.make_inputs(workload("decode_slices", batch, dim, N, steps, "bf16", seed=41),
+                            with_h0=True)
+    ys0, st0 = _run_decode(inp, steps)
+    state = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
+    xs, dts, zs = _steps(to_dev(inp, "x")), _steps(to_dev(inp, "dt")), _steps(to_dev(inp, "z"))
+    Bs, Cs = _steps(to_dev(inp, "Bm")), _steps(to_dev(inp, "Cm"))
+    xz = torch.cat([xs, zs], dim=2)                                   # [steps, batch, 2 dim]
+    pad = torch.zeros(steps, batch, r, dtype=torch.bfloat16, device="cuda")
+    xdbl = torch.cat([pad, Bs, Cs], dim=2)                            # [steps, batch, r + 2N]
+    A, Dk, bias = to_dev(inp, "A"), to_dev(inp, "Dskip"), to_dev(inp, "dt_bias")
+    ybuf = torch.full((steps, batch, 2 * dim), 555.0, device="cuda")
+    for s in range(steps):
+        ssm.ssm_state_update(state, xz[s, :, :dim], dts[s], A, xdbl[s, :, r:r + N],
+                             xdbl[s, :, r + N:], dt_bias=bias, Dskip=Dk, z=xz[s, :, dim:],
+                             y=ybuf[s, :, dim:])
+    torch.cuda.synchronize()
+    assert torch.equal(ybuf[:, :, dim:], ys0) and torch.equal(state, st0)
+    assert bool((ybuf[:, :, :dim] == 555.0).all())
+    rows = [(b, d) for b in range(batch) for d in (0, 1, 33, dim - 1)]
+    ry, rh = _oracle_decode(inp, rows)
+    gy = torch.stack([ybuf[:, b, dim + d] for b, d in rows]).cpu().numpy()
+    assert rel_err(gy, ry) <= tol_for("bf16")
+    # the conv's decode step on the same x half
+    W = 4
+    w, cb = synth.conv_parameters(inp.wl, W)
+    wt, bt = torch.from_numpy(w).cuda(), torch.from_numpy(cb).cuda()
+    cs0 = torch.zeros(batch, dim, W - 1, device="cuda")
+    cs1 = torch.zeros(batch, dim, W - 1, device="cuda")
+    for s in range(steps):
+        a = ssm.ssm_conv1d_update(cs0, xs[s], wt, bias=bt, out_dtype=torch.float32)
+        ob = torch.full((batch, 2 * dim), 9.0, device="cuda")
+        b_ = ssm.ssm_conv1d_update(cs1, xz[s, :, :dim], wt, bias=bt, out_dtype=torch.float32,
+                                   y=ob[:, :dim])
+        torch.cuda.synchronize()
+        assert torch.equal(a, b_) and bool((ob[:, dim:] == 9.0).all())
+    assert torch.equal(cs0, cs1)
