@@ -49,6 +49,7 @@ constexpr int kThreadsB = 64 * kWavesB;
 constexpr int kChanB = kThreadsB / kRowB;  // channels per workgroup
 constexpr int kKB = 4;                     // consecutive steps per lane
 constexpr int kTB = kRowB * kKB;           // steps per chunk
+static_assert(kTB == kCkptSteps, "one checkpoint per reverse-pass chunk");
 
 constexpr int kCopies = 8;                 // partial dBm / dCm copies (one per XCD)
 
@@ -688,8 +689,7 @@ hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream)
 
 size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 {
-    const size_t nchunks = (size_t(seqlen) + kTB - 1) / kTB;
-    const size_t checkpoints = size_t(batch) * size_t(dim) * nchunks * size_t(dstate);
+    const size_t checkpoints = scan_checkpoint_floats(batch, dim, seqlen, dstate);
     const size_t partials = size_t(kCopies) * 2 * size_t(batch) * size_t(dstate) * size_t(seqlen);
     // A forward pass that writes the checkpoints keeps its sequence-split
     // planes where the partial sums go later.

@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             if constexpr (kCkpt) {
                 // checkpoints for the backward pass: the state entering each
                 // 64-step half of the chunk (the carry, and lane 7's end)
-                static_assert(kRow * K == 128, "two 64-step checkpoints per chunk");
+                static_assert(kRow * K == 2 * kCkptSteps, "two checkpoints per chunk");
                 const int half = j == kRow / 2 - 1 ? 1 : 0;
                 const int ck = 2 * (ch + lseg / T) + half;  // global 64-step chunk
                 if (live && (j == 0 || half) && ck < p.nck)
@@ -452,7 +452,7 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
     const ScanSplit sp = scan_fwd_split(a.batch, a.dim, a.seqlen);
     ScanParams p{a.dim, a.seqlen, a.row, a.x_b, a.dt_b, a.z_b, a.y_b, a.bc_row, a.B_b, a.C_b,
                  a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
-                 a.Dskip, a.z, a.h0, a.y, a.hL, a.ck, (a.seqlen + 63) / 64,
+                 a.Dskip, a.z, a.h0, a.y, a.hL, a.ck, (a.seqlen + kCkptSteps - 1) / kCkptSteps,
                  sp.seg_len, sp.nseg, a.agg};
     const unsigned gx = (a.dim + kChannels - 1) / kChannels;
     if (sp.nseg > 1) {

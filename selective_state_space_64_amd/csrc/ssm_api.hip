@@ -183,7 +183,7 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
         return SSM_ERR_ALIAS;
 
     float *ws = static_cast<float *>(workspace);
-    const size_t ck_floats = size_t(batch) * dim * ((size_t(seqlen) + 63) / 64) * dstate;
+    const size_t ck_floats = ssm::scan_checkpoint_floats(batch, dim, seqlen, dstate);
     float *agg = split_bytes ? (ckpt ? ws + ck_floats : ws) : nullptr;
     ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
                     (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,

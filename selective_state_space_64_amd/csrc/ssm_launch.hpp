@@ -92,7 +92,17 @@ struct BwdArgs {
     long long row, x_b, dt_b, z_b, dy_b, dx_b, ddt_b, dz_b, bc_row, B_b, C_b;
 };
 
-// Device workspace of the backward pass: the state entering every chunk.
+// The backward pass keeps the state entering every kCkptSteps-step chunk
+// (batch * dim * ceil(seqlen / kCkptSteps) * dstate floats at the start of
+// its workspace); the forward writes the same layout with checkpoints on.
+constexpr int kCkptSteps = 64;
+inline size_t scan_checkpoint_floats(int batch, int dim, int seqlen, int dstate)
+{
+    return size_t(batch) * size_t(dim) * ((size_t(seqlen) + kCkptSteps - 1) / kCkptSteps) *
+           size_t(dstate);
+}
+
+// Device workspace of the backward pass: the checkpoints, then the partial sums.
 size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
 
 // All return hipSuccess or the launch error; arguments are already validated.
