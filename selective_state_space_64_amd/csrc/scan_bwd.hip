@@ -156,16 +156,6 @@ __device__ inline float row_total_last(float v)
     return v;
 }
 
-// v + the value of the neighbouring lane (lanes 2i and 2i + 1 exchange).
-__device__ inline float add_lane_pair(float v)
-{
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-        : "+v"(v));
-    return v;
-}
-
 // Two independent forward row scans (see row_scan in scan_common.hpp),
 // interleaved so that each one's DPP read hazard is covered by the other's
 // instructions instead of wait states.
@@ -592,27 +582,27 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
                 for (int g = 0; g < G; ++g) das[n + g] += dap[g];
             }
 
-            // dBm[b, n, t] and dCm[b, n, t] sum over channels: lanes 2i, 2i + 1
-            // add 8 channels each for one (state, quantity, step), combine
-            // through DPP, and the even lane issues the atomic add into this
-            // workgroup's copy.  One barrier per pair: the terms alternate
-            // between two buffers, and a thread writes a buffer again only
-            // after the next pair's barrier, which every thread reaches after
-            // finishing its sums over that buffer.
+            // dBm[b, n, t] and dCm[b, n, t] sum over channels: one thread per
+            // (state, quantity, step) adds the 16 channels and issues the
+            // atomic add into this workgroup's copy.  A wave covers one
+            // (state, quantity) and 64 consecutive steps, so each of its LDS
+            // reads touches 64 consecutive floats (no bank conflicts).  One
+            // barrier per pair: the terms alternate between two buffers, and
+            // a thread writes a buffer again only after the next pair's
+            // barrier, which every thread reaches after finishing its sums
+            // over that buffer.
             lds_barrier();
+            {
+                static_assert(kThreadsB == 2 * 2 * T, "one thread per (state, quantity, step)");
+                const int g = tid / (2 * T), qq = (tid / T) & 1, t = tid % T;
+                if (g < G) {
+                    const float *col = reinterpret_cast<const float *>(&sP[pb][g][qq][0][0]) + t;
+                    float acc = 0.0f;
 #pragma unroll
-            for (int rep = 0; rep < G; ++rep) {
-                const int trip = rep * (kThreadsB / 2) + (tid >> 1);  // (state, quantity, step)
-                const int half = tid & 1;
-                const int g = trip / (2 * T), qq = (trip / T) & 1, t = trip % T;
-                const float *col = reinterpret_cast<const float *>(&sP[pb][g][qq][half * (kChanB / 2)][0]) + t;
-                float acc = 0.0f;
-#pragma unroll
-                for (int cc = 0; cc < kChanB / 2; ++cc) acc += col[cc * T];
-                acc = add_lane_pair(acc);
-                const int tt = ch * T + t;
-                if (half == 0 && tt < L)
-                    atomicAdd(&part[size_t(qq) * bnl + size_t(n + g) * L + tt], acc);
+                    for (int cc = 0; cc < kChanB; ++cc) acc += col[cc * T];
+                    const int tt = ch * T + t;
+                    if (tt < L) atomicAdd(&part[size_t(qq) * bnl + size_t(n + g) * L + tt], acc);
+                }
             }
         }
 
