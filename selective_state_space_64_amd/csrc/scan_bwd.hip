@@ -13,25 +13,31 @@
 //     dCm[b,n,t] += ds_t h_t                            dz_t = dy_t s_t silu'(z_t)
 // where s_t = C_t . h_t + Dskip x_t is the forward readout before the gate.
 //
-// Four launches:
-//   1. zero the accumulated gradients (dA, dDskip, ddt_bias) and the partial
+// Launches:
+//   1. unless the forward already wrote them, the checkpoints: the forward
+//      kernel itself in its checkpoint-only mode (no readout), keeping the
+//      state entering every 64-step chunk (batch*dim*ceil(L/64)*N floats of
+//      workspace), split along the sequence like the forward when few
+//      (b, d) rows would leave the GPU idle;
+//   2. zero the accumulated gradients (dA, dDskip, ddt_bias) and the partial
 //      dBm / dCm sums;
-//   2. chunk_states_kernel: the forward recurrence once more (8 steps per
-//      lane, 128-step row chunks), keeping only the state entering every
-//      64-step chunk (batch*dim*ceil(L/64)*N floats of workspace);
-//   3. scan_bwd_kernel: 64-step chunks in reverse order.  Per chunk, for
-//      pairs of states (two independent chains in flight per wave, their DPP
-//      scans interleaved), the workgroup recomputes the chunk's states from
-//      its checkpoint with the forward in-row scan, folds the adjoint of each
-//      lane's 4 steps into an affine map, composes the maps of a row with the
-//      mirrored (reverse time) DPP scan, replays the lane's steps backwards
-//      and accumulates the gradients.  dBm and dCm sum over channels: each lane leaves its terms
+//   3. for a split shape, adjoint_agg_kernel: every segment but the first,
+//      in reverse time, from zero (dhL for the last): its adjoint aggregate;
+//   4. scan_bwd_kernel: per segment (one for unsplit shapes), 64-step chunks
+//      in reverse order, entering with the later segments' aggregates
+//      composed.  Per chunk, for pairs of states (two independent chains in
+//      flight per wave, their DPP scans interleaved), the workgroup
+//      recomputes the chunk's states from its checkpoint with the forward
+//      in-row scan, folds the adjoint of each lane's 4 steps into an affine
+//      map, composes the maps of a row with the mirrored (reverse time) DPP
+//      scan, replays the lane's steps backwards and accumulates the
+//      gradients.  dBm and dCm sum over channels: each lane leaves its terms
 //      in LDS, the workgroup adds its 16 channels, and one atomic add per
 //      (state, step) goes to one of 8 partial copies chosen by workgroup
 //      index, so that the workgroups sharing a copy sit on one XCD (the
 //      dispatcher deals workgroups to the 8 XCDs in turn) and their atomics
 //      resolve in that XCD's L2;
-//   4. bwd_sum_kernel: dBm, dCm = the sum of the 8 copies.
+//   5. bwd_sum_kernel: dBm, dCm = the sum of the 8 copies.
 // The layout and lane mapping follow the forward kernel: a workgroup owns one
 // batch row and 16 channels, each 16-lane DPP row one channel.
 #include <algorithm>
@@ -70,6 +76,11 @@ struct BwdParams {
     float *dBm, *dCm, *dA, *dDskip, *ddt_bias, *dh0;
     float *ck;    // [batch][dim][nchunks][N] state entering each 64-step chunk
     float *part;  // [kCopies][2][batch][N][seqlen] partial dBm, dCm sums
+    // Sequence split (the forward's segments): segment blockIdx.z covers
+    // steps [z seg_len, (z+1) seg_len); adj[s][b][d][0..N-1] is segment s's
+    // adjoint aggregate, adj[s][b][d][N] its Delta sum (s >= 1).
+    int seg_len, nseg;
+    float *adj;
 };
 
 // A lane's run of K = 4 steps is 8 bytes of bf16 or 16 bytes of fp32: one
@@ -293,92 +304,93 @@ __global__ void bwd_sum_kernel(const float *part, size_t n, float *dB, float *dC
     }
 }
 
-// The state entering every 64-step chunk, from the forward recurrence.  Rows
-// of 16 lanes with 8 steps per lane cover 128 steps, i.e. two backward
-// chunks: the state entering the first is the carry, the state entering the
-// second is lane 7's inclusive result.  Per state: lane fold, row scan,
-// carry.
-template <typename Tin, int N>
-__global__ __launch_bounds__(kThreadsB, 4) void chunk_states_kernel(BwdParams p)
+// Adjoint aggregate of every segment but the first, in reverse time (the
+// mirror of the forward's aggregate pass): per (b, d, n), the adjoint passed
+// to the left out of segment s when dhL (last segment) or zero enters it
+// from the right, and the segment's Delta sum.  The adjoint map of a
+// segment is affine, mu_left = exp(A sum Delta) mu_right + that aggregate,
+// so the reverse pass can enter every segment at once.
+template <typename Tin, typename Tg, int N>
+__global__ __launch_bounds__(kThreadsB) void adjoint_agg_kernel(BwdParams p)
 {
-    constexpr int K = 8, T = kRowB * K, Q = K / 4, NP = N + 1;
-    static_assert(T == 2 * kTB, "one row chunk spans two backward chunks");
-    __shared__ float4 sB[N * Q * kRowB];
+    constexpr int K = kKB, T = kTB, Q = K / 4, NP = N + 1;
+    __shared__ float4 sC[N * Q * kRowB];
     __shared__ float sAP[kChanB * NP];
-    __shared__ float sCar[kChanB * NP];
+    __shared__ float sMu[kChanB * NP];
 
     const int tid = threadIdx.x, j = tid & (kRowB - 1), c = tid / kRowB;
     const int b = blockIdx.y, dim = p.dim, L = p.seqlen;
+    const int seg = int(blockIdx.z) + 1;
     const int d = int(blockIdx.x) * kChanB + c;
     const bool live = d < dim;
     const int dc = live ? d : dim - 1;
     const size_t rowo = size_t(dc) * size_t(p.row);
-    const Tin *xr = static_cast<const Tin *>(p.x) + size_t(b) * size_t(p.x_b) + rowo;
     const Tin *dtr = static_cast<const Tin *>(p.dt) + size_t(b) * size_t(p.dt_b) + rowo;
-    const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * size_t(p.B_b);
+    const Tin *zr = p.z ? static_cast<const Tin *>(p.z) + size_t(b) * size_t(p.z_b) + rowo : nullptr;
+    const Tg *dyr = static_cast<const Tg *>(p.dy) + size_t(b) * size_t(p.dy_b) + rowo;
+    const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * size_t(p.C_b);
 
     for (int s = tid; s < kChanB * NP; s += kThreadsB) {
         const int cc = s / NP, n = s % NP;
         const int dd = min(int(blockIdx.x) * kChanB + cc, dim - 1);
         sAP[s] = n < N ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
-        sCar[s] = (n < N && p.h0) ? p.h0[(size_t(b) * dim + dd) * N + n] : 0.0f;
+        sMu[s] = (n < N && p.dhL && seg == p.nseg - 1) ? p.dhL[(size_t(b) * dim + dd) * N + n] : 0.0f;
     }
     const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
     const bool stager = tid < N * kRowB;
     const int sn = stager ? tid / kRowB : 0, sj = tid % kRowB;
     const float *ap = sAP + c * NP;
-    float *car = sCar + c * NP;
-    float *ckr = p.ck + (size_t(b) * dim + d) * size_t(p.nchunks) * N;  // used when live
-    const int nrow = (L + T - 1) / T;
+    float *mus = sMu + c * NP;
+    const int cpseg = p.seg_len / T;
+    const int c_lo = seg * cpseg;
+    const int c_hi = seg == p.nseg - 1 ? p.nchunks : min(p.nchunks, (seg + 1) * cpseg);
+    float dtot = 0.0f;
 
-    for (int ch = 0; ch < nrow; ++ch) {
+    for (int ch = c_hi - 1; ch >= c_lo; --ch) {
         lds_barrier();
-        if (stager) {
-            const int l = ch * T + sj * K;
-            const int cnt = max(0, min(K, L - l));
-            const Tin *q = Bb + size_t(sn) * size_t(p.bc_row) + l;
-            float v[K];
-            load_run<Tin, K>(q, cnt == K && (reinterpret_cast<uintptr_t>(q) & 15u) == 0, cnt, v);
-#pragma unroll
-            for (int i = 0; i < Q; ++i)
-                sB[(sn * Q + i) * kRowB + sj] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-        }
+        if (stager) stage_chunk<Tin, K>(sC, Cb, L, p.bc_row, ch, sn, sj);
         const int l0 = ch * T + j * K;
-        const int cnt = max(0, min(K, L - l0));
-        float xv[K], dv[K], delta[K], w[K];
-        load_run<Tin, K>(xr + l0, cnt == K && (reinterpret_cast<uintptr_t>(xr + l0) & 15u) == 0, cnt, xv);
-        load_run<Tin, K>(dtr + l0, cnt == K && (reinterpret_cast<uintptr_t>(dtr + l0) & 15u) == 0, cnt, dv);
-        float sumd = 0.0f;
+        const int cnt = live ? max(0, min(K, L - l0)) : 0;
+        float delta[K], ds[K], sumd = 0.0f;
+        {
+            float dv[K], gy[K], zv[K];
+            load4<Tin>(dtr + l0, cnt, dv);
+            load4<Tg>(dyr + l0, cnt, gy);
+            if (zr) load4<Tin>(zr + l0, cnt, zv);
 #pragma unroll
-        for (int i = 0; i < K; ++i) {
-            const float dl = softplus(dv[i] + bias);
-            delta[i] = i < cnt ? dl : 0.0f;
-            w[i] = delta[i] * xv[i];
-            sumd += delta[i];
+            for (int i = 0; i < K; ++i) {
+                const bool in = i < cnt;
+                delta[i] = in ? softplus(dv[i] + bias) : 0.0f;
+                const float g = zr ? zv[i] * sigmoid_hw(zv[i]) : 1.0f;
+                ds[i] = in ? gy[i] * g : 0.0f;
+                sumd += delta[i];
+            }
         }
+        dtot += sumd;
         lds_barrier();
-        const float4 *bp = sB + j;
-        const bool second = 2 * ch + 1 < p.nchunks;
+        const float4 *cp = sC + j;
 #pragma unroll 1
         for (int n = 0; n < N; ++n) {
             const float a1 = ap[n];
-            float bv[K];
+            float cv[K], da[K];
+            lds_run<K>(cp + n * Q * kRowB, cv);
 #pragma unroll
-            for (int q = 0; q < Q; ++q) {
-                const float4 v4 = bp[(n * Q + q) * kRowB];
-                bv[4 * q] = v4.x; bv[4 * q + 1] = v4.y; bv[4 * q + 2] = v4.z; bv[4 * q + 3] = v4.w;
-            }
-            float hl = w[0] * bv[0];
+            for (int i = 0; i < K; ++i) da[i] = exp2_hw(delta[i] * a1);
+            float q = ds[K - 1] * cv[K - 1];
 #pragma unroll
-            for (int i = 1; i < K; ++i) hl = __builtin_fmaf(exp2_hw(delta[i] * a1), hl, w[i] * bv[i]);
-            float aa = exp2_hw(sumd * a1);
-            const float cin = car[n];
-            float hend, h = cin;
-            row_scan(aa, hl, hend, h);
-            if (j == kRowB - 1) car[n] = hend;
-            if (live && j == 0) ckr[size_t(2 * ch) * N + n] = cin;
-            if (live && j == kRowB / 2 - 1 && second) ckr[size_t(2 * ch + 1) * N + n] = hend;
+            for (int i = K - 2; i >= 0; --i) q = __builtin_fmaf(da[i + 1], q, ds[i] * cv[i]);
+            float pm = exp2_hw(sumd * a1), qm = da[0] * q, mend, mu = mus[n];
+            row_scan_rev(pm, qm, mend, mu);
+            if (j == 0) mus[n] = mend;
         }
+    }
+    dtot = row_sum(dtot);
+    lds_barrier();
+    if (live && j == 0) {
+        float *ag = p.adj + ((size_t(seg) * gridDim.y + b) * dim + d) * NP;
+#pragma unroll
+        for (int n = 0; n < N; ++n) ag[n] = mus[n];
+        ag[N] = dtot;
     }
 }
 
@@ -399,6 +411,7 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 
     const int tid = threadIdx.x, j = tid & (kRowB - 1), c = tid / kRowB;
     const int b = blockIdx.y, dim = p.dim, L = p.seqlen;
+    const int seg = blockIdx.z;
     const int d = int(blockIdx.x) * kChanB + c;
     const bool live = d < dim;
     const int dc = live ? d : dim - 1;
@@ -417,8 +430,19 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
     for (int s = tid; s < kChanB * NP; s += kThreadsB) {
         const int cc = s / NP, n = s % NP;
         const int dd = min(int(blockIdx.x) * kChanB + cc, dim - 1);
-        sAP[s] = n < N ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
-        sMu[s] = (n < N && p.dhL) ? p.dhL[(size_t(b) * dim + dd) * N + n] : 0.0f;
+        const float a1 = n < N ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
+        sAP[s] = a1;
+        // the adjoint entering this segment from the right: dhL for the last
+        // segment, else the later segments' aggregates composed right to left
+        float mu = (n < N && p.dhL) ? p.dhL[(size_t(b) * dim + dd) * N + n] : 0.0f;
+        if (n < N && seg < p.nseg - 1) {
+            mu = 0.0f;
+            for (int s2 = p.nseg - 1; s2 > seg; --s2) {
+                const float *ag = p.adj + ((size_t(s2) * gridDim.y + b) * dim + dd) * NP;
+                mu = __builtin_fmaf(exp2_hw(a1 * ag[N]), mu, ag[n]);
+            }
+        }
+        sMu[s] = mu;
         sDA[s] = 0.0f;
     }
     const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
@@ -432,10 +456,13 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
     float dskip_acc = 0.0f, dbias_acc = 0.0f;
     // this workgroup's partial copy of dBm / dCm, at batch row b
     const size_t bnl = size_t(p.batch) * N * L;
-    const unsigned wg = blockIdx.x + blockIdx.y * gridDim.x;
+    const unsigned wg = blockIdx.x + (blockIdx.y + blockIdx.z * gridDim.y) * gridDim.x;
     float *part = p.part + size_t(wg % kCopies) * 2 * bnl + size_t(b) * N * L;
+    const int cpseg = p.seg_len / T;
+    const int c_lo = seg * cpseg;
+    const int c_hi = seg == p.nseg - 1 ? p.nchunks : min(p.nchunks, (seg + 1) * cpseg);
 
-    for (int ch = p.nchunks - 1; ch >= 0; --ch) {
+    for (int ch = c_hi - 1; ch >= c_lo; --ch) {
         lds_barrier();
         if (stager) {
             stage_chunk<Tin, K>(sB, Bb, L, p.bc_row, ch, sn, sj);
@@ -639,25 +666,48 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
     }
 }
 
+// Workspace layout (floats): the checkpoints; then the partial dBm/dCm
+// copies, a region the forward's split planes share while the checkpoints
+// are computed; then, for a split shape, the adjoint planes.
+size_t bwd_partials_floats(int batch, int dim, int seqlen, int dstate)
+{
+    const size_t partials = size_t(kCopies) * 2 * size_t(batch) * size_t(dstate) * size_t(seqlen);
+    return std::max(partials, scan_fwd_split_bytes(batch, dim, seqlen, dstate) / sizeof(float));
+}
+
 template <typename Tin, typename Tg, int N>
 hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
 {
     const int nchunks = (a.seqlen + kTB - 1) / kTB;
+    const ScanSplit sp = scan_fwd_split(a.batch, a.dim, a.seqlen);
     float *ck = static_cast<float *>(a.workspace);
-    float *part = ck + size_t(a.batch) * a.dim * nchunks * N;
+    float *part = ck + scan_checkpoint_floats(a.batch, a.dim, a.seqlen, N);
+    float *adj = part + bwd_partials_floats(a.batch, a.dim, a.seqlen, N);
     BwdParams p{a.batch, a.dim, a.seqlen, nchunks,
                 a.row, a.x_b, a.dt_b, a.z_b, a.dy_b, a.dx_b, a.ddt_b, a.dz_b, a.bc_row, a.B_b, a.C_b,
                 a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
                 a.Dskip, a.z, a.h0, a.dy, a.dhL, a.dx, a.ddt, a.dz, a.dBm, a.dCm, a.dA,
-                a.dDskip, a.ddt_bias, a.dh0, ck, part};
+                a.dDskip, a.ddt_bias, a.dh0, ck, part, sp.seg_len, sp.nseg, adj};
+    if (!a.ckpt_given) {
+        // the checkpoints from the forward kernel itself (split like the
+        // forward, its planes in the partial-sum region, no readout)
+        ScanArgs f{a.batch, a.dim, a.seqlen, N, a.in_bf16, 0, 0, a.x, a.dt, a.dt_bias, a.A,
+                   a.Bm, a.Cm, nullptr, nullptr, a.h0, nullptr, nullptr, ck,
+                   a.row, a.x_b, a.dt_b, 0, 0, a.bc_row, a.B_b, a.C_b,
+                   sp.nseg > 1 ? part : nullptr, 1};
+        const hipError_t e = launch_scan_fwd(f, stream);
+        if (e != hipSuccess) return e;
+    }
     const size_t nbc = size_t(a.batch) * N * a.seqlen;
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, stream, part,
                        size_t(kCopies) * 2 * nbc, a.dA, size_t(a.dim) * N, a.dDskip, size_t(a.dim),
                        a.ddt_bias, size_t(a.dim));
-    const dim3 grid((a.dim + kChanB - 1) / kChanB, a.batch);
-    if (!a.ckpt_given)
-        hipLaunchKernelGGL((chunk_states_kernel<Tin, N>), grid, dim3(kThreadsB), 0, stream, p);
-    hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, N>), grid, dim3(kThreadsB), 0, stream, p);
+    const unsigned gx = (a.dim + kChanB - 1) / kChanB;
+    if (sp.nseg > 1)
+        hipLaunchKernelGGL((adjoint_agg_kernel<Tin, Tg, N>), dim3(gx, a.batch, sp.nseg - 1),
+                           dim3(kThreadsB), 0, stream, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, N>), dim3(gx, a.batch, sp.nseg), dim3(kThreadsB),
+                       0, stream, p);
     hipLaunchKernelGGL(bwd_sum_kernel, dim3(1024), dim3(256), 0, stream, part, nbc, a.dBm, a.dCm);
     return hipGetLastError();
 }
@@ -679,12 +729,12 @@ hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream)
 
 size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 {
-    const size_t checkpoints = scan_checkpoint_floats(batch, dim, seqlen, dstate);
-    const size_t partials = size_t(kCopies) * 2 * size_t(batch) * size_t(dstate) * size_t(seqlen);
     // A forward pass that writes the checkpoints keeps its sequence-split
-    // planes where the partial sums go later.
-    return checkpoints * sizeof(float) +
-           std::max(partials * sizeof(float), scan_fwd_split_bytes(batch, dim, seqlen, dstate));
+    // planes where the partial sums go later; the adjoint planes of a split
+    // backward pass (as many as the forward's) follow.
+    return (scan_checkpoint_floats(batch, dim, seqlen, dstate) +
+            bwd_partials_floats(batch, dim, seqlen, dstate)) * sizeof(float) +
+           scan_fwd_split_bytes(batch, dim, seqlen, dstate);
 }
 
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream)

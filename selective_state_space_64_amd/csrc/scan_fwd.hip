@@ -109,11 +109,15 @@ __device__ inline bool aligned16(const void *p)
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-template <typename Tin, typename Tout, int N, int K, bool kZoh, bool kCkpt, bool kAgg>
+template <typename Tin, typename Tout, int N, int K, bool kZoh, bool kCkpt, bool kAgg, bool kOut>
 __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kernel(ScanParams p)
 {
     static_assert(K % 8 == 0, "K must be a multiple of 8");
     static_assert(!(kCkpt && kAgg), "the aggregate pass writes no checkpoints");
+    static_assert(kOut || (kCkpt && !kAgg), "a main pass without output writes checkpoints");
+    // kRead: the readout (Cm, z, the replay, y); off in the aggregate pass and
+    // in the checkpoint-only pass the backward uses
+    constexpr bool kRead = !kAgg && kOut;
     static_assert(N * kRow <= kThreads, "one staging slot per thread");
     constexpr int T = kRow * K;  // timesteps per chunk
     constexpr int Q = K / 4;     // float4 per lane per state
@@ -156,11 +160,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     // Wave-uniform: every row of every streamed tensor starts on a 16-byte
     // boundary, so all runs of a chunk that lies inside the sequence can use
     // unguarded 16-byte vector accesses.
-    const bool rows_vec = aligned16(xw) && aligned16(dtw) && (!zw || aligned16(zw)) &&
-                          aligned16(yw) && aligned16(Bb) && aligned16(Cb) &&
+    const bool rows_vec = aligned16(xw) && aligned16(dtw) && aligned16(Bb) &&
                           (size_t(p.row) * sizeof(Tin)) % 16 == 0 &&
-                          (size_t(p.row) * sizeof(Tout)) % 16 == 0 &&
-                          (size_t(p.bc_row) * sizeof(Tin)) % 16 == 0;
+                          (size_t(p.bc_row) * sizeof(Tin)) % 16 == 0 &&
+                          (!kRead || ((!zw || aligned16(zw)) && aligned16(yw) && aligned16(Cb) &&
+                                      (size_t(p.row) * sizeof(Tout)) % 16 == 0));
     auto chunk_full = [&](int chunk) { return rows_vec && (chunk + 1) * T <= L; };
 
     for (int s = tid; s < kChannels * NP; s += kThreads) {
@@ -255,9 +259,9 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     const int nchunks = (L + T - 1) / T;
     if (stager) {
         stage_load(Bb, 0, stB);
-        if constexpr (!kAgg) stage_load(Cb, 0, stC);
+        if constexpr (kRead) stage_load(Cb, 0, stC);
         stage_store(sB[0], stB);
-        if constexpr (!kAgg) stage_store(sC[0], stC);
+        if constexpr (kRead) stage_store(sC[0], stC);
     }
     xd_load(0);
     lds_barrier();
@@ -321,7 +325,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         // One state: local fold, row scan, carry update and replay.
         auto state_step = [&](int n) {
             float cv[K];
-            if constexpr (!kAgg) {
+            if constexpr (kRead) {
                 load_b(cp, cv);
                 cp += Q * kRow;
             }
@@ -363,7 +367,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             load_b(bp, bv);          // next state's B (one past the end on the last state)
             ap = aptr[n + 1];
             carry = aptr[NP + n + 1];
-            if constexpr (!kAgg) {
+            if constexpr (kRead) {
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
                     h = __builtin_fmaf(dA[i], h, bb[i]);
@@ -381,20 +385,20 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             // Two states per loop trip share the LDS address updates (3.5
             // fewer VALU per state, 1-2 % faster at 128 VGPRs); the other
             // variants would spill at that unroll, so they keep one.
-            constexpr int kSU = (sizeof(Tin) == 2 && N == 16 && !kZoh && !kCkpt && !kAgg) ? 2 : 1;
+            constexpr int kSU = (sizeof(Tin) == 2 && N == 16 && !kZoh && !kCkpt && kRead) ? 2 : 1;
             if (more && stager) {
                 stage_load(Bb, ch + 1, stB);
-                if constexpr (!kAgg) stage_load(Cb, ch + 1, stC);
+                if constexpr (kRead) stage_load(Cb, ch + 1, stC);
             }
 #pragma unroll kSU
             for (int n = 0; n < N1; ++n) state_step(n);
             if (more && stager) {
                 stage_store(sB[buf ^ 1], stB);
-                if constexpr (!kAgg) stage_store(sC[buf ^ 1], stC);
+                if constexpr (kRead) stage_store(sC[buf ^ 1], stC);
             }
 #pragma unroll kSU
             for (int n = N1; n < N2; ++n) state_step(n);
-            if (!kAgg && zw) z_load(ch, yoff);
+            if (kRead && zw) z_load(ch, yoff);
             if (more) xd_load(ch + 1);
 #pragma unroll kSU
             for (int n = N2; n < N; ++n) state_step(n);
@@ -402,24 +406,24 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             // few states: everything is fetched up front
             if (more && stager) {
                 stage_load(Bb, ch + 1, stB);
-                if constexpr (!kAgg) stage_load(Cb, ch + 1, stC);
+                if constexpr (kRead) stage_load(Cb, ch + 1, stC);
             }
-            if (!kAgg && zw) z_load(ch, yoff);
+            if (kRead && zw) z_load(ch, yoff);
             if (more) xd_load(ch + 1);
 #pragma unroll 1
             for (int n = 0; n < N; ++n) state_step(n);
             if (more && stager) {
                 stage_store(sB[buf ^ 1], stB);
-                if constexpr (!kAgg) stage_store(sC[buf ^ 1], stC);
+                if constexpr (kRead) stage_store(sC[buf ^ 1], stC);
             }
         }
 
         if constexpr (kAgg) dtot += sumd;
-        if (!kAgg && zw) {
+        if (kRead && zw) {
 #pragma unroll
             for (int i = 0; i < K; ++i) yv[i] *= silu(decode_raw_at<Tin, K>(rz, i));
         }
-        if (!kAgg && live) {
+        if (kRead && live) {
             Tout *yr = at(yw, uint32_t((lane_row + uint32_t(l0)) * sizeof(Tout)));
             if (full)
                 store_y<Tout, K>(yr, true, K, yv);
@@ -457,20 +461,29 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
     const unsigned gx = (a.dim + kChannels - 1) / kChannels;
     if (sp.nseg > 1) {
         // every segment but the last: its end state and Delta sum
-        hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, true>),
+        hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, true, true>),
                            dim3(gx, a.batch, sp.nseg - 1), dim3(kThreads), 0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const dim3 grid(gx, a.batch, sp.nseg);
+    if (a.ckpt_only) {
+        // no output: one instantiation (fp32 Tout) serves every caller
+        if constexpr (!kZoh && sizeof(Tout) == 4) {
+            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true, false, false>), grid,
+                               dim3(kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
     if constexpr (!kZoh) {
         if (a.ck) {
-            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true, false>), grid,
+            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true, false, true>), grid,
                                dim3(kThreads), 0, stream, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, false>), grid, dim3(kThreads),
+    hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, false, true>), grid, dim3(kThreads),
                        0, stream, p);
     return hipGetLastError();
 }

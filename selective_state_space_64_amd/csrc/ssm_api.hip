@@ -188,7 +188,7 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
     ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
                     (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,
                     ckpt ? ws : nullptr,
-                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], bc_row, bc_b[0], bc_b[1], agg};
+                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], bc_row, bc_b[0], bc_b[1], agg, 0};
     const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

@@ -24,6 +24,8 @@ struct ScanArgs {
     // Workspace of the sequence split (scan_fwd_split_bytes), or NULL when
     // the shape is not split.
     float *agg;
+    // Checkpoints only (for the backward pass): no readout, no y, no hL.
+    int ckpt_only;
 };
 
 // Sequence split of the forward scan: segments of seg_len steps (a multiple

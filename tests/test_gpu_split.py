@@ -179,3 +179,43 @@ def test_split_workspace_given_and_rejected():
     assert e.value.status == 7
     torch.cuda.synchronize()
     assert bool((y0 == 7.0).all())
+
+
+# ------------------------------------------------------------ backward pass
+SPLIT_BWD = [
+    # (batch, dim, N, L, dtype): split by the library's rule
+    (1, 16, 16, 4096, "f32"), (2, 3, 8, 3001, "bf16"), (1, 20, 16, 5000, "f32"),
+    (1, 5, 4, 10000, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SPLIT_BWD, ids=lambda s: "b%d_d%d_N%d_L%d_%s" % s)
+def test_split_bwd_full_tensor(shape):
+    """The backward pass at split shapes: checkpoints from the split forward
+    kernel, adjoint aggregates of the later segments, every segment's reverse
+    pass at once; every gradient against the oracle, with h0, dhL and the gate."""
+    import oracle
+    batch, dim, N, L, dt = shape
+    print("split bwd", shape, flush=True)
+    assert ssm.lib().ssm_scan_fwd_workspace_bytes(batch, dim, L, N) > 0
+    inp = synth.make_inputs(workload("split_bwd", batch, dim, N, L, dt, seed=28), with_h0=True)
+    rng = np.random.default_rng(6)
+    dyv = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    dhL = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    g = ssm.ssm_scan_bwd(to_dev(inp, "x"), to_dev(inp, "dt"), to_dev(inp, "A"), to_dev(inp, "Bm"),
+                         to_dev(inp, "Cm"), torch.from_numpy(dyv).cuda(),
+                         dt_bias=to_dev(inp, "dt_bias"), Dskip=to_dev(inp, "Dskip"),
+                         z=to_dev(inp, "z"), h0=torch.from_numpy(inp.h0.astype(np.float32)).cuda(),
+                         dhL=torch.from_numpy(dhL).cuda())
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(inp.values("x"), inp.values("dt"), inp.A.astype(np.float64),
+                        inp.values("Bm"), inp.values("Cm"), dyv.astype(np.float64),
+                        dt_bias=inp.dt_bias.astype(np.float64), Dskip=inp.Dskip.astype(np.float64),
+                        z=inp.values("z"), h0=inp.h0.astype(np.float64),
+                        dhL=dhL.astype(np.float64))
+    for k in ("dx", "ddt", "dz", "dBm", "dCm", "dh0"):
+        e = rel_err(g[k].cpu().numpy(), r[k])
+        assert e <= 1e-4, (shape, k, e)
+    for k in ("dA", "dDskip", "ddt_bias"):
+        e = rel_err(g[k].cpu().numpy()[None], r[k][None])
+        assert e <= 1e-4, (shape, k, e)
