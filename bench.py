@@ -71,7 +71,7 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-SCAN_KERNEL = "scan_fwd_kernel<ssm::bf16_t, float, 16, 8, false, false, false>"
+SCAN_KERNEL = "scan_fwd_kernel<ssm::bf16_t, float, 16, 8, false, false, false, true>"
 
 
 def ingest_counters(fetch_dir, write_dir, copyf_dir, copyw_dir, copy_mib=256, workload=None):
