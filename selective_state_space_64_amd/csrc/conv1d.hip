@@ -13,9 +13,10 @@
 //
 // The forward pass reads each input once and writes each output once: it is
 // bound by HBM bandwidth, not arithmetic (W fma + one silu per output).  A
-// lane owns 8 consecutive outputs of one row; consecutive lanes own
-// consecutive runs of the same row, so a wave reads and writes contiguous
-// 1 KB (bf16) stretches with 16-byte vector accesses.  The W-1 inputs before a
+// lane owns 16 consecutive outputs of one row (two 16-byte vectors of bf16
+// in flight per lane; 8 measured 5 % slower, 32 much slower); consecutive
+// lanes own consecutive runs of the same row, so a wave reads and writes
+// contiguous 2 KB (bf16) stretches with 16-byte vector accesses.  The W-1 inputs before a
 // run are the previous lane's last inputs (a lane shuffle, so every input is
 // read from memory once), the conv state for a row's first run, or, for lane 0
 // of a wave, W-1 element loads.
@@ -27,7 +28,11 @@
 namespace ssm {
 namespace {
 
-constexpr int kRun = 8;          // outputs per lane
+#ifndef SSM_CONV_RUN
+#define SSM_CONV_RUN 16
+#endif
+constexpr int kRun = SSM_CONV_RUN;  // outputs per lane (a multiple of 8)
+static_assert(kRun % 8 == 0, "runs are whole 16-byte vectors of bf16 and fp32");
 constexpr int kConvThreads = 256;
 
 struct ConvParams {
@@ -79,8 +84,9 @@ __device__ inline void store_run<float>(float *p, bool vec, int count, const flo
 {
     if (vec) {
         f32x4 *q = reinterpret_cast<f32x4 *>(p);
-        q[0] = f32x4{v[0], v[1], v[2], v[3]};
-        q[1] = f32x4{v[4], v[5], v[6], v[7]};
+#pragma unroll
+        for (int i = 0; i < kRun / 4; ++i)
+            q[i] = f32x4{v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
     } else {
 #pragma unroll
         for (int i = 0; i < kRun; ++i)
@@ -92,8 +98,13 @@ template <>
 __device__ inline void store_run<bf16_t>(bf16_t *p, bool vec, int count, const float *v)
 {
     if (vec) {
-        *reinterpret_cast<u32x4 *>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        u32x4 *q = reinterpret_cast<u32x4 *>(p);
+#pragma unroll
+        for (int i = 0; i < kRun / 8; ++i) {
+            const float *w = v + 8 * i;
+            q[i] = u32x4{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]),
+                         pack_bf16x2(w[4], w[5]), pack_bf16x2(w[6], w[7])};
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < kRun; ++i)
