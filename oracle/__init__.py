@@ -46,6 +46,8 @@ MUTANTS = {
     24: "backward: gate derivative sigmoid(z) instead of silu'(z)",
     25: "backward: softplus derivative taken as softplus",
     26: "backward: C gradient paired with the previous state",
+    27: "ZOH backward: Delta derivative of B-bar taken from the Delta B form",
+    28: "ZOH backward: A gradient without the B-bar term",
 }
 
 _dp = ctypes.POINTER(ctypes.c_double)
@@ -84,7 +86,7 @@ class Oracle:
         lib.ssm_oracle_conv1d_update_f64.restype = ctypes.c_int
         lib.ssm_oracle_conv1d_update_f64.argtypes = [ctypes.c_int] * 4 + [_dp] * 5 + [ctypes.c_int]
         lib.ssm_oracle_scan_bwd_f64.restype = ctypes.c_int
-        lib.ssm_oracle_scan_bwd_f64.argtypes = [ctypes.c_int] * 4 + [_dp] * 20 + [ctypes.c_int]
+        lib.ssm_oracle_scan_bwd_f64.argtypes = [ctypes.c_int] * 5 + [_dp] * 20 + [ctypes.c_int]
         lib.ssm_oracle_mutant_id.restype = ctypes.c_int
         self._lib = lib
         self.mutant = lib.ssm_oracle_mutant_id()
@@ -140,9 +142,9 @@ class Oracle:
         return y, state
 
     def scan_bwd(self, x, dt, A, Bm, Cm, dy, dt_bias=None, Dskip=None, z=None, h0=None,
-                 dhL=None, threads=None):
-        """Vector-Jacobian products of scan_fwd (Delta*B form) for the loss
-        sum(dy * y) + sum(dhL * hL).  Returns a dict with dx, ddt, dz (None
+                 dhL=None, zoh=False, threads=None):
+        """Vector-Jacobian products of scan_fwd (Delta*B form, or the exact ZOH
+        form with zoh=True) for the loss sum(dy * y) + sum(dhL * hL).  Returns a dict with dx, ddt, dz (None
         without z), dBm, dCm, dA, dDskip, ddt_bias and dh0."""
         x = np.asarray(x)
         batch, dim, L = x.shape
@@ -166,7 +168,7 @@ class Oracle:
         g["dz"] = np.empty((batch, dim, L), np.float64) if z is not None else None
         nt = threads or os.cpu_count() or 1
         rc = self._lib.ssm_oracle_scan_bwd_f64(
-            batch, dim, L, N, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm),
+            batch, dim, L, N, 1 if zoh else 0, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(Bm), _ptr(Cm),
             _ptr(Dskip), _ptr(z), _ptr(h0), _ptr(dy), _ptr(dhL), _ptr(g["dx"]), _ptr(g["ddt"]),
             _ptr(g["ddt_bias"]), _ptr(g["dA"]), _ptr(g["dBm"]), _ptr(g["dCm"]), _ptr(g["dDskip"]),
             _ptr(g["dz"]), _ptr(g["dh0"]), int(nt))

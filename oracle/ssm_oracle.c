@@ -421,10 +421,10 @@ int ssm_oracle_conv1d_update_f64(int batch, int dim, int width, int act, double 
  *   dA                   [dim][N]         (summed over batch and time)
  *   dDskip, ddt_bias     [dim]            (summed over batch and time)
  *   dh0                  [batch][dim][N]
- * Only the Delta B form of B-bar is differentiated here.
+ * Both forms of B-bar are differentiated (zoh != 0: the exact ZOH form).
  * ---------------------------------------------------------------------- */
 typedef struct {
-    int batch, dim, seqlen, dstate;
+    int batch, dim, seqlen, dstate, zoh;
     const double *x, *dt, *dt_bias, *A, *Bm, *Cm, *Dskip, *z, *h0, *dy, *dhL;
     double *dx, *ddt, *dz, *dh0;
 } bwd_args;
@@ -435,6 +435,27 @@ typedef struct {
 } bwd_acc;
 
 static double sigmoid(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/* The exact ZOH input factor g(Delta, A) = (exp(Delta A) - 1) / A ([MAMBA]
+ * Method, diagonal A; g = Delta at A = 0), so that B-bar = g B.  Its
+ * derivatives: dg/dDelta = exp(Delta A); dg/dA = Delta^2 psi(Delta A) with
+ * psi(t) = (t e^t - (e^t - 1)) / t^2 = sum_m (m + 1) t^m / (m + 2)!, taken
+ * from the series where the closed form cancels (|t| < 1). */
+static double zoh_g(double delta, double an)
+{
+    return an != 0.0 ? expm1(delta * an) / an : delta;
+}
+
+static double zoh_psi(double t)
+{
+    if (fabs(t) >= 1.0) return (t * exp(t) - expm1(t)) / (t * t);
+    double sum = 0.0, term = 0.5; /* m = 0: 1 / 2! */
+    for (int m = 0; m < 40; ++m) {
+        sum += term;
+        term *= t * (double)(m + 2) / ((double)(m + 1) * (double)(m + 3)); /* (m+2)/(m+3)! t^(m+1) */
+    }
+    return sum;
+}
 
 static int bwd_row(const bwd_args *a, const bwd_acc *acc, int b, int d)
 {
@@ -458,8 +479,9 @@ static int bwd_row(const bwd_args *a, const bwd_acc *acc, int b, int d)
         const double delta = softplus(dt[t] + bias);
         double acc_s = 0.0;
         for (int n = 0; n < N; ++n) {
+            const double g = a->zoh ? zoh_g(delta, Arow[n]) : delta;
             const double h = exp(delta * Arow[n]) * hs[(size_t)t * N + n] +
-                             delta * Bm[(size_t)n * L + t] * x[t];
+                             g * Bm[(size_t)n * L + t] * x[t];
             hs[(size_t)(t + 1) * N + n] = h;
             acc_s += Cm[(size_t)n * L + t] * h;
         }
@@ -496,6 +518,13 @@ static int bwd_row(const bwd_args *a, const bwd_acc *acc, int b, int d)
             const double h = hs[(size_t)(t + 1) * N + n];
             const double hp = hs[(size_t)t * N + n];
             const double abar = exp(delta * An);
+            /* B-bar = g B: g = Delta (dg/dDelta = 1, dg/dA = 0), or the ZOH g */
+            const double g = a->zoh ? zoh_g(delta, An) : delta;
+            double dg_dd = a->zoh ? abar : 1.0;
+            const double dg_da = a->zoh ? delta * delta * zoh_psi(delta * An) : 0.0;
+#if ORACLE_MUTANT == 27
+            if (a->zoh) dg_dd = 1.0; /* planted: ZOH Delta derivative of the Delta B form */
+#endif
             lam[n] += ds * cn;                                   /* readout y_t <- C h_t */
 #if ORACLE_MUTANT == 26
             acc->dCm[((size_t)b * N + n) * L + t] += ds * hp;    /* planted: C meets h_{t-1} */
@@ -503,17 +532,19 @@ static int bwd_row(const bwd_args *a, const bwd_acc *acc, int b, int d)
             acc->dCm[((size_t)b * N + n) * L + t] += ds * h;
 #endif
 #if ORACLE_MUTANT == 20
-            ddelta += lam[n] * bn * x[t];                        /* planted: no A-bar term */
+            ddelta += lam[n] * dg_dd * bn * x[t];                /* planted: no A-bar term */
 #else
-            ddelta += lam[n] * (An * abar * hp + bn * x[t]);     /* h_t = abar h_{t-1} + delta B x */
+            ddelta += lam[n] * (An * abar * hp + dg_dd * bn * x[t]); /* h_t = abar h_{t-1} + g B x */
 #endif
 #if ORACLE_MUTANT == 21
             acc->dA[(size_t)d * N + n] += lam[n] * abar * hp;    /* planted: Delta factor dropped */
+#elif ORACLE_MUTANT == 28
+            acc->dA[(size_t)d * N + n] += lam[n] * delta * abar * hp; /* planted: ZOH term dropped */
 #else
-            acc->dA[(size_t)d * N + n] += lam[n] * delta * abar * hp;
+            acc->dA[(size_t)d * N + n] += lam[n] * (delta * abar * hp + dg_da * bn * x[t]);
 #endif
-            acc->dBm[((size_t)b * N + n) * L + t] += lam[n] * delta * x[t];
-            dxt += lam[n] * delta * bn;
+            acc->dBm[((size_t)b * N + n) * L + t] += lam[n] * g * x[t];
+            dxt += lam[n] * g * bn;
 #if ORACLE_MUTANT != 22
             lam[n] *= abar;                                      /* -> d l / d h_{t-1} */
 #endif
@@ -559,7 +590,7 @@ static void *bwd_rows(void *p)
  * per-thread buffers and added in thread order, so results do not depend on
  * scheduling.  Returns 0, -1 on bad arguments, -2 on allocation failure.
  */
-int ssm_oracle_scan_bwd_f64(int batch, int dim, int seqlen, int dstate,
+int ssm_oracle_scan_bwd_f64(int batch, int dim, int seqlen, int dstate, int zoh,
                             const double *x, const double *dt, const double *dt_bias,
                             const double *A, const double *Bm, const double *Cm,
                             const double *Dskip, const double *z, const double *h0,
@@ -572,8 +603,8 @@ int ssm_oracle_scan_bwd_f64(int batch, int dim, int seqlen, int dstate,
         !dCm || !dDskip)
         return -1;
     if (z && !dz) return -1;
-    bwd_args a = {batch, dim, seqlen, dstate, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy, dhL,
-                  dx, ddt, dz, dh0};
+    bwd_args a = {batch, dim, seqlen, dstate, zoh ? 1 : 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0,
+                  dy, dhL, dx, ddt, dz, dh0};
     const long rows = (long)batch * dim;
     const size_t nbc = (size_t)batch * dstate * seqlen, na = (size_t)dim * dstate;
     if (nthreads < 1) nthreads = 1;

@@ -404,8 +404,8 @@ def _bwd_problem(seed, batch=2, dim=3, L=23, N=4):
     return rng, p, dy, dhL
 
 
-def _loss(o, p, dy, dhL):
-    y, hL = o.scan_fwd(**p)
+def _loss(o, p, dy, dhL, zoh=False):
+    y, hL = o.scan_fwd(**p, zoh=zoh)
     return float((dy * y).sum() + (dhL * hL).sum())
 
 
@@ -441,6 +441,36 @@ def pin_bwd_finite_differences(o):
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
 
 
+def pin_bwd_zoh(o):
+    """The exact ZOH form ([MAMBA] Method): the same exact directional
+    derivatives for the inputs the loss is affine in, and central
+    differences for the rest, through the ZOH forward oracle; one channel
+    has A = 0 (B-bar = Delta B there, and its A gradient takes the series
+    limit Delta^2 / 2)."""
+    rng, p, dy, dhL = _bwd_problem(44)
+    p["A"][1, 2] = 0.0
+    g = o.scan_bwd(dy=dy, dhL=dhL, zoh=True, **p)
+    for name, gname in (("x", "dx"), ("h0", "dh0"), ("Bm", "dBm"), ("Cm", "dCm")):
+        v = rng.standard_normal(p[name].shape)
+        lhs = (_loss(o, {**p, name: v}, dy, dhL, True)
+               - _loss(o, {**p, name: np.zeros_like(v)}, dy, dhL, True))
+        rhs = float((g[gname] * v).sum())
+        assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs)), (name, lhs, rhs)
+    eps = 1e-6
+    for name, gname in (("dt", "ddt"), ("dt_bias", "ddt_bias"), ("A", "dA"), ("z", "dz")):
+        v = rng.standard_normal(p[name].shape)
+        fd = (_loss(o, {**p, name: p[name] + eps * v}, dy, dhL, True)
+              - _loss(o, {**p, name: p[name] - eps * v}, dy, dhL, True)) / (2 * eps)
+        an = float((g[gname] * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+    # the A = 0 entry alone, where the forward switches to its limit branch
+    v = np.zeros_like(p["A"])
+    v[1, 2] = 1.0
+    fd = (_loss(o, {**p, "A": p["A"] + eps * v}, dy, dhL, True)
+          - _loss(o, {**p, "A": p["A"] - eps * v}, dy, dhL, True)) / (2 * eps)
+    assert abs(fd - g["dA"][1, 2]) <= 1e-6 * max(1.0, abs(fd)), (fd, g["dA"][1, 2])
+
+
 def pin_bwd_no_gate_no_state(o):
     """Without gate, skip, bias and h0 the same identities hold, and the
     returned dh0 is the adjoint at t = -1 (finite differences through h0)."""
@@ -465,7 +495,7 @@ PINS = [pin_hand_examples, pin_lti_convolution, pin_small_delta, pin_large_delta
         pin_bracketings, pin_split_resume, pin_decode_equals_scan, pin_linearity,
         pin_equivariance, pin_softplus_silu, pin_conv_hand_examples, pin_conv_library,
         pin_conv_impulse, pin_conv_split_resume, pin_conv_decode_equals_prefill,
-        pin_bwd_linear_inputs, pin_bwd_finite_differences, pin_bwd_no_gate_no_state]
+        pin_bwd_linear_inputs, pin_bwd_finite_differences, pin_bwd_zoh, pin_bwd_no_gate_no_state]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
