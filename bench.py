@@ -310,9 +310,11 @@ BWD_SLOTS_PER_ROW_STEP = 40  # softplus 9, sigmoid(u) 9, silu + silu' 14, gradie
 
 
 def bench_bwd(torch, ssm, wl, t, launches=10):
-    """Backward pass (all launches of one ssm_scan_bwd call: zero-fill,
-    chunk states, reverse pass, sum of partial copies) on the layer,
-    dy ~ N(0, 1) fp32, gradients fp32, outputs and workspace preallocated."""
+    """Backward pass (all launches of one ssm_scan_bwd call: checkpoint
+    recompute, zero-fill, reverse pass, sum of partial copies) on the layer,
+    dy ~ N(0, 1) fp32, gradients fp32, outputs and workspace preallocated;
+    also in training order after a forward that writes the checkpoints, and
+    for the exact zero-order-hold form."""
     dy = torch.randn((wl.batch, wl.dim, wl.seqlen), device="cuda")
     ws = torch.empty(ssm.lib().ssm_scan_bwd_workspace_bytes(wl.batch, wl.dim, wl.seqlen, wl.dstate),
                      dtype=torch.uint8, device="cuda")
@@ -366,6 +368,7 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
     fwd_ckpt_ms = timed(fwd_ckpt)
     fwd_ckpt()
     bwd_ckpt_ms = timed(lambda: call(2))
+    zoh_ms = timed(lambda: call(1))  # SSM_FLAG_ZOH_B, checkpoints recomputed
     elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
     slots = elems * BWD_SLOTS_PER_ELEM + wl.batch * wl.dim * wl.seqlen * BWD_SLOTS_PER_ROW_STEP
     achieved = slots / (ms * 1e-3) / 1e12
@@ -376,9 +379,11 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
                          "model": "fp32 VALU issue slots (transcendental = 4), %.2f slots/element"
                                   % (slots / elems)},
             "with_forward_checkpoints": {"forward_ms": fwd_ckpt_ms, "backward_ms": bwd_ckpt_ms},
-            "note": "zero-fill + chunk-state recompute + reverse pass + partial-copy sum; "
+            "zoh_ms_mean": zoh_ms,
+            "note": "checkpoint recompute + zero-fill + reverse pass + partial-copy sum; "
                     "with_forward_checkpoints: the forward writes the checkpoints and the "
-                    "backward skips its recomputation pass"}
+                    "backward skips its recomputation pass; zoh: the exact zero-order-hold "
+                    "form of B-bar"}
 
 
 def main():

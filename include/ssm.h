@@ -77,7 +77,7 @@ typedef enum {
  * B-bar = (Delta A)^-1 (exp(Delta A) - 1) Delta B, instead of Delta B. */
 #define SSM_FLAG_ZOH_B 0x1u
 
-/* flags bit 1 (ssm_scan_fwd with the Delta B form only, and ssm_scan_bwd):
+/* flags bit 1 (ssm_scan_fwd, with either form of B-bar, and ssm_scan_bwd):
  * checkpoints for the backward pass.  The backward recomputes the scan's
  * states from the state entering every 64-step chunk ("Hardware-aware state
  * expansion": states are recomputed, not stored).  With this bit,

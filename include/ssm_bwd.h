@@ -7,11 +7,11 @@
  * in and read back from HBM.  ssm_scan_bwd returns the gradients of
  *     l = sum(dy * y) + sum(dhL * hL)
  * with respect to every input of ssm_scan_fwd (see ssm.h for the forward map
- * and layouts), for the Delta * B form of B-bar (the exact zero-order-hold
- * form has no backward here: SSM_FLAG_ZOH_B is SSM_ERR_UNSUPPORTED).  flags
- * may hold SSM_FLAG_CHECKPOINTS: `workspace` then already holds the
- * checkpoints that ssm_scan_fwd wrote with that flag for the same x, dt,
- * dt_bias, A, Bm and h0, and the recomputation pass is skipped.
+ * and layouts), for the Delta * B form of B-bar or, with SSM_FLAG_ZOH_B, the
+ * exact zero-order-hold form.  flags may also hold SSM_FLAG_CHECKPOINTS:
+ * `workspace` then already holds the checkpoints that ssm_scan_fwd wrote
+ * with that flag for the same x, dt, dt_bias, A, Bm, h0 and form of B-bar,
+ * and the recomputation pass is skipped.
  *
  * Per (b, d), with u_t = dt_t + dt_bias, Delta_t = softplus(u_t),
  * A-bar_t = exp(Delta_t A), s_t = C_t . h_t + Dskip x_t, ds_t = dy_t silu(z_t):
@@ -23,6 +23,11 @@
  *     dA[d,n] = sum_{b,t} lambda_t Delta_t A-bar_t h_{t-1}
  *     dDskip[d] = sum_{b,t} ds_t x_t,  ddt_bias[d] = sum_{b,t} ddt_t
  *     dh0 = A-bar_0 lambda_0
+ * With SSM_FLAG_ZOH_B the input term Delta_t B_t x_t becomes g_t B_t x_t,
+ * g = (exp(Delta A) - 1) / A (Delta at A = 0; "Method" section): Delta_t is
+ * replaced by g_t in dx and dBm, the B_t x_t term of ddt gains the factor
+ * dg/dDelta = A-bar_t, and dA gains sum_{b,t} lambda_t B_t x_t dg/dA with
+ * dg/dA = Delta^2 psi(Delta A), psi(u) = (u e^u - (e^u - 1)) / u^2.
  *
  * Conventions are those of ssm.h (caller-owned device pointers, densely
  * packed, nothing allocated; argument errors return before any launch and

@@ -290,9 +290,9 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
 
 def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=None, dhL=None,
                  grad_dtype=torch.float32, workspace=None, checkpoints_in_workspace=False,
-                 dx=None, ddt=None, dz=None, stream=None):
+                 dx=None, ddt=None, dz=None, zoh=False, stream=None):
     """Gradients of sum(dy * y) + sum(dhL * hL) through ssm_scan_fwd (Delta*B
-    form).  Returns a dict: dx, ddt, dz (None without z) in grad_dtype; dBm,
+    form, or the exact zero-order-hold form with zoh=True).  Returns a dict: dx, ddt, dz (None without z) in grad_dtype; dBm,
     dCm, dA, dDskip, ddt_bias, dh0 in fp32 (dDskip / ddt_bias / dh0 are
     computed for every call).  checkpoints_in_workspace=True: `workspace`
     holds the checkpoints a forward call wrote (SSM_FLAG_CHECKPOINTS).
@@ -341,6 +341,8 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
         _ptr(g["ddt_bias"], "ddt_bias"), _ptr(g["dh0"], "dh0"),
     ]
     flags = SSM_FLAG_CHECKPOINTS if checkpoints_in_workspace else 0
+    if zoh:
+        flags |= SSM_FLAG_ZOH_B
     st = lib().ssm_scan_bwd_strided(batch, dim, L, N, _dtype_code(ind), flags, *args,
                                     _dtype_code(grad_dtype), *gargs, _ptr(workspace, "workspace"),
                                     workspace.numel() * workspace.element_size(),

@@ -395,7 +395,9 @@ __global__ __launch_bounds__(kThreadsB) void adjoint_agg_kernel(BwdParams p)
 }
 
 // 3 waves per SIMD: the two chains of a state pair need ~150 VGPRs.
-template <typename Tin, typename Tg, int N>
+// kZoh: the exact zero-order-hold input term g B x, g = phi(Delta A) Delta,
+// with dg/dDelta = A-bar and dg/dA = Delta^2 psi(Delta A).
+template <typename Tin, typename Tg, int N, bool kZoh>
 __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 {
     constexpr int K = kKB, T = kTB, Q = K / 4, NP = N + 1;
@@ -481,6 +483,7 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
         const int cnt = live ? max(0, min(K, L - l0)) : 0;
         // per step: sb = sum_n lambda B, sah = sum_n lambda A A-bar h_{t-1}
         float xv[K], delta[K], w[K], ds[K], sacc[K], sb[K], sah[K], sgu[K], gzf[K];
+        [[maybe_unused]] float invd[K], sba[K];  // exact ZOH: 1/Delta, sum_n lambda A-bar B
         float sumd = 0.0f;
         {
             float dv[K], gy[K], zv[K];
@@ -507,6 +510,10 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
                 sacc[i] = skip * xv[i];
                 sb[i] = 0.0f;
                 sah[i] = 0.0f;
+                if constexpr (kZoh) {
+                    invd[i] = in ? rcp_hw(dl) : 0.0f;
+                    sba[i] = 0.0f;
+                }
                 sumd += delta[i];
                 dskip_acc = __builtin_fmaf(ds[i], xv[i], dskip_acc);
             }
@@ -515,11 +522,17 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 
         const float4 *bp = sB + j, *cp = sC + j;
         static_assert(N % 2 == 0 || N == 1, "states are processed in pairs");
-        constexpr int G = N >= 2 ? 2 : 1;  // states in flight per iteration
+        // states in flight per iteration (the exact-ZOH terms need the
+        // registers of the second chain: with two it spills)
+        constexpr int G = (N >= 2 && !kZoh) ? 2 : 1;
 #pragma unroll 1
         for (int n = 0; n < N; n += G) {
             const int pb = (n / G) & 1;  // sP buffer of this pair
             float a1[G], An[G], bv[G][K], cv[G][K], da[G][K], hh[G][K], ptot[G], hl[G];
+            // bg: B times the input factor's Delta-free part (phi(Delta A) for
+            // the exact ZOH form, 1 otherwise), so B-bar x = w bg, w = Delta x
+            [[maybe_unused]] float ph[G][K], inva[G];
+            float bg[G][K];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 a1[g] = ap[n + g];
@@ -528,9 +541,20 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
                 lds_run<K>(cp + (n + g) * Q * kRowB, cv[g]);
 #pragma unroll
                 for (int i = 0; i < K; ++i) da[g][i] = exp2_hw(delta[i] * a1[g]);
-                hl[g] = w[0] * bv[g][0];
+                if constexpr (kZoh) {
+                    inva[g] = rcp_hw(a1[g]) * kLog2e;  // 1/A
 #pragma unroll
-                for (int i = 1; i < K; ++i) hl[g] = __builtin_fmaf(da[g][i], hl[g], w[i] * bv[g][i]);
+                    for (int i = 0; i < K; ++i) {
+                        ph[g][i] = phi_zoh(delta[i] * An[g], da[g][i], invd[i] * inva[g]);
+                        bg[g][i] = bv[g][i] * ph[g][i];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < K; ++i) bg[g][i] = bv[g][i];
+                }
+                hl[g] = w[0] * bg[g][0];
+#pragma unroll
+                for (int i = 1; i < K; ++i) hl[g] = __builtin_fmaf(da[g][i], hl[g], w[i] * bg[g][i]);
                 ptot[g] = exp2_hw(sumd * a1[g]);
             }
             // forward states of this chunk, from the checkpoint
@@ -549,7 +573,7 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
             for (int g = 0; g < G; ++g) {
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
-                    h[g] = __builtin_fmaf(da[g][i], h[g], w[i] * bv[g][i]);
+                    h[g] = __builtin_fmaf(da[g][i], h[g], w[i] * bg[g][i]);
                     hh[g][i] = h[g];
                     sacc[i] = __builtin_fmaf(cv[g][i], h[g], sacc[i]);
                 }
@@ -587,12 +611,22 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 #pragma unroll
                 for (int i = K - 1; i >= 0; --i) {
                     lam = __builtin_fmaf(ds[i], cv[g][i], lam);
-                    const float hpa = __builtin_fmaf(-w[i], bv[g][i], hh[g][i]);  // A-bar h_{t-1}
+                    const float hpa = __builtin_fmaf(-w[i], bg[g][i], hh[g][i]);  // A-bar h_{t-1}
                     const float lh = lam * hpa;
                     sah[i] = __builtin_fmaf(An[g], lh, sah[i]);
                     dap[g] = __builtin_fmaf(delta[i], lh, dap[g]);
-                    sb[i] = __builtin_fmaf(lam, bv[g][i], sb[i]);
-                    gbv[i] = lam * w[i];
+                    sb[i] = __builtin_fmaf(lam, bg[g][i], sb[i]);
+                    if constexpr (kZoh) {
+                        // dg/dDelta = A-bar (the Delta gradient), dg/dA = Delta^2 psi
+                        const float ps =
+                            psi_zoh(delta[i] * An[g], da[g][i], invd[i] * inva[g]);
+                        sba[i] = __builtin_fmaf(lam * da[g][i], bv[g][i], sba[i]);
+                        dap[g] = __builtin_fmaf(lam * bv[g][i] * xv[i], delta[i] * delta[i] * ps,
+                                                dap[g]);
+                        gbv[i] = lam * w[i] * ph[g][i];
+                    } else {
+                        gbv[i] = lam * w[i];
+                    }
                     gcv[i] = ds[i] * hh[g][i];
                     lam *= da[g][i];
                 }
@@ -639,7 +673,11 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 gx[i] = __builtin_fmaf(delta[i], sb[i], skip * ds[i]);
-                gdt[i] = __builtin_fmaf(xv[i], sb[i], sah[i]) * sgu[i];
+                if constexpr (kZoh) {
+                    gdt[i] = __builtin_fmaf(xv[i], sba[i], sah[i]) * sgu[i];
+                } else {
+                    gdt[i] = __builtin_fmaf(xv[i], sb[i], sah[i]) * sgu[i];
+                }
                 dbias_acc += i < cnt ? gdt[i] : 0.0f;
                 gz[i] = gzf[i] * sacc[i];
             }
@@ -675,7 +713,7 @@ size_t bwd_partials_floats(int batch, int dim, int seqlen, int dstate)
     return std::max(partials, scan_fwd_split_bytes(batch, dim, seqlen, dstate) / sizeof(float));
 }
 
-template <typename Tin, typename Tg, int N>
+template <typename Tin, typename Tg, int N, bool kZoh>
 hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
 {
     const int nchunks = (a.seqlen + kTB - 1) / kTB;
@@ -691,7 +729,7 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
     if (!a.ckpt_given) {
         // the checkpoints from the forward kernel itself (split like the
         // forward, its planes in the partial-sum region, no readout)
-        ScanArgs f{a.batch, a.dim, a.seqlen, N, a.in_bf16, 0, 0, a.x, a.dt, a.dt_bias, a.A,
+        ScanArgs f{a.batch, a.dim, a.seqlen, N, a.in_bf16, 0, kZoh ? 1 : 0, a.x, a.dt, a.dt_bias, a.A,
                    a.Bm, a.Cm, nullptr, nullptr, a.h0, nullptr, nullptr, ck,
                    a.row, a.x_b, a.dt_b, 0, 0, a.bc_row, a.B_b, a.C_b,
                    sp.nseg > 1 ? part : nullptr, 1};
@@ -706,23 +744,29 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
     if (sp.nseg > 1)
         hipLaunchKernelGGL((adjoint_agg_kernel<Tin, Tg, N>), dim3(gx, a.batch, sp.nseg - 1),
                            dim3(kThreadsB), 0, stream, p);
-    hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, N>), dim3(gx, a.batch, sp.nseg), dim3(kThreadsB),
-                       0, stream, p);
+    hipLaunchKernelGGL((scan_bwd_kernel<Tin, Tg, N, kZoh>), dim3(gx, a.batch, sp.nseg),
+                       dim3(kThreadsB), 0, stream, p);
     hipLaunchKernelGGL(bwd_sum_kernel, dim3(1024), dim3(256), 0, stream, part, nbc, a.dBm, a.dCm);
     return hipGetLastError();
 }
 
-template <typename Tin, typename Tg>
+template <typename Tin, typename Tg, bool kZoh>
 hipError_t launch_bwd_n(const BwdArgs &a, hipStream_t stream)
 {
     switch (a.dstate) {
-    case 1: return launch_bwd_typed<Tin, Tg, 1>(a, stream);
-    case 2: return launch_bwd_typed<Tin, Tg, 2>(a, stream);
-    case 4: return launch_bwd_typed<Tin, Tg, 4>(a, stream);
-    case 8: return launch_bwd_typed<Tin, Tg, 8>(a, stream);
-    case 16: return launch_bwd_typed<Tin, Tg, 16>(a, stream);
+    case 1: return launch_bwd_typed<Tin, Tg, 1, kZoh>(a, stream);
+    case 2: return launch_bwd_typed<Tin, Tg, 2, kZoh>(a, stream);
+    case 4: return launch_bwd_typed<Tin, Tg, 4, kZoh>(a, stream);
+    case 8: return launch_bwd_typed<Tin, Tg, 8, kZoh>(a, stream);
+    case 16: return launch_bwd_typed<Tin, Tg, 16, kZoh>(a, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <typename Tin, typename Tg>
+hipError_t launch_bwd_mode(const BwdArgs &a, hipStream_t stream)
+{
+    return a.zoh ? launch_bwd_n<Tin, Tg, true>(a, stream) : launch_bwd_n<Tin, Tg, false>(a, stream);
 }
 
 }  // namespace
@@ -740,10 +784,11 @@ size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream)
 {
     if (a.in_bf16) {
-        return a.grad_bf16 ? launch_bwd_n<bf16_t, bf16_t>(a, stream)
-                           : launch_bwd_n<bf16_t, float>(a, stream);
+        return a.grad_bf16 ? launch_bwd_mode<bf16_t, bf16_t>(a, stream)
+                           : launch_bwd_mode<bf16_t, float>(a, stream);
     }
-    return a.grad_bf16 ? launch_bwd_n<float, bf16_t>(a, stream) : launch_bwd_n<float, float>(a, stream);
+    return a.grad_bf16 ? launch_bwd_mode<float, bf16_t>(a, stream)
+                       : launch_bwd_mode<float, float>(a, stream);
 }
 
 }  // namespace ssm

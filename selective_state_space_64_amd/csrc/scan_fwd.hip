@@ -469,19 +469,17 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
     const dim3 grid(gx, a.batch, sp.nseg);
     if (a.ckpt_only) {
         // no output: one instantiation (fp32 Tout) serves every caller
-        if constexpr (!kZoh && sizeof(Tout) == 4) {
-            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true, false, false>), grid,
+        if constexpr (sizeof(Tout) == 4) {
+            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, true, false, false>), grid,
                                dim3(kThreads), 0, stream, p);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
     }
-    if constexpr (!kZoh) {
-        if (a.ck) {
-            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, false, true, false, true>), grid,
-                               dim3(kThreads), 0, stream, p);
-            return hipGetLastError();
-        }
+    if (a.ck) {
+        hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, true, false, true>), grid,
+                           dim3(kThreads), 0, stream, p);
+        return hipGetLastError();
     }
     hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, false, true>), grid, dim3(kThreads),
                        0, stream, p);

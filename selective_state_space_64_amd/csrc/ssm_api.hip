@@ -123,8 +123,7 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
         return SSM_ERR_BAD_SHAPE;
-    if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS)) != 0 ||
-        flags == (SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS))
+    if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS)) != 0)
         return SSM_ERR_UNSUPPORTED;
 
     const size_t st_elems = mul3(batch, dim, dstate);
@@ -417,7 +416,8 @@ ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
     if (!valid_dtype(in_dtype) || !valid_dtype(grad_dtype)) return SSM_ERR_BAD_DTYPE;
     if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
         return SSM_ERR_BAD_SHAPE;
-    if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_CHECKPOINTS) != 0) return SSM_ERR_UNSUPPORTED;
+    if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_CHECKPOINTS | SSM_FLAG_ZOH_B)) != 0)
+        return SSM_ERR_UNSUPPORTED;
 
     const size_t bc_elems = mul3(batch, dstate, seqlen);
     const size_t st_elems = mul3(batch, dim, dstate);
@@ -478,7 +478,7 @@ ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
                    x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy, dhL, dx, ddt, dz, dBm, dCm, dA,
                    dDskip, ddt_bias, dh0, workspace, (flags & SSM_FLAG_CHECKPOINTS) != 0,
                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], seq_b[4], seq_b[5], seq_b[6],
-                   bc_row, bc_b[0], bc_b[1]};
+                   bc_row, bc_b[0], bc_b[1], (flags & SSM_FLAG_ZOH_B) != 0};
     const hipError_t e = ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

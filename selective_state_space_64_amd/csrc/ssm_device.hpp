@@ -190,6 +190,22 @@ __device__ inline float phi_zoh(float x, float abar, float inv_x)
     return fabsf(x) < 0.0625f ? p : big;
 }
 
+// psi(x) = (x e^x - (e^x - 1)) / x^2, the A-derivative factor of the exact
+// ZOH input term: d/dA [(e^(Delta A) - 1) / A] = Delta^2 psi(Delta A).  For
+// |x| < 1/4 the Taylor series sum_m (m + 1) x^m / (m + 2)! to x^5 (truncation
+// below 1e-7 relative) avoids the cancellation of the closed form; elsewhere
+// the closed form is accurate to ~1e-5.  psi(0) = 1/2.
+__device__ inline float psi_zoh(float x, float abar, float inv_x)
+{
+    float p = __builtin_fmaf(x, 1.0f / 840.0f, 1.0f / 144.0f);
+    p = __builtin_fmaf(x, p, 1.0f / 30.0f);
+    p = __builtin_fmaf(x, p, 0.125f);
+    p = __builtin_fmaf(x, p, 1.0f / 3.0f);
+    p = __builtin_fmaf(x, p, 0.5f);
+    const float big = __builtin_fmaf(x, abar, 1.0f - abar) * inv_x * inv_x;
+    return fabsf(x) < 0.25f ? p : big;
+}
+
 // ---------------------------------------------------------------- DPP lane moves
 // dpp_ctrl encodings (GFX9 DPP): row_shr:s = 0x110 + s within a 16-lane row;
 // row_newbcast:k = 0x150 + k broadcasts lane k of each row to the whole row.

@@ -92,6 +92,7 @@ struct BwdArgs {
     // Strides in elements (time stride 1): rows of x, dt, z, dy, dx, ddt, dz
     // `row` apart, rows of Bm, Cm `bc_row` apart, batch entries `*_b` apart.
     long long row, x_b, dt_b, z_b, dy_b, dx_b, ddt_b, dz_b, bc_row, B_b, C_b;
+    int zoh;  // the exact zero-order-hold form of B-bar
 };
 
 // The backward pass keeps the state entering every kCkptSteps-step chunk

@@ -115,7 +115,7 @@ ERRORS = [
     ("batch_huge", dict(batch=70000), 2), ("L_huge", dict(seqlen=(1 << 28) - 4095), 2),
     ("in_dtype", dict(in_dtype=7), 3), ("out_dtype", dict(out_dtype=-1), 3),
     ("N3", dict(dstate=3), 6), ("N32", dict(dstate=32), 6), ("flag_bit2", dict(flags=4), 6),
-    ("flag_other", dict(flags=0x81), 6), ("zoh_with_checkpoints", dict(flags=3), 6),
+    ("flag_other", dict(flags=0x81), 6), ("zoh_checkpoints_without_workspace", dict(flags=3), 1),
     ("checkpoints_without_workspace", dict(flags=2), 1),
 ]
 

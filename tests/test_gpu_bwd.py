@@ -191,7 +191,7 @@ def test_bwd_argument_errors():
                               None, a["z"], None, 0, f(dy), None, a["dx"], f(outs[1]), a["dz"],
                               a["dBm"], f(dC), f(dAo), None, None, None, f(ws), ws.numel(), None)
 
-    assert call(flags=1) == 6          # the exact-ZOH form has no backward
+    assert call(flags=4) == 6          # an unknown flag bit
     assert call(dz=None) == 1          # z given without dz
     assert call(dx=f(x)) == 5          # output over an input
     assert call(dBm=f(dC)) == 5        # two outputs overlapping

@@ -83,3 +83,54 @@ def test_zoh_decode_matches_oracle(dtype):
         torch.cuda.synchronize()
         assert rel_err(y.cpu().numpy(), ry) <= tol_for(dtype), s
     assert rel_err(state.cpu().numpy(), ref) <= tol_for(dtype)
+
+
+# ------------------------------------------------------------ backward pass
+ZOH_BWD = [
+    # (batch, dim, N, L, dtype)
+    (2, 16, 16, 300, "f32"), (1, 17, 8, 1000, "bf16"), (2, 5, 4, 777, "f32"),
+    (1, 20, 16, 5000, "f32"),  # split along the sequence
+]
+
+
+@pytest.mark.parametrize("shape", ZOH_BWD, ids=lambda s: "b%d_d%d_N%d_L%d_%s" % s)
+def test_zoh_bwd_full_tensor(shape):
+    """The backward of the exact ZOH form (SSM_FLAG_ZOH_B) against the oracle's
+    ZOH backward, every gradient in full; the checkpoints are recomputed in
+    the call and, again, handed over by a ZOH forward with
+    SSM_FLAG_CHECKPOINTS (the two must agree)."""
+    import oracle
+    batch, dim, N, L, dt = shape
+    print("zoh bwd", shape, flush=True)
+    inp = synth.make_inputs(workload("zoh_bwd", batch, dim, N, L, dt, seed=71), with_h0=True)
+    rng = np.random.default_rng(8)
+    dyv = rng.standard_normal((batch, dim, L)).astype(np.float32)
+    dhL = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}
+    h0 = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
+    kw = dict(dt_bias=t["dt_bias"], Dskip=t["Dskip"], z=t["z"], h0=h0)
+    dy = torch.from_numpy(dyv).cuda()
+    g = ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy,
+                         dhL=torch.from_numpy(dhL).cuda(), zoh=True, **kw)
+    ws = torch.zeros(ssm.lib().ssm_scan_bwd_workspace_bytes(batch, dim, L, N), dtype=torch.uint8,
+                     device="cuda")
+    y, _ = ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], zoh=True, checkpoints=ws,
+                            **kw)
+    g2 = ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy,
+                          dhL=torch.from_numpy(dhL).cuda(), zoh=True, workspace=ws,
+                          checkpoints_in_workspace=True, **kw)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(inp.values("x"), inp.values("dt"), inp.A.astype(np.float64),
+                        inp.values("Bm"), inp.values("Cm"), dyv.astype(np.float64),
+                        dt_bias=inp.dt_bias.astype(np.float64), Dskip=inp.Dskip.astype(np.float64),
+                        z=inp.values("z"), h0=inp.h0.astype(np.float64),
+                        dhL=dhL.astype(np.float64), zoh=True)
+    ry, _ = oracle_full(inp, h0=inp.h0, zoh=True)
+    assert rel_err(y.cpu().numpy(), ry) <= tol_for(dt)
+    for k in ("dx", "ddt", "dz", "dBm", "dCm", "dh0"):
+        e = rel_err(g[k].cpu().numpy(), r[k])
+        assert e <= 1e-4, (shape, k, e)
+        assert rel_err(g2[k].cpu().numpy(), g[k].cpu().numpy()) <= 1e-5, k
+    for k in ("dA", "dDskip", "ddt_bias"):
+        e = rel_err(g[k].cpu().numpy()[None], r[k][None])
+        assert e <= 1e-4, (shape, k, e)
