@@ -394,8 +394,9 @@ def main():
         print(json.dumps(rec))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: every box here has one GPU and the scan is "
-              "benchmarked on a single device (--gpus %d is not supported)" % args.gpus,
+        print("bench.py measures one GPU: the scan is benchmarked on a single device, "
+              "and runs over several GPUs are not part of this library (--gpus %d is not "
+              "supported)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     import torch

@@ -173,7 +173,7 @@ typedef struct {
  * ssm_scan_fwd on strided inputs and output: the same arguments, flags and
  * errors, with `layout` (host pointer, read during the call only; NULL means
  * dense) giving the strides of x, dt, z, y, Bm and Cm.  A, Dskip, dt_bias, h0,
- * hL and the checkpoints stay dense.  Overlap is judged on address ranges: y
+ * hL and the checkpoints stay dense.  Overlap is checked on address ranges: y
  * and hL must not overlap the range from the first to the last element of any
  * input (as laid out by the strides), so y may not be interleaved with an
  * input even where no element coincides.
@@ -209,7 +209,7 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
  * [batch][dt_rank + 2 dstate] row.  Batch strides in ELEMENTS (0 means
  * dense: dim for x, dt, z, y; dstate for Bm, Cm); each at least that dense
  * value.  A negative stride, one below its minimum, or a tensor spanning 2^56
- * elements or more is SSM_ERR_BAD_SHAPE; overlap is judged on address
+ * elements or more is SSM_ERR_BAD_SHAPE; overlap is checked on address
  * ranges from first to last element.
  */
 typedef struct {

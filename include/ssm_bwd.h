@@ -89,7 +89,7 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
  *                  dim * seq_row
  *   bc_row, bc_batch[2]  as in ssm_scan_layout_t, for Bm and Cm
  * dBm, dCm and every other argument stay dense.  The limits and errors are
- * those of ssm_scan_layout_t; overlap is judged on each tensor's address
+ * those of ssm_scan_layout_t; overlap is checked on each tensor's address
  * range from its first to its last element, so two outputs (dx and dz, say)
  * may not be interleaved halves of one buffer, while dz alone may be written
  * into half of one.

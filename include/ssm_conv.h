@@ -67,7 +67,7 @@ ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype
  *   x_batch, y_batch  distance between batch entries; >= dim * row stride;
  *                     0 means dim * row stride
  * A stride below its minimum, a negative one, or a tensor spanning 2^56
- * elements or more is SSM_ERR_BAD_SHAPE.  Overlap is judged on each tensor's
+ * elements or more is SSM_ERR_BAD_SHAPE.  Overlap is checked on each tensor's
  * address range from its first to its last element.  weight, bias and the
  * conv states stay dense.
  */

@@ -1,8 +1,8 @@
 """Shared test utilities: device copies of synthetic inputs, oracle calls on
 sampled rows, and the parity metric.
 
-Parity metric (the pages fix no precision; the reading is stated here and in
-the design doc): for outputs g and oracle values r grouped in rows R (the (b, d, :)
+Parity metric (the pages fix no precision, so this reading is the one every
+parity test uses): for outputs g and oracle values r grouped in rows R (the (b, d, :)
 row over time for y, the (b, d, :) row over states for the final state, the
 (b, :) row over channels for a decode step),
     err = max_i |g_i - r_i| / max(|r_i|, rms_R(r)),
