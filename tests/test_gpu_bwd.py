@@ -5,8 +5,9 @@ and finite differences).
 Full-tensor comparisons of every gradient at small shapes (several chunks,
 ragged tails, channel counts that leave part of a workgroup empty, every
 supported state size, with and without gate / skip / bias / h0 / dhL), the
-whole Mamba-130M-shaped layer (batch 8, dim 1536, L 2048, bf16 inputs), bf16
-gradient outputs, and the long sequence (L = 2^20) on sampled channels for
+whole Mamba-130M-shaped layer (batch 8, dim 1536, L 2048, bf16 inputs) and
+the whole Mamba-2.8B-shaped layer (batch 4, dim 5120, L 2048), bf16 gradient
+outputs, and the long sequence (L = 2^20) on sampled channels for
 the per-channel gradients.
 
 Tolerances (metric of tests/helpers.py): the gradients are fp32 chains of the
@@ -130,6 +131,19 @@ def test_bwd_130m_layer_full():
     print("bwd", wl.name, flush=True)
     inp = synth.make_inputs(wl, with_h0=True)
     g, r = _compare(inp)
+    errs = _errors(g, r)
+    print("  " + " ".join("%s %.1e" % kv for kv in errs.items()), flush=True)
+    _check(errs, torch.float32, wl.name)
+
+
+def test_bwd_2p8b_layer_full():
+    """Mamba-2.8B-shaped layer (batch 4, dim 5120, N 16, L 2048, bf16 in, fp32
+    gradients) in the configuration the benchmark times (gate, skip and bias,
+    no h0 or dhL): every gradient against the oracle, in full."""
+    wl = synth.WORKLOADS[2]
+    print("bwd", wl.name, flush=True)
+    inp = synth.make_inputs(wl)
+    g, r = _compare(inp, use_h0=False, use_dhL=False, seed=6)
     errs = _errors(g, r)
     print("  " + " ".join("%s %.1e" % kv for kv in errs.items()), flush=True)
     _check(errs, torch.float32, wl.name)

@@ -2,8 +2,9 @@
 
 Full-tensor comparison at sizes the oracle finishes in seconds (several
 chunks, ragged tails, channel counts that leave part of a workgroup empty,
-every supported state size), and sampled-row comparison at the full sizes of
-the four scan workloads in the launch configuration the benchmark times.
+every supported state size), the two layer workloads (Mamba-130M and
+Mamba-2.8B shapes) in full and on sampled rows, and the long sequence on
+sampled rows, in the launch configuration the benchmark times.
 """
 import sys
 
@@ -102,6 +103,22 @@ def test_layer_workloads_sampled(idx):
     ey, eh = rel_err(gy, ry), rel_err(gh, rh)
     _say("  %d rows: err y %.3e hL %.3e" % (len(rows), ey, eh))
     assert np.isfinite(y.cpu().numpy()).all()
+    assert ey <= tol_for(wl.dtype) and eh <= tol_for(wl.dtype)
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_layer_workloads_full(idx):
+    """The two layer workloads in full: every y and hL value against the
+    oracle (a few seconds of fp64 CPU work at the 2.8B shape)."""
+    wl = synth.WORKLOADS[idx]
+    _say("workload %s, full" % wl.name)
+    inp = synth.make_inputs(wl)
+    y, hL = _gpu(inp)
+    gy, gh = y.cpu().numpy(), hL.cpu().numpy()
+    del y, hL
+    ry, rh = oracle_full(inp)
+    ey, eh = rel_err(gy, ry), rel_err(gh, rh)
+    _say("  err y %.3e hL %.3e" % (ey, eh))
     assert ey <= tol_for(wl.dtype) and eh <= tol_for(wl.dtype)
 
 
