@@ -1,6 +1,7 @@
 """Invariants of the HIP path that need no oracle: resume from a saved state,
 decode = scan, exact (bitwise) layout and causality probes, guard bands
-around the outputs, determinism, and in-place h0 -> hL."""
+around the outputs, determinism, in-place h0 -> hL, and calls on concurrent
+streams."""
 import numpy as np
 import pytest
 import torch
@@ -137,3 +138,66 @@ def test_deterministic_and_inplace_state():
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(h1, h2)
     assert torch.equal(y1, y3) and torch.equal(h1, hin) and h3 is hin
+
+
+def test_concurrent_streams():
+    """The library keeps no state between calls: a split forward, an unsplit
+    forward, a backward pass and decode steps enqueued at once on four streams
+    (each with its own buffers and workspace) give the same bits as the same
+    calls run one after another (the backward's atomic sums within fp32
+    rounding, their order being free)."""
+    a = _dev_all(synth.make_inputs(workload("cs_a", 2, 40, 16, 1500, "bf16", seed=71)))
+    s = _dev_all(synth.make_inputs(workload("cs_s", 1, 32, 16, 8192, "f32", seed=72)))
+    c = _dev_all(synth.make_inputs(workload("cs_c", 2, 24, 8, 700, "f32", seed=73)))
+    d_inp = synth.make_inputs(workload("cs_d", 3, 64, 16, 4, "bf16", seed=74), with_h0=True)
+    d = _dev_all(d_inp)
+    dy = torch.randn(2, 24, 700, device="cuda")
+    ws_s = torch.empty(ssm.lib().ssm_scan_fwd_workspace_bytes(1, 32, 8192, 16), dtype=torch.uint8,
+                       device="cuda")
+    assert ws_s.numel() > 0
+    atomic = {"dA", "dBm", "dCm", "dDskip", "ddt_bias"}
+
+    def fwd_a():
+        return dict(zip(("y", "hL"), _scan(a)))
+
+    def fwd_s():
+        return dict(zip(("y", "hL"), _scan(s, workspace=ws_s)))
+
+    def bwd_c():
+        g = ssm.ssm_scan_bwd(c["x"], c["dt"], c["A"], c["Bm"], c["Cm"], dy, dt_bias=c["dt_bias"],
+                             Dskip=c["Dskip"], z=c["z"])
+        return {k: v for k, v in g.items() if v is not None}
+
+    def decode_d():
+        st = torch.from_numpy(d_inp.h0).cuda()
+        out = {}
+        for i in range(4):
+            step = {k: d[k][:, :, i].contiguous() for k in ("x", "dt", "z", "Bm", "Cm")}
+            out["y%d" % i] = ssm.ssm_state_update(
+                st, step["x"], step["dt"], d["A"], step["Bm"], step["Cm"], dt_bias=d["dt_bias"],
+                Dskip=d["Dskip"], z=step["z"])
+        out["state"] = st
+        return out
+
+    steps = (fwd_a, fwd_s, bwd_c, decode_d)
+    ref = []
+    for fn in steps:
+        ref.append({k: v.clone() for k, v in fn().items()})
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in steps]
+    cur = torch.cuda.current_stream()
+    out = []
+    for st, fn in zip(streams, steps):
+        st.wait_stream(cur)
+        with torch.cuda.stream(st):
+            out.append(fn())
+    for st in streams:
+        cur.wait_stream(st)
+    torch.cuda.synchronize()
+    for fn, r, o in zip(steps, ref, out):
+        assert r.keys() == o.keys(), fn.__name__
+        for k in r:
+            if fn is bwd_c and k in atomic:
+                assert rel_err(o[k].cpu().numpy()[None], r[k].cpu().numpy()[None]) <= 1e-6, k
+            else:
+                assert torch.equal(r[k], o[k]), (fn.__name__, k)
