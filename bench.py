@@ -257,6 +257,11 @@ def bench_decode(torch, ssm, synth, steps_cap=256):
             "bytes_per_call": per_call_bytes,
             "graph_us_per_call": graph_ms * 1e3, "graph_matches_eager": graph_ok,
             "graph_hbm_gbps_algorithmic": per_call_bytes / (graph_ms * 1e-3) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": per_call_bytes / (graph_ms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": per_call_bytes / (graph_ms * 1e-3) / PEAK_HBM, "traffic": None,
+                         "algorithmic_bytes": per_call_bytes,
+                         "timing": "per step of the graph replay (launch gaps included)"},
             "note": "one launch per token, state fp32 in place; 21 MB state can stay in the 256 MB MALL"}
 
 
