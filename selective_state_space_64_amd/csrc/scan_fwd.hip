@@ -132,6 +132,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     // Per channel: NP entries of A * log2(e), then NP entries of the state
     // entering the current chunk.
     __shared__ float sAC[kChannels * 2 * NP];
+    // Checkpoints: per channel, the state at the 64-step midpoint of the
+    // chunk (lane 7's end state), gathered so that the row of N states goes
+    // out in 16-byte stores.
+    __shared__ float sMid[kCkpt ? kChannels * NP : 1];
 
     const int tid = threadIdx.x;
     const int j = tid & (kRow - 1);
@@ -155,6 +159,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     const Tin *zw = p.z ? static_cast<const Tin *>(p.z) + size_t(b) * size_t(p.z_b) + row0 : nullptr;
     Tout *yw = static_cast<Tout *>(p.y) + size_t(b) * size_t(p.y_b) + row0;
     const uint32_t lane_row = uint32_t(dc - d0) * uint32_t(p.row);  // elements
+    // Checkpoint rows: a wave-uniform base at the wave's first channel and a
+    // 32-bit lane offset (under 4 nck N <= 2^28 floats).
+    [[maybe_unused]] float *ckw = kCkpt ? p.ck + (size_t(b) * dim + d0) * size_t(p.nck) * N : nullptr;
+    [[maybe_unused]] const uint32_t ck_lane = uint32_t(dc - d0) * uint32_t(p.nck) * uint32_t(N) + uint32_t(j);
     const Tin *Bb = static_cast<const Tin *>(p.Bm) + size_t(b) * size_t(p.B_b) + size_t(lseg);
     const Tin *Cb = static_cast<const Tin *>(p.Cm) + size_t(b) * size_t(p.C_b) + size_t(lseg);
     // Wave-uniform: every row of every streamed tensor starts on a 16-byte
@@ -307,6 +315,17 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             }
         }
         const bool more = ch + 1 < nchunks;
+        // Checkpoints for the backward pass: the state entering each 64-step
+        // half of the chunk, one (b, d, half) row of N states per store
+        // instruction (lane j writes state j), so every row goes out as one
+        // contiguous line instead of N scattered words.
+        [[maybe_unused]] auto store_ck = [&](const float *src, int half) {
+            static_assert(kRow * K == 2 * kCkptSteps, "two checkpoints per chunk");
+            static_assert(N <= kRow, "one lane per state");
+            const int ck = 2 * (ch + lseg / T) + half;  // global 64-step chunk
+            if (live && j < N && ck < p.nck) ckw[ck_lane + uint32_t(ck) * uint32_t(N)] = src[j];
+        };
+        if constexpr (kCkpt) store_ck(aptr + NP, 0);  // the carry entering the chunk
 
         const float4 *bp = sB[buf] + j;
         const float4 *cp = sC[buf] + j;
@@ -350,18 +369,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
 #pragma unroll
             for (int i = 1; i < K; ++i) hl = __builtin_fmaf(dA[i], hl, bb[i]);
             float aa = exp2_hw(sumd * ap);
-            [[maybe_unused]] const float cin = carry;
             float hend, h = carry;
             row_scan(aa, hl, hend, h);
             if (j == kRow - 1) aptr[NP + n] = hend;
             if constexpr (kCkpt) {
-                // checkpoints for the backward pass: the state entering each
-                // 64-step half of the chunk (the carry, and lane 7's end)
-                static_assert(kRow * K == 2 * kCkptSteps, "two checkpoints per chunk");
-                const int half = j == kRow / 2 - 1 ? 1 : 0;
-                const int ck = 2 * (ch + lseg / T) + half;  // global 64-step chunk
-                if (live && (j == 0 || half) && ck < p.nck)
-                    p.ck[((size_t(b) * dim + d) * p.nck + ck) * N + n] = half ? hend : cin;
+                if (j == kRow / 2 - 1) sMid[c * NP + n] = hend;  // entering the chunk's second half
             }
             bp += Q * kRow;
             load_b(bp, bv);          // next state's B (one past the end on the last state)
@@ -430,6 +442,7 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             else if (cnt > 0)
                 store_y<Tout, K>(yr, cnt == K && aligned16(yr), cnt, yv);
         }
+        if constexpr (kCkpt) store_ck(sMid + c * NP, 1);  // lane 7's end states, same wave
         lds_barrier();
     }
 
