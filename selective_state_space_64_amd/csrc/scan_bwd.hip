@@ -25,7 +25,9 @@
 //      in reverse time, from zero (dhL for the last): its adjoint aggregate;
 //   4. scan_bwd_kernel: per segment (one for unsplit shapes), 64-step chunks
 //      in reverse order, entering with the later segments' aggregates
-//      composed.  Per chunk, for pairs of states (two independent chains in
+//      composed.  Every global load of a chunk (x, dt, dy, z, its Bm / Cm
+//      run and checkpoint) is issued one chunk ahead, during the previous
+//      chunk's work.  Per chunk, for pairs of states (two independent chains in
 //      flight per wave, their DPP scans interleaved), the workgroup
 //      recomputes the chunk's states from its checkpoint with the forward
 //      in-row scan, folds the adjoint of each lane's 4 steps into an affine
@@ -133,6 +135,49 @@ __device__ inline void store4(T *q, int count, const float *v)
                 reinterpret_cast<uint16_t *>(q)[i] = uint16_t(pack_bf16x2(v[i], 0.0f) & 0xffffu);
             }
         }
+    }
+}
+
+// A lane's 4-step run as raw words (bf16: 2, fp32: 4), loaded a chunk ahead
+// and decoded where it is used, so that the wait for the load sits there.
+template <typename T>
+struct Run4 {
+    uint32_t w[sizeof(T)];
+};
+
+template <typename T>
+__device__ inline void load4_raw(const T *q, int count, Run4<T> &r)
+{
+    if (count == 4 && run_aligned(q)) {
+        if constexpr (sizeof(T) == 4) {
+            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(q));
+            r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+        } else {
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(q));
+            r.w[0] = v.x; r.w[1] = v.y;
+        }
+    } else if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.w[i] = i < count ? __float_as_uint(q[i]) : 0u;
+    } else {
+        uint32_t e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = i < count ? uint32_t(q[i].bits) : 0u;
+        r.w[0] = e[0] | (e[1] << 16);
+        r.w[1] = e[2] | (e[3] << 16);
+    }
+}
+
+template <typename T>
+__device__ inline void decode4(const Run4<T> &r, float *out)
+{
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(r.w[i]);
+    } else {
+        out[0] = io<bf16_t>::lo(r.w[0]); out[1] = io<bf16_t>::hi(r.w[0]);
+        out[2] = io<bf16_t>::lo(r.w[1]); out[3] = io<bf16_t>::hi(r.w[1]);
     }
 }
 
@@ -464,33 +509,66 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
     const int c_lo = seg * cpseg;
     const int c_hi = seg == p.nseg - 1 ? p.nchunks : min(p.nchunks, (seg + 1) * cpseg);
 
+    // Everything a chunk reads from memory is fetched one chunk ahead (the
+    // chunks run in reverse): this lane's x, dt, dy, z, the staging thread's
+    // Bm / Cm run and its checkpoint entry.  With fp32 inputs the Bm / Cm runs
+    // are loaded at the chunk start instead: their 8 more registers spilled.
+    constexpr bool kPfBC = sizeof(Tin) == 2;
+    static_assert(kChanB * N <= kThreadsB, "one checkpoint entry per thread");
+    const bool ck_thread = tid < kChanB * N;
+    const int ck_c = ck_thread ? tid / N : 0, ck_n = tid % N;
+    const float *ck_row = p.ck + (size_t(b) * dim + min(int(blockIdx.x) * kChanB + ck_c, dim - 1)) *
+                                     size_t(p.nchunks) * N + ck_n;
+    Run4<Tin> px, pdt, pz, pB, pC;
+    Run4<Tg> pdy;
+    float pck = 0.0f;
+    auto prefetch = [&](int ch) {
+        const int l0 = ch * T + j * K;
+        const int cnt = live ? max(0, min(K, L - l0)) : 0;
+        load4_raw<Tin>(xr + l0, cnt, px);
+        load4_raw<Tin>(dtr + l0, cnt, pdt);
+        load4_raw<Tg>(dyr + l0, cnt, pdy);
+        if (zr) load4_raw<Tin>(zr + l0, cnt, pz);
+        if (kPfBC && stager) {
+            const int l = ch * T + sj * K;
+            const int c2 = max(0, min(K, L - l));
+            load4_raw<Tin>(Bb + size_t(sn) * size_t(p.bc_row) + l, c2, pB);
+            load4_raw<Tin>(Cb + size_t(sn) * size_t(p.bc_row) + l, c2, pC);
+        }
+        if (ck_thread) pck = ck_row[size_t(ch) * N];
+    };
+    if (c_hi > c_lo) prefetch(c_hi - 1);
+
     for (int ch = c_hi - 1; ch >= c_lo; --ch) {
         lds_barrier();
-        if (stager) {
+        if (kPfBC && stager) {
+            float v[K];
+            decode4<Tin>(pB, v);
+            sB[sn * kRowB + sj] = make_float4(v[0], v[1], v[2], v[3]);
+            decode4<Tin>(pC, v);
+            sC[sn * kRowB + sj] = make_float4(v[0], v[1], v[2], v[3]);
+        } else if (stager) {
             stage_chunk<Tin, K>(sB, Bb, L, p.bc_row, ch, sn, sj);
             stage_chunk<Tin, K>(sC, Cb, L, p.bc_row, ch, sn, sj);
         }
-        for (int s = tid; s < kChanB * N; s += kThreadsB) {
-            const int cc = s / N, n = s % N;
-            const int dd = min(int(blockIdx.x) * kChanB + cc, dim - 1);
-            sH[cc * NP + n] = p.ck[((size_t(b) * dim + dd) * p.nchunks + ch) * N + n];
-        }
+        if (ck_thread) sH[ck_c * NP + ck_n] = pck;
+        // per step: sb = sum_n lambda B, sah = sum_n lambda A A-bar h_{t-1}
+        float xv[K], delta[K], w[K], ds[K], sacc[K], sb[K], sah[K], sgu[K], gzf[K];
+        [[maybe_unused]] float invd[K], sba[K];  // exact ZOH: 1/Delta, sum_n lambda A-bar B
+        float dv[K], gy[K], zv[K];
+        decode4<Tin>(px, xv);
+        decode4<Tin>(pdt, dv);
+        decode4<Tg>(pdy, gy);
+        if (zr) decode4<Tin>(pz, zv);
+        if (ch > c_lo) prefetch(ch - 1);
 
         // Per-step quantities of this lane's K steps.  Steps past the end of
         // the sequence and dead channels get Delta = 0 and ds = 0: identity
         // maps that add nothing to any sum.
         const int l0 = ch * T + j * K;
         const int cnt = live ? max(0, min(K, L - l0)) : 0;
-        // per step: sb = sum_n lambda B, sah = sum_n lambda A A-bar h_{t-1}
-        float xv[K], delta[K], w[K], ds[K], sacc[K], sb[K], sah[K], sgu[K], gzf[K];
-        [[maybe_unused]] float invd[K], sba[K];  // exact ZOH: 1/Delta, sum_n lambda A-bar B
         float sumd = 0.0f;
         {
-            float dv[K], gy[K], zv[K];
-            load4<Tin>(xr + l0, cnt, xv);
-            load4<Tin>(dtr + l0, cnt, dv);
-            load4<Tg>(dyr + l0, cnt, gy);
-            if (zr) load4<Tin>(zr + l0, cnt, zv);
 #pragma unroll
             for (int i = 0; i < K; ++i) {
                 const bool in = i < cnt;
