@@ -1,6 +1,7 @@
 """GPU parity of ssm_state_update (through the C ABI) against the fp64 oracle:
 the 256-step decode workload on a [64, 5120, 16] fp32 state updated in place,
-and small shapes compared in full.  The oracle side runs the same steps as
+small shapes compared in full, and shapes that take the four-rows-per-lane
+launch compared in full.  The oracle side runs the same steps as
 one scan from the initial state (the decode recurrence and the scan are the
 same function; the oracle's own pins show it)."""
 import numpy as np
@@ -10,7 +11,7 @@ import torch
 import oracle
 import selective_state_space_64_amd as ssm
 from selective_state_space_64_amd import synth
-from helpers import TOL_BF16_OUT, rel_err, sample_rows, to_dev, tol_for, workload
+from helpers import TOL_BF16_OUT, oracle_full, rel_err, sample_rows, to_dev, tol_for, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +79,42 @@ def test_decode_small_full(shape):
         gh = state.reshape(batch * dim, N).cpu().numpy()
         tol = tol_for(dt)
         assert rel_err(gy, ry) <= tol and rel_err(gh, rh) <= tol, (shape, gate)
+
+
+@pytest.mark.parametrize("shape", [(300, 1000, 16, 3, "bf16"), (600, 1000, 8, 3, "f32"),
+                                   (1100, 1000, 4, 2, "bf16"), (1100, 1000, 1, 2, "f32")],
+                         ids=lambda s: "b%d_d%d_N%d_steps%d_%s" % s)
+def test_decode_four_rows_per_lane_full(shape):
+    """Shapes large enough for the launch that gives each lane four (b, d)
+    rows, with a dim that leaves rows of the last workgroup dead: every y and
+    state value against the oracle (the steps run as one scan)."""
+    batch, dim, N, steps, dt = shape
+    inp = synth.make_inputs(workload("dec4", batch, dim, N, steps, dt, seed=31), with_h0=True)
+    ys, state = _run_decode(inp, steps)
+    ry, rh = oracle_full(inp, h0=inp.h0)
+    # y and the state are compared over rows of channels, (b, :) per step and
+    # (b, :, n) per state: a row over only 2-3 steps or N = 1 states would turn
+    # the rounding of a value that cancels to near zero into a relative error
+    gy = ys.cpu().numpy()                      # [steps, batch, dim]
+    tol = tol_for(dt)
+    ey = rel_err(gy, np.transpose(ry, (2, 0, 1)))
+    eh = rel_err(state.transpose(1, 2).cpu().numpy(), np.transpose(rh, (0, 2, 1)))
+    print("  %s: err y %.3e state %.3e" % (shape, ey, eh), flush=True)
+    assert ey <= tol and eh <= tol
+    if N == 16:
+        # the same steps on projection halves (x, z of one [batch, 2 dim] row,
+        # y into half of another): equal bit for bit to the dense calls
+        state2 = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
+        xz = torch.cat([_steps(to_dev(inp, "x")), _steps(to_dev(inp, "z"))], dim=2)
+        dts, Bs, Cs = _steps(to_dev(inp, "dt")), _steps(to_dev(inp, "Bm")), _steps(to_dev(inp, "Cm"))
+        A, Dk, bias = to_dev(inp, "A"), to_dev(inp, "Dskip"), to_dev(inp, "dt_bias")
+        ybuf = torch.full((steps, batch, 2 * dim), 555.0, device="cuda")
+        for st in range(steps):
+            ssm.ssm_state_update(state2, xz[st, :, :dim], dts[st], A, Bs[st], Cs[st], dt_bias=bias,
+                                 Dskip=Dk, z=xz[st, :, dim:], y=ybuf[st, :, :dim])
+        torch.cuda.synchronize()
+        assert torch.equal(ybuf[:, :, :dim], ys) and torch.equal(state2, state)
+        assert bool((ybuf[:, :, dim:] == 555.0).all())
 
 
 def test_decode_bf16_output():
