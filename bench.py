@@ -274,6 +274,13 @@ def bench_conv(torch, ssm, synth, wl, x, launches=20):
     stream = torch.cuda.current_stream()
     for _ in range(3):
         ssm.ssm_conv1d_fwd(x, wt, bias=bt, y=y, return_final_state=False)
+    # launches back to back between two events (the roofline's time base),
+    # then events around each launch for the per-launch mean
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for _ in range(launches):
+        ssm.ssm_conv1d_fwd(x, wt, bias=bt, y=y, return_final_state=False)
+    r1.record(stream)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(launches)]
     for e0, e1 in evs:
@@ -281,10 +288,12 @@ def bench_conv(torch, ssm, synth, wl, x, launches=20):
         ssm.ssm_conv1d_fwd(x, wt, bias=bt, y=y, return_final_state=False)
         e1.record(stream)
     torch.cuda.synchronize()
-    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ms = r0.elapsed_time(r1) / launches
+    per_launch = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
     nbytes = 2 * x.numel() * x.element_size() + wl.dim * 5 * 4
     achieved = nbytes / (ms * 1e-3)
     out = {"workload": "conv1d W4 silu, %s" % wl.name, "kernel_ms_mean": ms,
+           "per_launch_events_ms_mean": per_launch,
            "outputs_per_s": x.numel() / (ms * 1e-3),
            "roofline": {"bound": "hbm", "achieved": achieved / 1e9, "peak": PEAK_HBM / 1e9,
                         "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
@@ -346,16 +355,16 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
             raise RuntimeError("ssm_scan_bwd failed with status %d" % st)
 
     def timed(fn):
+        # calls back to back between two events on the launch stream
         for _ in range(2):
             fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(launches)]
-        for e0, e1 in evs:
-            e0.record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
             fn()
-            e1.record(stream)
+        e1.record(stream)
         torch.cuda.synchronize()
-        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        return e0.elapsed_time(e1) / launches
 
     ms = timed(call)
     # training order: the forward writes the checkpoints (SSM_FLAG_CHECKPOINTS)
@@ -439,19 +448,31 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # The timed region: K steps back to back between two HIP events on the
+    # launch stream (their mean is the kernel's average launch duration, the
+    # roofline's time base); the wall clock around it gives ms_per_step.
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    r0.record(stream)
+    for _ in range(args.steps):
+        step()
+    r1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = r0.elapsed_time(r1) / args.steps
+    # the spread per launch, from events around each launch of a second loop
+    # (the event packets between launches add about a microsecond each)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
     for a, b in evs:
         a.record(stream)
         step()
         b.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = np.array([a.elapsed_time(b) for a, b in evs])
     ms_step = wall * 1e3 / args.steps
-    kern_s = float(launch_ms.mean()) * 1e-3
+    kern_s = region_ms * 1e-3
     elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
     in_bytes = 2 if wl.dtype == "bf16" else 4
     slots = algorithmic_slots(wl.batch, wl.dim, wl.seqlen, wl.dstate)
@@ -474,8 +495,10 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "dim": wl.dim, "dstate": wl.dstate,
                    "seqlen": wl.seqlen, "input_dtype": wl.dtype, "output_dtype": "f32",
                    "parallelism": "single GPU"},
-        "kernel_ms": {"mean": float(launch_ms.mean()), "min": float(launch_ms.min()),
-                      "median": float(np.median(launch_ms)), "p90": float(np.percentile(launch_ms, 90))},
+        "kernel_ms": {"mean": region_ms, "timing": "K launches back to back between two events",
+                      "per_launch_mean": float(launch_ms.mean()), "per_launch_min": float(launch_ms.min()),
+                      "per_launch_median": float(np.median(launch_ms)),
+                      "per_launch_p90": float(np.percentile(launch_ms, 90))},
         "hbm_gbps_algorithmic": nbytes / kern_s / 1e9,
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
                      "frac": achieved / peak, "traffic": counter_traffic(wl.name),
@@ -486,18 +509,17 @@ def main():
                              "algorithmic_bytes": nbytes}},
     }
     # exact zero-order-hold B-bar variant of the same step (SSM_FLAG_ZOH_B)
-    zev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(10)]
     for _ in range(2):
         ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
                          Dskip=t["Dskip"], z=t["z"], y=y, hL=hL, zoh=True)
-    for a, b in zev:
-        a.record(stream)
+    z0, z1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    z0.record(stream)
+    for _ in range(10):
         ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dt_bias=t["dt_bias"],
                          Dskip=t["Dskip"], z=t["z"], y=y, hL=hL, zoh=True)
-        b.record(stream)
+    z1.record(stream)
     torch.cuda.synchronize()
-    zms = float(np.mean([a.elapsed_time(b) for a, b in zev]))
+    zms = z0.elapsed_time(z1) / 10
     result["zoh_variant"] = {"kernel_ms_mean": zms, "elements_per_s": elems / (zms * 1e-3)}
     if not args.no_decode:
         result["decode"] = bench_decode(torch, ssm, synth)
