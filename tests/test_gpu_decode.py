@@ -21,7 +21,7 @@ def _steps(t):
     return t.permute(2, 0, 1).contiguous()
 
 
-def _run_decode(inp, steps, gate=True, out_dtype=torch.float32):
+def _run_decode(inp, steps, gate=True, out_dtype=torch.float32, zoh=False):
     state = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
     xs, dts, zs = _steps(to_dev(inp, "x")), _steps(to_dev(inp, "dt")), _steps(to_dev(inp, "z"))
     Bs, Cs = _steps(to_dev(inp, "Bm")), _steps(to_dev(inp, "Cm"))
@@ -29,7 +29,7 @@ def _run_decode(inp, steps, gate=True, out_dtype=torch.float32):
     ys = torch.empty((steps,) + tuple(state.shape[:2]), dtype=out_dtype, device="cuda")
     for s in range(steps):
         ssm.ssm_state_update(state, xs[s], dts[s], A, Bs[s], Cs[s], dt_bias=bias, Dskip=Dk,
-                             z=zs[s] if gate else None, y=ys[s], out_dtype=out_dtype)
+                             z=zs[s] if gate else None, y=ys[s], out_dtype=out_dtype, zoh=zoh)
     torch.cuda.synchronize()
     return ys, state
 
@@ -81,17 +81,19 @@ def test_decode_small_full(shape):
         assert rel_err(gy, ry) <= tol and rel_err(gh, rh) <= tol, (shape, gate)
 
 
-@pytest.mark.parametrize("shape", [(300, 1000, 16, 3, "bf16"), (600, 1000, 8, 3, "f32"),
-                                   (1100, 1000, 4, 2, "bf16"), (1100, 1000, 1, 2, "f32")],
-                         ids=lambda s: "b%d_d%d_N%d_steps%d_%s" % s)
+@pytest.mark.parametrize("shape", [(300, 1000, 16, 3, "bf16", False), (600, 1000, 8, 3, "f32", False),
+                                   (1100, 1000, 4, 2, "bf16", False), (1100, 1000, 1, 2, "f32", False),
+                                   (300, 1000, 16, 3, "bf16", True)],
+                         ids=lambda s: "b%d_d%d_N%d_steps%d_%s_zoh%d" % s)
 def test_decode_four_rows_per_lane_full(shape):
     """Shapes large enough for the launch that gives each lane four (b, d)
-    rows, with a dim that leaves rows of the last workgroup dead: every y and
-    state value against the oracle (the steps run as one scan)."""
-    batch, dim, N, steps, dt = shape
+    rows, with a dim that leaves rows of the last workgroup dead, one of them
+    with the exact zero-order-hold B-bar: every y and state value against the
+    oracle (the steps run as one scan)."""
+    batch, dim, N, steps, dt, zoh = shape
     inp = synth.make_inputs(workload("dec4", batch, dim, N, steps, dt, seed=31), with_h0=True)
-    ys, state = _run_decode(inp, steps)
-    ry, rh = oracle_full(inp, h0=inp.h0)
+    ys, state = _run_decode(inp, steps, zoh=zoh)
+    ry, rh = oracle_full(inp, h0=inp.h0, zoh=zoh)
     # y and the state are compared over rows of channels, (b, :) per step and
     # (b, :, n) per state: a row over only 2-3 steps or N = 1 states would turn
     # the rounding of a value that cancels to near zero into a relative error
@@ -101,7 +103,7 @@ def test_decode_four_rows_per_lane_full(shape):
     eh = rel_err(state.transpose(1, 2).cpu().numpy(), np.transpose(rh, (0, 2, 1)))
     print("  %s: err y %.3e state %.3e" % (shape, ey, eh), flush=True)
     assert ey <= tol and eh <= tol
-    if N == 16:
+    if N == 16 and not zoh:
         # the same steps on projection halves (x, z of one [batch, 2 dim] row,
         # y into half of another): equal bit for bit to the dense calls
         state2 = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
