@@ -140,7 +140,6 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     const int tid = threadIdx.x;
     const int j = tid & (kRow - 1);
     const int c = tid / kRow;                 // channel within the workgroup
-    const int cw = c & 3;                     // channel within the wave
     const int b = blockIdx.y;
     const int dim = p.dim;
     const int seg = blockIdx.z;
