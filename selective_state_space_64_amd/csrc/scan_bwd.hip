@@ -736,9 +736,9 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
                 const int g = tid / (2 * T), qq = (tid / T) & 1, t = tid % T;
                 if (g < G) {
                     const float *col = reinterpret_cast<const float *>(&sP[pb][g][qq][0][0]) + t;
-                    float acc = 0.0f;
+                    float acc = col[0];
 #pragma unroll
-                    for (int cc = 0; cc < kChanB; ++cc) acc += col[cc * T];
+                    for (int cc = 1; cc < kChanB; ++cc) acc += col[cc * T];
                     const int tt = ch * T + t;
                     if (tt < L) atomicAdd(&part[size_t(qq) * bnl + size_t(n + g) * L + tt], acc);
                 }
