@@ -647,8 +647,13 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
             } else {
                 row_scan(aa[0], hl[0], hend[0], h[0]);
             }
+            // hin: the state entering the lane's first step (A-bar h_{t-1} is
+            // formed below as a product, not as h_t - B-bar x, which cancels
+            // when A-bar ~ 0)
+            float hin[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
+                hin[g] = h[g];
 #pragma unroll
                 for (int i = 0; i < K; ++i) {
                     h[g] = __builtin_fmaf(da[g][i], h[g], w[i] * bg[g][i]);
@@ -689,7 +694,7 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 #pragma unroll
                 for (int i = K - 1; i >= 0; --i) {
                     lam = __builtin_fmaf(ds[i], cv[g][i], lam);
-                    const float hpa = __builtin_fmaf(-w[i], bg[g][i], hh[g][i]);  // A-bar h_{t-1}
+                    const float hpa = da[g][i] * (i > 0 ? hh[g][i - 1] : hin[g]);  // A-bar h_{t-1}
                     const float lh = lam * hpa;
                     sah[i] = __builtin_fmaf(An[g], lh, sah[i]);
                     dap[g] = __builtin_fmaf(delta[i], lh, dap[g]);
