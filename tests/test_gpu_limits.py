@@ -5,7 +5,8 @@ oracle.
   pass, the decode step and the conv, compared in full;
 - seqlen = 2^28 - 4096, the longest sequence the scan accepts: four
   channels (the fourth sits at the largest in-wave row offset), split into
-  1024 segments, the last channel's whole row against the oracle;
+  1024 segments, the last channel's whole row against the oracle, for the
+  forward and for the per-channel gradients of the backward pass;
 - one past each limit is rejected before launch (also covered without a GPU
   in test_abi.py).
 """
@@ -121,3 +122,35 @@ def test_scan_max_seqlen():
         one = torch.zeros(1, 1, L + 1, device="cuda")
         ssm.ssm_scan_fwd(one, one, torch.zeros(1, 1, device="cuda"), one, one)
     assert e.value.status == 2
+
+
+def test_bwd_max_seqlen():
+    """The backward pass at the longest supported sequence (fp32, four
+    channels, N = 1, split into 1024 segments): the fourth channel's
+    per-channel gradients (dx, ddt, dz over the whole row, dA, dDskip,
+    ddt_bias) against the oracle run on that channel alone (dBm and dCm sum
+    over channels and are covered at the shorter shapes)."""
+    L, dim = MAX_SEQLEN, 4
+    wl = workload("max_seqlen_bwd", 1, dim, 1, L, "f32", seed=56)
+    print("bwd max seqlen", flush=True)
+    inp = synth.make_inputs(wl)
+    dyv = np.random.default_rng(57).standard_normal((1, dim, L), dtype=np.float32)
+    t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}
+    g = ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], torch.from_numpy(dyv).cuda(),
+                         dt_bias=t["dt_bias"], Dskip=t["Dskip"], z=t["z"])
+    torch.cuda.synchronize()
+    d = dim - 1
+    got = {k: g[k][0, d].cpu().numpy() for k in ("dx", "ddt", "dz")}
+    got.update({k: g[k][d].cpu().numpy() for k in ("dA", "dDskip", "ddt_bias")})
+    del g, t
+    torch.cuda.empty_cache()
+    row = lambda a: np.ascontiguousarray(a[:, d:d + 1], dtype=np.float64)
+    r = oracle.scan_bwd(row(inp.x), row(inp.dt), inp.A[d:d + 1].astype(np.float64),
+                        inp.Bm.astype(np.float64), inp.Cm.astype(np.float64), row(dyv),
+                        dt_bias=inp.dt_bias[d:d + 1].astype(np.float64),
+                        Dskip=inp.Dskip[d:d + 1].astype(np.float64), z=row(inp.z))
+    del inp
+    for k in ("dx", "ddt", "dz"):
+        assert rel_err(got[k][None], r[k][0]) <= TOL_F32, k
+    for k in ("dA", "dDskip", "ddt_bias"):
+        assert rel_err(np.atleast_1d(got[k])[None], np.atleast_1d(r[k][0])[None]) <= TOL_F32, k
