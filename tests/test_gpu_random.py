@@ -32,7 +32,7 @@ def _configs(n, seed=2024):
     return out
 
 
-CONFIGS = _configs(24)
+CASES = _configs(24)
 
 
 def _id(c):
@@ -48,7 +48,7 @@ def _view(t, strided):
     return buf[:, :t.shape[1]], buf
 
 
-@pytest.mark.parametrize("c", CONFIGS, ids=_id)
+@pytest.mark.parametrize("c", CASES, ids=_id)
 def test_random_forward_and_backward(c):
     print("random", _id(c), flush=True)
     inp = synth.make_inputs(workload("random", c["batch"], c["dim"], c["N"], c["L"], c["dtype"],
@@ -96,7 +96,7 @@ def test_random_forward_and_backward(c):
     del keep
 
 
-@pytest.mark.parametrize("c", CONFIGS[:12], ids=_id)
+@pytest.mark.parametrize("c", CASES[:12], ids=_id)
 def test_random_decode_and_conv(c):
     """Decode steps over the first few positions against the scan oracle, and
     the conv over the whole sequence, for the same random shapes."""
