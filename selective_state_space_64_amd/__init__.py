@@ -137,11 +137,11 @@ def _dtype_code(t):
 def _ptr(t, name, shape=None, dtype=None):
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError("%s must be a CUDA (HIP) tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
@@ -160,9 +160,9 @@ def _rows(ts, names, shape, dtype):
             ptrs.append(None)
             bstrides.append(0)
             continue
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError("%s must be a CUDA (HIP) tensor" % name)
-        if tuple(t.shape) != tuple(shape):
+        if t.shape != shape:
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
         want = dtype[name] if isinstance(dtype, dict) else dtype
         if t.dtype != want:
@@ -185,9 +185,9 @@ def _bptr(t, name, shape, dtype):
     whose last index is contiguous, e.g. one half of a projection row."""
     if t is None:
         return None, 0
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError("%s must be a CUDA (HIP) tensor" % name)
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
