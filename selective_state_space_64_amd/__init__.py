@@ -18,6 +18,7 @@ Dskip, dt_bias [dim]; h0, hL, state [batch, dim, N] (decode: drop L);
 conv weight [dim, W], bias [dim], conv state [batch, dim, W-1].
 """
 import ctypes
+import functools
 import os
 
 import torch
@@ -152,7 +153,9 @@ def _rows(ts, names, shape, dtype):
     """Pointers, shared row stride and batch strides of [batch, rows, L]
     tensors whose time index is contiguous (views such as halves of one
     projection output).  Strides of size-1 dimensions are free and read as the
-    dense default (0)."""
+    dense default (0).  Broadcast views (stride 0 on a dimension of size > 1,
+    e.g. from expand()) are rejected: the C ABI reads a stride of 0 as the
+    dense default, so passing one through would index past the allocation."""
     batch, rows, L = shape
     ptrs, bstrides, rstride = [], [], None
     for t, name in zip(ts, names):
@@ -160,15 +163,18 @@ def _rows(ts, names, shape, dtype):
             ptrs.append(None)
             bstrides.append(0)
             continue
-        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        if not isinstance(t, torch.Tensor):
             raise TypeError("%s must be a CUDA (HIP) tensor" % name)
         if t.shape != shape:
             raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
         want = dtype[name] if isinstance(dtype, dict) else dtype
         if t.dtype != want:
             raise TypeError("%s must be %s, got %s" % (name, want, t.dtype))
+        _no_broadcast(t, name)
         if L > 1 and t.stride(2) != 1:
             raise ValueError("%s must have a contiguous time index (stride 1)" % name)
+        if not t.is_cuda:
+            raise TypeError("%s must be a CUDA (HIP) tensor" % name)
         if rows > 1:
             if rstride is None:
                 rstride = t.stride(1)
@@ -180,21 +186,56 @@ def _rows(ts, names, shape, dtype):
     return ptrs, (rstride if rstride is not None else 0), bstrides
 
 
+def _no_broadcast(t, name):
+    """Raise for a view that repeats memory along a dimension (stride 0 on a
+    dimension of size > 1): the kernels would read it at dense offsets."""
+    for k in range(t.dim()):
+        if t.shape[k] > 1 and t.stride(k) == 0:
+            raise ValueError("%s is a broadcast view (stride 0 along dimension %d); "
+                             "pass a materialised tensor (.contiguous())" % (name, k))
+
+
+def _no_broadcast_args(**tensors):
+    """_no_broadcast over every tensor argument of a call, before any other
+    check, so that such a view is reported as what it is."""
+    for name, t in tensors.items():
+        if isinstance(t, torch.Tensor):
+            _no_broadcast(t, name)
+
+
 def _bptr(t, name, shape, dtype):
     """Pointer and batch stride (elements; 0 = dense) of a [batch, n] tensor
-    whose last index is contiguous, e.g. one half of a projection row."""
+    whose last index is contiguous, e.g. one half of a projection row.
+    Broadcast views (stride 0 on a dimension of size > 1) are rejected."""
     if t is None:
         return None, 0
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+    if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a CUDA (HIP) tensor" % name)
     if t.shape != shape:
         raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
     if t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    _no_broadcast(t, name)
     if shape[1] > 1 and t.stride(1) != 1:
         raise ValueError("%s must have a contiguous last index" % name)
+    if not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
     sb = t.stride(0)
     return t.data_ptr(), (sb if shape[0] > 1 and sb != shape[1] else 0)
+
+
+def _on_caller_stream(fn):
+    """Run the call with `stream` (when given) as the current stream, so that
+    every tensor allocated inside it (outputs, workspace) belongs to the stream
+    the kernels are enqueued on: the caching allocator then cannot hand such a
+    block to work on another stream while these kernels still use it."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return call
 
 
 def _stream(stream, device):
@@ -202,6 +243,7 @@ def _stream(stream, device):
     return s.cuda_stream
 
 
+@_on_caller_stream
 def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
                  out_dtype=torch.float32, return_final_state=True, y=None, hL=None,
                  zoh=False, checkpoints=None, workspace=None, stream=None):
@@ -216,6 +258,8 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     workspace: device scratch of ssm_scan_fwd_workspace_bytes(...) bytes for
     shapes whose sequence the library splits across workgroups (few batch
     rows and channels, long L); allocated here when not given."""
+    _no_broadcast_args(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, dt_bias=dt_bias, Dskip=Dskip, z=z, h0=h0,
+                       y=y, hL=hL)
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -255,12 +299,15 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     return y, hL
 
 
+@_on_caller_stream
 def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None,
                      out_dtype=torch.float32, y=None, zoh=False, stream=None):
     """One decode step; updates `state` in place and returns y [batch, dim].
     zoh=True selects the exact zero-order-hold B-bar (SSM_FLAG_ZOH_B).
     x, dt, z, y, Bm and Cm may be batch-strided views with a contiguous last
     index (x and z as halves of the step's [batch, 2 dim] projection row)."""
+    _no_broadcast_args(state=state, x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, dt_bias=dt_bias, Dskip=Dskip,
+                       z=z, y=y)
     batch, dim, N = state.shape
     ind = x.dtype
     if y is None:
@@ -288,6 +335,7 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     return y
 
 
+@_on_caller_stream
 def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=None, dhL=None,
                  grad_dtype=torch.float32, workspace=None, checkpoints_in_workspace=False,
                  dx=None, ddt=None, dz=None, zoh=False, stream=None):
@@ -300,6 +348,8 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
     dense) may be strided views with a contiguous time index and one shared
     row stride, e.g. z and dz as halves of the projection's buffers; Bm and
     Cm likewise with their own row stride."""
+    _no_broadcast_args(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, dy=dy, dt_bias=dt_bias, Dskip=Dskip, z=z,
+                       h0=h0, dhL=dhL, dx=dx, ddt=ddt, dz=dz)
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -351,12 +401,14 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
     return g
 
 
+@_on_caller_stream
 def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=None,
                    return_final_state=True, y=None, stateL=None, stream=None):
     """Causal depthwise conv over [batch, dim, L]; returns (y, stateL).
     out_dtype defaults to x's dtype (the conv output feeds the scan's x).
     x and y may be strided views with a contiguous time index (x as the
     first half of the input projection's [batch, 2 dim, L] output)."""
+    _no_broadcast_args(x=x, weight=weight, bias=bias, state0=state0, y=y, stateL=stateL)
     if x.dim() != 3:
         raise ValueError("x must be [batch, dim, L]")
     batch, dim, L = x.shape
@@ -380,11 +432,13 @@ def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=No
     return y, stateL
 
 
+@_on_caller_stream
 def ssm_conv1d_update(state, x, weight, *, bias=None, silu=True, out_dtype=None, y=None,
                       stream=None):
     """One decode step of the conv; shifts `state` [batch, dim, W-1] in place
     and returns y [batch, dim].  x and y may be batch-strided views with a
     contiguous last index (x as the first half of the step's projection row)."""
+    _no_broadcast_args(state=state, x=x, weight=weight, bias=bias, y=y)
     batch, dim, H = state.shape
     out_dtype = out_dtype or x.dtype
     if y is None:

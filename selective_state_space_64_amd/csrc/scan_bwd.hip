@@ -6,7 +6,10 @@
 // "Mamba: Linear-Time Sequence Modeling with Selective State Spaces": the
 // backward pass recomputes the intermediate states).  Per (b, d) the adjoint
 //     lambda_t = ds_t C_t + A-bar_{t+1} lambda_{t+1},   ds_t = dy_t silu(z_t)
-// runs backwards in time; with hp_t = A-bar_t h_{t-1} = h_t - Delta_t B_t x_t
+// runs backwards in time; with hp_t = A-bar_t h_{t-1}, formed as the product
+// of A-bar_t with the previous state (kept from the forward replay), not as
+// the difference h_t - Delta_t B_t x_t, which cancels for channels that reset
+// (A-bar ~ 0: h_t is then almost all input term),
 //     dx_t      = Dskip ds_t + sum_n lambda_t Delta_t B_t
 //     dDelta_t  = sum_n lambda_t (A hp_t + B_t x_t),   ddt_t = dDelta_t sigmoid(u_t)
 //     dA[d,n]  += lambda_t Delta_t hp_t                 dBm[b,n,t] += lambda_t Delta_t x_t

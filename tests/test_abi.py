@@ -84,6 +84,71 @@ def test_host_only_entry_points():
     assert L.ssm_scan_fwd_workspace_bytes(4, 5120, 2048, 16) == 0
 
 
+# ---------------------------------------------------------------- CPU: broadcast views
+# The C ABI reads a stride of 0 as "dense default", so a broadcast view (an
+# expand()-ed tensor: stride 0 on a dimension of size > 1) passed through
+# unchanged would make the kernels read past its one stored copy.  The binding
+# must refuse such views before anything reaches the library.  CPU tensors
+# suffice: the view checks come before the device check.
+def _scan_inputs(batch=2, dim=8, L=40, N=4, dtype=torch.float32):
+    g = torch.Generator().manual_seed(0)
+    r = lambda *s: torch.randn(*s, generator=g).to(dtype)
+    return dict(x=r(batch, dim, L), dt=r(batch, dim, L), A=-torch.rand(dim, N), Bm=r(batch, N, L),
+                Cm=r(batch, N, L), z=r(batch, dim, L))
+
+
+@pytest.mark.parametrize("which", ["Bm_batch", "Cm_state", "x_batch", "x_channel", "z_channel",
+                                   "dt_batch"])
+def test_binding_rejects_broadcast_views_scan(which):
+    t = _scan_inputs()
+    name, how = which.split("_")
+    full = t[name]
+    if how == "batch":
+        t[name] = full[:1].expand(*full.shape)
+    elif how == "channel" or how == "state":
+        t[name] = full[:, :1].expand(*full.shape)
+    assert 0 in t[name].stride()
+    with pytest.raises(ValueError, match="broadcast"):
+        ssm.ssm_scan_fwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], z=t["z"], y=torch.empty(2, 8, 40),
+                         hL=torch.empty(2, 8, 4))
+    with pytest.raises(ValueError, match="broadcast"):
+        ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], torch.randn(2, 8, 40), z=t["z"],
+                         dx=torch.empty(2, 8, 40), ddt=torch.empty(2, 8, 40), dz=torch.empty(2, 8, 40),
+                         workspace=torch.empty(1, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("which", ["x", "Bm", "Cm", "z", "dt"])
+def test_binding_rejects_broadcast_views_decode(which):
+    batch, dim, N = 3, 8, 4
+    t = {k: torch.randn(batch, n) for k, n in (("x", dim), ("dt", dim), ("z", dim), ("Bm", N),
+                                                ("Cm", N))}
+    t[which] = t[which][:1].expand(batch, t[which].shape[1])
+    assert t[which].stride(0) == 0
+    with pytest.raises(ValueError, match="broadcast"):
+        ssm.ssm_state_update(torch.zeros(batch, dim, N), t["x"], t["dt"], -torch.rand(dim, N),
+                             t["Bm"], t["Cm"], z=t["z"], y=torch.empty(batch, dim))
+
+
+def test_binding_rejects_broadcast_views_conv():
+    x = torch.randn(1, 8, 40).expand(3, 8, 40)
+    with pytest.raises(ValueError, match="broadcast"):
+        ssm.ssm_conv1d_fwd(x, torch.randn(8, 4), y=torch.empty(3, 8, 40), return_final_state=False)
+    with pytest.raises(ValueError, match="broadcast"):
+        ssm.ssm_conv1d_update(torch.zeros(3, 8, 3), torch.randn(1, 8).expand(3, 8), torch.randn(8, 4),
+                              y=torch.empty(3, 8))
+
+
+def test_binding_accepts_size_one_strides():
+    """A size-1 dimension may carry any stride (it is never stepped over):
+    such views pass the view checks and only fail the device check here."""
+    x = torch.randn(1, 8, 40).expand(1, 8, 40)
+    x2 = torch.randn(8, 1, 40).transpose(0, 1)  # batch 1, odd strides
+    for v in (x, x2):
+        with pytest.raises(TypeError, match="CUDA"):
+            ssm.ssm_scan_fwd(v, v, -torch.rand(8, 4), torch.randn(1, 4, 40), torch.randn(1, 4, 40),
+                             y=torch.empty(1, 8, 40), hL=torch.empty(1, 8, 4))
+
+
 # ---------------------------------------------------------------- GPU: errors
 def _bufs(batch=2, dim=8, L=40, N=16, dtype=torch.bfloat16):
     g = torch.Generator().manual_seed(0)

@@ -201,3 +201,43 @@ def test_concurrent_streams():
                 assert rel_err(o[k].cpu().numpy()[None], r[k].cpu().numpy()[None]) <= 1e-6, k
             else:
                 assert torch.equal(r[k], o[k]), (fn.__name__, k)
+
+
+def test_explicit_stream_argument():
+    """Calls given stream= (a stream that is not the current one) allocate
+    their outputs and workspace on that stream: a split forward and a backward
+    pass whose workspaces the binding allocates, followed at once by
+    allocations and writes on the current stream, give the same bits as the
+    same calls on the current stream (the backward's atomic sums within fp32
+    rounding)."""
+    s = _dev_all(synth.make_inputs(workload("es_s", 1, 32, 16, 8192, "f32", seed=81)))
+    c = _dev_all(synth.make_inputs(workload("es_c", 1, 24, 16, 6000, "bf16", seed=82)))
+    assert ssm.lib().ssm_scan_fwd_workspace_bytes(1, 32, 8192, 16) > 0
+    assert ssm.lib().ssm_scan_fwd_workspace_bytes(1, 24, 6000, 16) > 0  # split backward too
+    dy = torch.randn(1, 24, 6000, device="cuda")
+    atomic = {"dA", "dBm", "dCm", "dDskip", "ddt_bias"}
+
+    def run(stream=None):
+        y, hL = _scan(s, stream=stream)
+        g = ssm.ssm_scan_bwd(c["x"], c["dt"], c["A"], c["Bm"], c["Cm"], dy, dt_bias=c["dt_bias"],
+                             Dskip=c["Dskip"], z=c["z"], stream=stream)
+        out = {k: v for k, v in g.items() if v is not None}
+        out.update(y=y, hL=hL)
+        return out
+
+    ref = {k: v.clone() for k, v in run().items()}
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    out = run(stream=side)
+    # work on the current stream that would reuse any block the call freed on it
+    junk = [torch.full((1 << 20,), 7.0, device="cuda") for _ in range(16)]
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    assert all(bool((j == 7.0).all()) for j in junk)
+    for k in ref:
+        if k in atomic:
+            assert rel_err(out[k].cpu().numpy()[None], ref[k].cpu().numpy()[None]) <= 1e-6, k
+        else:
+            assert torch.equal(ref[k], out[k]), k
