@@ -187,6 +187,32 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
                                   const ssm_scan_layout_t *layout, void *stream);
 
 /*
+ * ssm_scan_fwd_strided without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call itself allocates nothing either.
+ * Where ssm_scan_fwd_workspace_bytes(...) is non-zero (a sequence split), the
+ * split's planes go to a scratch array inside the library: one copy per GPU,
+ * 4 456 448 bytes (4096 x 16 x 17 floats), held from the library's first use
+ * on that GPU until the process ends.  Every split shape fits in it (the
+ * split makes segments x batch x dim at most 4096 x 16); a shape that did not
+ * would be SSM_ERR_WORKSPACE.  All calls on one GPU share that GPU's array:
+ * calls that overlap in time on the same GPU (on other streams or from other
+ * threads) race on it and must be serialised by the caller.  Nothing in it
+ * needs clearing between calls.  `stream` must belong to the current device.
+ * Arguments, layout, results and errors are those of ssm_scan_fwd_strided,
+ * except that SSM_FLAG_CHECKPOINTS (which needs the backward pass's
+ * workspace) is SSM_ERR_UNSUPPORTED.  The device address of the array is
+ * looked up on the first call on each device; a failure there is SSM_ERR_HIP.
+ * Results equal those of ssm_scan_fwd_strided bit for bit (same kernels).
+ */
+ssm_status_t ssm_scan_fwd_noalloc(int batch, int dim, int seqlen, int dstate,
+                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                                  float *hL, const ssm_scan_layout_t *layout, void *stream);
+
+/*
  * One decode step (seqlen = 1) on a persistent state.
  *   state    [batch][dim][dstate]   fp32, read and overwritten in place
  *   x, dt    [batch][dim]           in_dtype

@@ -36,7 +36,8 @@ STATUS = {
     7: "SSM_ERR_WORKSPACE", 8: "SSM_ERR_HIP",
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
-           "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_state_update", "ssm_state_update_strided",
+           "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_scan_fwd_noalloc",
+           "ssm_state_update", "ssm_state_update_strided",
            "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided", "ssm_conv1d_update",
            "ssm_conv1d_update_strided",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_strided"]
@@ -96,6 +97,9 @@ def lib():
         L.ssm_scan_fwd_strided.restype = i
         L.ssm_scan_fwd_strided.argtypes = ([i, i, i, i, i, u] + [vp] * 9 +
                                            [i, vp, vp, vp, sz, ctypes.POINTER(ScanLayout), vp])
+        L.ssm_scan_fwd_noalloc.restype = i
+        L.ssm_scan_fwd_noalloc.argtypes = ([i, i, i, i, i, u] + [vp] * 9 +
+                                           [i, vp, vp, ctypes.POINTER(ScanLayout), vp])
         L.ssm_state_update_strided.restype = i
         L.ssm_state_update_strided.argtypes = ([i, i, i, i, u] + [vp] * 9 +
                                                [i, vp, ctypes.POINTER(UpdateLayout), vp])
@@ -295,6 +299,35 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
     st = lib().ssm_scan_fwd_strided(batch, dim, L, N, _dtype_code(ind), flags, *args,
                                     _dtype_code(y.dtype), yp, hp, wp, wb, ctypes.byref(layout),
                                     _stream(stream, x.device))
+    _check(st)
+    return y, hL
+
+
+def ssm_scan_fwd_noalloc(x, dt, A, Bm, Cm, *, y, hL=None, dt_bias=None, Dskip=None, z=None,
+                         h0=None, zoh=False, stream=None):
+    """ssm_scan_fwd through the allocation-free entry point: nothing is
+    allocated, here or in the library (y, and hL if wanted, are given by the
+    caller; a sequence split uses the library's per-GPU scratch array, so
+    calls overlapping in time on one GPU must be serialised).  Returns (y, hL)."""
+    _no_broadcast_args(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, dt_bias=dt_bias, Dskip=Dskip, z=z, h0=h0,
+                       y=y, hL=hL)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, dim, L]")
+    batch, dim, L = x.shape
+    N = A.shape[-1]
+    ind, f32 = x.dtype, torch.float32
+    (xp, dtp, zp, yp), row, seq_b = _rows(
+        (x, dt, z, y), ("x", "dt", "z", "y"), (batch, dim, L),
+        {"x": ind, "dt": ind, "z": ind, "y": y.dtype})
+    (Bp, Cp), bc_row, bc_b = _rows((Bm, Cm), ("Bm", "Cm"), (batch, N, L), ind)
+    layout = ScanLayout(row, (ctypes.c_longlong * 4)(*seq_b), bc_row,
+                        (ctypes.c_longlong * 2)(*bc_b))
+    st = lib().ssm_scan_fwd_noalloc(
+        batch, dim, L, N, _dtype_code(ind), SSM_FLAG_ZOH_B if zoh else 0, xp, dtp,
+        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32), Bp, Cp,
+        _ptr(Dskip, "Dskip", (dim,), f32), zp, _ptr(h0, "h0", (batch, dim, N), f32),
+        _dtype_code(y.dtype), yp, _ptr(hL, "hL", (batch, dim, N), f32), ctypes.byref(layout),
+        _stream(stream, x.device))
     _check(st)
     return y, hL
 

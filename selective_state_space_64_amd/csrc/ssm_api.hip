@@ -7,6 +7,8 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ssm_launch.hpp"
 
 namespace {
@@ -69,6 +71,134 @@ bool batch_span(long long given, int batch, int rows, long long rs, int seqlen, 
     return true;
 }
 
+// Device scratch of ssm_scan_fwd_noalloc: a file-scope array, one copy per
+// GPU (held from the library's first use on that GPU until the process
+// ends).  It holds the sequence split's planes, at most kScratchBytes: the
+// split gives at most 4096 / (batch * ceil(dim / 16)) segments, so segments x
+// batch x dim <= 4096 * 16, times (dstate + 1) <= 17 floats.  In host code
+// the array's name is only a stand-in for the symbol; its device address
+// comes from hipGetSymbolAddress, once per device, and only that address is
+// ever handed to a kernel.  Every call on a GPU shares that GPU's copy, so
+// calls that overlap in time on one GPU (other streams, other threads) race
+// on it.  Nothing in it needs clearing between calls: the aggregate pass
+// writes every plane the main pass reads.
+constexpr size_t kScratchBytes = size_t(4096) * 16 * 17 * sizeof(float);
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on that device).
+hipError_t scratch_address(float **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+// ssm_scan_fwd_strided, and with noalloc set ssm_scan_fwd_noalloc: the
+// split's planes then go to the library's own scratch array instead of the
+// caller's workspace (which must be NULL), and checkpoints are refused.
+ssm_status_t scan_fwd_impl(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+                           unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                           const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                           const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                           float *hL, void *workspace, size_t workspace_bytes,
+                           const ssm_scan_layout_t *layout, void *stream, bool noalloc)
+{
+    if (!x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
+        return SSM_ERR_BAD_SHAPE;
+    if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS)) != 0)
+        return SSM_ERR_UNSUPPORTED;
+    if (noalloc && (flags & SSM_FLAG_CHECKPOINTS)) return SSM_ERR_UNSUPPORTED;
+
+    const size_t st_elems = mul3(batch, dim, dstate);
+    if (!mul3(batch, dim, seqlen) || !mul3(batch, dstate, seqlen) || !st_elems)
+        return SSM_ERR_BAD_SHAPE;
+    const ssm_scan_layout_t dense{};
+    const ssm_scan_layout_t &lay = layout ? *layout : dense;
+    // Strides with defaults filled in, and each tensor's span in elements.
+    long long row, bc_row, seq_b[4], bc_b[2];
+    size_t seq_span[4], bc_span[2];
+    if (!row_stride(lay.seq_row, seqlen, row) || !row_stride(lay.bc_row, seqlen, bc_row))
+        return SSM_ERR_BAD_SHAPE;
+    for (int i = 0; i < 4; ++i)
+        if (!batch_span(lay.seq_batch[i], batch, dim, row, seqlen, seq_b[i], seq_span[i]))
+            return SSM_ERR_BAD_SHAPE;
+    for (int i = 0; i < 2; ++i)
+        if (!batch_span(lay.bc_batch[i], batch, dstate, bc_row, seqlen, bc_b[i], bc_span[i]))
+            return SSM_ERR_BAD_SHAPE;
+    const bool ckpt = (flags & SSM_FLAG_CHECKPOINTS) != 0;
+    const size_t split_bytes = ssm::scan_fwd_split_bytes(batch, dim, seqlen, dstate);
+    // Bytes of the workspace this call uses: the backward pass's workspace
+    // with checkpoints (the split's planes then follow the checkpoints),
+    // otherwise the split's planes, if any.
+    const size_t ws_bytes = noalloc ? 0
+                            : ckpt  ? ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate)
+                                    : split_bytes;
+    if (ckpt && !workspace) return SSM_ERR_NULL_ARG;
+    if (noalloc && split_bytes > kScratchBytes) return SSM_ERR_WORKSPACE;
+
+    const size_t in = dsize(in_dtype);
+    for (const void *p : {x, dt, Bm, Cm, z})
+        if (misaligned(p, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)dt_bias, (const void *)A, (const void *)Dskip,
+                          (const void *)h0, (const void *)hL})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+    if (ws_bytes && misaligned(workspace, 4)) return SSM_ERR_MISALIGNED;
+
+    const size_t ybytes = seq_span[3] * dsize(out_dtype);
+    const size_t hbytes = st_elems * sizeof(float);
+    if (workspace_bytes < ws_bytes || (ws_bytes && !workspace)) return SSM_ERR_WORKSPACE;
+    struct In {
+        const void *p;
+        size_t bytes;
+    } inputs[] = {{x, seq_span[0] * in}, {dt, seq_span[1] * in},    {dt_bias, dim * sizeof(float)},
+                  {A, size_t(dim) * dstate * sizeof(float)},
+                  {Bm, bc_span[0] * in}, {Cm, bc_span[1] * in},     {Dskip, dim * sizeof(float)},
+                  {z, seq_span[2] * in}, {h0, hbytes}};
+    for (const In &i : inputs) {
+        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        // hL may be exactly h0 (read before written per channel), nothing else
+        if (hL && !(i.p == h0 && hL == h0) && overlaps(hL, hbytes, i.p, i.bytes))
+            return SSM_ERR_ALIAS;
+        if (overlaps(workspace, ws_bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, ybytes, hL, hbytes)) return SSM_ERR_ALIAS;
+    if (overlaps(workspace, ws_bytes, y, ybytes) || overlaps(workspace, ws_bytes, hL, hbytes))
+        return SSM_ERR_ALIAS;
+
+    float *ws = static_cast<float *>(workspace);
+    const size_t ck_floats = ssm::scan_checkpoint_floats(batch, dim, seqlen, dstate);
+    float *agg = split_bytes ? (ckpt ? ws + ck_floats : ws) : nullptr;
+    if (noalloc) {
+        float *own = nullptr;
+        if (scratch_address(&own) != hipSuccess) return SSM_ERR_HIP;
+        agg = split_bytes ? own : nullptr;
+    }
+    ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                    (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,
+                    ckpt ? ws : nullptr,
+                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], bc_row, bc_b[0], bc_b[1], agg, 0};
+    const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,77 +249,20 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
                                   float *hL, void *workspace, size_t workspace_bytes,
                                   const ssm_scan_layout_t *layout, void *stream)
 {
-    if (!x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
-    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
-    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
-        return SSM_ERR_BAD_SHAPE;
-    if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS)) != 0)
-        return SSM_ERR_UNSUPPORTED;
+    return scan_fwd_impl(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A, Bm, Cm,
+                         Dskip, z, h0, out_dtype, y, hL, workspace, workspace_bytes, layout, stream,
+                         false);
+}
 
-    const size_t st_elems = mul3(batch, dim, dstate);
-    if (!mul3(batch, dim, seqlen) || !mul3(batch, dstate, seqlen) || !st_elems)
-        return SSM_ERR_BAD_SHAPE;
-    const ssm_scan_layout_t dense{};
-    const ssm_scan_layout_t &lay = layout ? *layout : dense;
-    // Strides with defaults filled in, and each tensor's span in elements.
-    long long row, bc_row, seq_b[4], bc_b[2];
-    size_t seq_span[4], bc_span[2];
-    if (!row_stride(lay.seq_row, seqlen, row) || !row_stride(lay.bc_row, seqlen, bc_row))
-        return SSM_ERR_BAD_SHAPE;
-    for (int i = 0; i < 4; ++i)
-        if (!batch_span(lay.seq_batch[i], batch, dim, row, seqlen, seq_b[i], seq_span[i]))
-            return SSM_ERR_BAD_SHAPE;
-    for (int i = 0; i < 2; ++i)
-        if (!batch_span(lay.bc_batch[i], batch, dstate, bc_row, seqlen, bc_b[i], bc_span[i]))
-            return SSM_ERR_BAD_SHAPE;
-    const bool ckpt = (flags & SSM_FLAG_CHECKPOINTS) != 0;
-    const size_t split_bytes = ssm::scan_fwd_split_bytes(batch, dim, seqlen, dstate);
-    // Bytes of the workspace this call uses: the backward pass's workspace
-    // with checkpoints (the split's planes then follow the checkpoints),
-    // otherwise the split's planes, if any.
-    const size_t ws_bytes = ckpt ? ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate)
-                                 : split_bytes;
-    if (ckpt && !workspace) return SSM_ERR_NULL_ARG;
-
-    const size_t in = dsize(in_dtype);
-    for (const void *p : {x, dt, Bm, Cm, z})
-        if (misaligned(p, in)) return SSM_ERR_MISALIGNED;
-    for (const void *p : {(const void *)dt_bias, (const void *)A, (const void *)Dskip,
-                          (const void *)h0, (const void *)hL})
-        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
-    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
-    if (ws_bytes && misaligned(workspace, 4)) return SSM_ERR_MISALIGNED;
-
-    const size_t ybytes = seq_span[3] * dsize(out_dtype);
-    const size_t hbytes = st_elems * sizeof(float);
-    if (workspace_bytes < ws_bytes || (ws_bytes && !workspace)) return SSM_ERR_WORKSPACE;
-    struct In {
-        const void *p;
-        size_t bytes;
-    } inputs[] = {{x, seq_span[0] * in}, {dt, seq_span[1] * in},    {dt_bias, dim * sizeof(float)},
-                  {A, size_t(dim) * dstate * sizeof(float)},
-                  {Bm, bc_span[0] * in}, {Cm, bc_span[1] * in},     {Dskip, dim * sizeof(float)},
-                  {z, seq_span[2] * in}, {h0, hbytes}};
-    for (const In &i : inputs) {
-        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
-        // hL may be exactly h0 (read before written per channel), nothing else
-        if (hL && !(i.p == h0 && hL == h0) && overlaps(hL, hbytes, i.p, i.bytes))
-            return SSM_ERR_ALIAS;
-        if (overlaps(workspace, ws_bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
-    }
-    if (overlaps(y, ybytes, hL, hbytes)) return SSM_ERR_ALIAS;
-    if (overlaps(workspace, ws_bytes, y, ybytes) || overlaps(workspace, ws_bytes, hL, hbytes))
-        return SSM_ERR_ALIAS;
-
-    float *ws = static_cast<float *>(workspace);
-    const size_t ck_floats = ssm::scan_checkpoint_floats(batch, dim, seqlen, dstate);
-    float *agg = split_bytes ? (ckpt ? ws + ck_floats : ws) : nullptr;
-    ssm::ScanArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
-                    (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,
-                    ckpt ? ws : nullptr,
-                    row, seq_b[0], seq_b[1], seq_b[2], seq_b[3], bc_row, bc_b[0], bc_b[1], agg, 0};
-    const hipError_t e = ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+ssm_status_t ssm_scan_fwd_noalloc(int batch, int dim, int seqlen, int dstate,
+                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                                  float *hL, const ssm_scan_layout_t *layout, void *stream)
+{
+    return scan_fwd_impl(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A, Bm, Cm,
+                         Dskip, z, h0, out_dtype, y, hL, nullptr, 0, layout, stream, true);
 }
 
 ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
