@@ -368,6 +368,71 @@ def ssm_state_update(state, x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=Non
     return y
 
 
+class StateUpdateSteps:
+    """Token-by-token decode over step-major buffers with the arguments
+    checked once: the per-token call is a pointer offset and one C call.
+
+        steps = StateUpdateSteps(state, A, xs, dts, Bs, Cs, ys=ys, dt_bias=..., Dskip=..., zs=...)
+        for s in range(n): steps(s)      # = ssm_state_update(state, xs[s], ..., y=ys[s])
+
+    xs, dts, zs, ys are [steps, batch, dim] and Bs, Cs [steps, batch, N]
+    tensors (any of them may instead be [batch, dim] / [batch, N], reused
+    for every step), each step's slice a batch-strided view as
+    ssm_state_update accepts.  The buffers must stay alive and in place while
+    the object is used; the stream is fixed at construction (the current one
+    by default).  The library still validates every call."""
+
+    def __init__(self, state, A, xs, dts, Bs, Cs, *, ys, dt_bias=None, Dskip=None, zs=None,
+                 zoh=False, stream=None):
+        _no_broadcast_args(state=state, A=A, xs=xs, dts=dts, Bs=Bs, Cs=Cs, ys=ys, dt_bias=dt_bias,
+                           Dskip=Dskip, zs=zs)
+        batch, dim, N = state.shape
+        ind, f32 = xs.dtype, torch.float32
+        self.nsteps = None
+        per = []   # (base pointer, bytes per step) of x, dt, z, y, Bm, Cm
+        bstr = []  # batch strides (0 = dense)
+        for t, name, n, dtype in ((xs, "xs", dim, ind), (dts, "dts", dim, ind), (zs, "zs", dim, ind),
+                                  (ys, "ys", dim, None), (Bs, "Bs", N, ind), (Cs, "Cs", N, ind)):
+            if t is None:
+                per.append((None, 0))
+                bstr.append(0)
+                continue
+            if dtype is not None and t.dtype != dtype:
+                raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+            one = t[0] if t.dim() == 3 else t
+            p, sb = _bptr(one, name, (batch, n), t.dtype)
+            if t.dim() == 3:
+                if self.nsteps is not None and t.shape[0] != self.nsteps:
+                    raise ValueError("%s has %d steps, expected %d" % (name, t.shape[0], self.nsteps))
+                self.nsteps = t.shape[0]
+                per.append((p, t.stride(0) * t.element_size()))
+            else:
+                per.append((p, 0))
+            bstr.append(sb)
+        self._per = per
+        self._layout = UpdateLayout(*bstr) if any(bstr) else None
+        self._lp = None if self._layout is None else ctypes.byref(self._layout)
+        self._fixed = (batch, dim, N, _dtype_code(ind), SSM_FLAG_ZOH_B if zoh else 0,
+                       _ptr(state, "state", (batch, dim, N), f32))
+        self._bias = _ptr(dt_bias, "dt_bias", (dim,), f32)
+        self._A = _ptr(A, "A", (dim, N), f32)
+        self._D = _ptr(Dskip, "Dskip", (dim,), f32)
+        self._out = _dtype_code(ys.dtype)
+        self._stream = _stream(stream, state.device)
+        self._fn = lib().ssm_state_update_strided
+        self._keep = (state, A, xs, dts, Bs, Cs, ys, dt_bias, Dskip, zs)
+
+    def __call__(self, s):
+        if self.nsteps is not None and not 0 <= s < self.nsteps:
+            raise IndexError("step %d of %d" % (s, self.nsteps))
+        (x, xs), (d, ds), (z, zs), (y, ys), (b, bs), (c, cs) = self._per
+        st = self._fn(*self._fixed, x + s * xs, d + s * ds, self._bias, self._A, b + s * bs,
+                      c + s * cs, self._D, None if z is None else z + s * zs, self._out, y + s * ys,
+                      self._lp, self._stream)
+        if st != 0:
+            _check(st)
+
+
 @_on_caller_stream
 def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=None, dhL=None,
                  grad_dtype=torch.float32, workspace=None, checkpoints_in_workspace=False,

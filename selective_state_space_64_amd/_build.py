@@ -10,6 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssm.so")
+PEAKS_LIB = os.path.join(HERE, "libssm_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["ssm_api.hip", "scan_fwd.hip", "state_update.hip", "conv1d.hip", "scan_bwd.hip"]
 ARCH = "gfx950"
@@ -34,18 +35,25 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose=False):
+    """libssm.so (the library) and libssm_peaks.so (the issue-rate probes
+    the benchmark reports beside the nominal peaks)."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + ["peaks.hip"]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PEAKS_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, PEAKS_LIB)
     return LIB
 
 

@@ -67,15 +67,54 @@ def test_counter_ingestion_scales_by_the_copy(tmp_path, monkeypatch):
                             str(tmp_path / "copyw"), copy_mib=1, workload="w")
     assert rec["copy_calibration"]["fetch_scale"] == 2.0
     assert rec["copy_calibration"]["write_scale"] == 1.0
-    assert rec["fetch_size_kib_per_dispatch"] == 200.0
+    assert rec["fetch_size_kib_per_dispatch"] == {b.SCAN_KERNEL: 200.0}
     assert rec["traffic_bytes_per_launch"] == (200.0 * 2 + 50.0) * 1024
-    assert json.loads(out.read_text()) == rec
+    assert json.loads(out.read_text()) == {"w": rec}
     # read back for the same sources and workload; another workload gets none
     assert b.counter_traffic("w") == rec["traffic_bytes_per_launch"]
     assert b.counter_traffic("another workload") is None
     # a changed kernel source (another hash) makes the stored traffic stale
     monkeypatch.setattr(b, "kernel_sources_sha256", lambda: "0" * 64)
     assert b.counter_traffic("w") is None
+
+
+def test_counter_ingestion_sums_the_kernels_of_a_step(tmp_path, monkeypatch):
+    """A split step is two launches (aggregate pass, main pass): its traffic
+    is the sum of both kernels' per-dispatch means; records of several
+    workloads live side by side in the one file."""
+    b = _bench()
+    out = tmp_path / "counters.json"
+    monkeypatch.setattr(b, "COUNTERS", str(out))
+    main, agg = b.scan_kernel_name("f32"), b.scan_kernel_name("f32", agg=True)
+    assert main != agg and "true, true>" in agg
+    _write_counters(tmp_path / "fetch", [(main, "FETCH_SIZE", 100.0), (agg, "FETCH_SIZE", 60.0),
+                                         (agg, "FETCH_SIZE", 80.0)])
+    _write_counters(tmp_path / "write", [(main, "WRITE_SIZE", 30.0), (agg, "WRITE_SIZE", 2.0)])
+    _write_counters(tmp_path / "copyf", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", 1024.0)])
+    _write_counters(tmp_path / "copyw", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024.0)])
+    dirs = [str(tmp_path / d) for d in ("fetch", "write", "copyf", "copyw")]
+    r1 = b.ingest_counters(*dirs, copy_mib=1, workload="long", kernels=(main, agg))
+    assert r1["traffic_bytes_per_launch"] == (100.0 + 70.0 + 30.0 + 2.0) * 1024
+    r2 = b.ingest_counters(*dirs, copy_mib=1, workload="layer", kernels=(main,))
+    stored = json.loads(out.read_text())
+    assert stored == {"long": r1, "layer": r2}
+    assert b.counter_traffic("long") == r1["traffic_bytes_per_launch"]
+    assert b.counter_traffic("layer") == (100.0 + 30.0) * 1024
+
+
+def test_roofline_picks_the_binding_roof():
+    b = _bench()
+    # the 2.8B layer: ALU time (slots / 78.6 T) exceeds the HBM time (bytes / 8 TB/s)
+    r = b.roofline(4, 5120, 2048, 16, 2, 200e-6)
+    assert r["bound"] == "alu"
+    assert r["hbm"]["min_seconds"] < b.algorithmic_slots(4, 5120, 2048, 16) / b.PEAK_SLOTS
+    assert r["frac"] == pytest.approx(b.algorithmic_slots(4, 5120, 2048, 16) / 200e-6 / b.PEAK_SLOTS)
+    # the fp32 2^20-step sequence: 16 bytes per (b, d, l) put HBM ahead
+    r = b.roofline(1, 1536, 1 << 20, 16, 4, 15e-3)
+    assert r["bound"] == "hbm"
+    assert r["algorithmic_bytes"] == b.algorithmic_bytes(1, 1536, 1 << 20, 16, 4, 4)
+    assert r["frac"] == pytest.approx(r["algorithmic_bytes"] / 15e-3 / b.PEAK_HBM)
+    assert r["alu"]["min_seconds"] < r["algorithmic_bytes"] / b.PEAK_HBM
 
 
 def test_ingestion_without_samples_fails_loudly(tmp_path, monkeypatch):

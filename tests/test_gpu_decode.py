@@ -1,5 +1,6 @@
 """GPU parity of ssm_state_update (through the C ABI) against the fp64 oracle:
-the 256-step decode workload on a [64, 5120, 16] fp32 state updated in place,
+the 256-step decode workload on a [64, 5120, 16] fp32 state updated in place
+(in full),
 small shapes compared in full, and shapes that take the four-rows-per-lane
 launch compared in full.  The oracle side runs the same steps as
 one scan from the initial state (the decode recurrence and the scan are the
@@ -49,20 +50,57 @@ def _oracle_decode(inp, rows, gate=True):
     return np.stack(ys), np.stack(hs)
 
 
-def test_decode_workload_sampled():
+def test_decode_workload_full():
+    """The decode workload in full: 256 steps on the [64, 5120, 16] state,
+    every y of every step and every final state value against the oracle
+    (the steps run there as one scan from the initial state).  y is compared
+    over rows of channels (b, :) per step, the state over (b, d, :)."""
     wl = synth.WORKLOADS[4]
     print("workload", wl.name, flush=True)
     inp = synth.make_inputs(wl)
     ys, state = _run_decode(inp, wl.seqlen)
-    rows = sample_rows(wl.batch, wl.dim, per_batch=4, seed=4)[::3]
-    bi = torch.tensor([r[0] for r in rows], device="cuda")
-    di = torch.tensor([r[1] for r in rows], device="cuda")
-    gy = ys[:, bi, di].T.cpu().numpy()
-    gh = state[bi, di].cpu().numpy()
-    ry, rh = _oracle_decode(inp, rows)
-    ey, eh = rel_err(gy, ry), rel_err(gh, rh)
-    print("  %d rows x %d steps: err y %.3e state %.3e" % (len(rows), wl.seqlen, ey, eh), flush=True)
+    gy, gh = ys.cpu().numpy(), state.cpu().numpy()    # [steps, batch, dim], [batch, dim, N]
+    del ys, state
+    assert np.isfinite(gy).all() and np.isfinite(gh).all()
+    ry, rh = oracle_full(inp, h0=inp.h0)             # [batch, dim, steps], [batch, dim, N]
+    ey = rel_err(gy, np.transpose(ry, (2, 0, 1)))
+    eh = rel_err(gh, rh)
+    print("  %d x %d rows x %d steps: err y %.3e state %.3e"
+          % (wl.batch, wl.dim, wl.seqlen, ey, eh), flush=True)
     assert ey <= tol_for("bf16") and eh <= tol_for("bf16")
+
+
+def test_decode_steps_object_matches_calls():
+    """StateUpdateSteps (arguments checked once, per step a pointer offset)
+    gives the same bits as ssm_state_update called per step, also with some
+    inputs given once for every step and x / z as projection halves."""
+    inp = synth.make_inputs(workload("decobj", 5, 300, 16, 6, "bf16", seed=41), with_h0=True)
+    ys_ref, st_ref = _run_decode(inp, 6)
+    state = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
+    xz = torch.cat([_steps(to_dev(inp, "x")), _steps(to_dev(inp, "z"))], dim=2)  # [steps, b, 2d]
+    xs, zs = xz[..., :300], xz[..., 300:]
+    dts = _steps(to_dev(inp, "dt"))
+    Bs, Cs = _steps(to_dev(inp, "Bm")), _steps(to_dev(inp, "Cm"))
+    A, Dk, bias = to_dev(inp, "A"), to_dev(inp, "Dskip"), to_dev(inp, "dt_bias")
+    ys = torch.empty((6, 5, 300), device="cuda")
+    run = ssm.StateUpdateSteps(state, A, xs, dts, Bs, Cs, ys=ys, dt_bias=bias, Dskip=Dk, zs=zs)
+    for s in range(6):
+        run(s)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, ys_ref) and torch.equal(state, st_ref)
+    with pytest.raises(IndexError):
+        run(6)
+    # Bm given once for every step: equals calls passing the same Bm each time
+    state2 = torch.from_numpy(inp.h0.astype(np.float32)).cuda()
+    state3 = state2.clone()
+    ys2, ys3 = torch.empty_like(ys), torch.empty_like(ys)
+    run2 = ssm.StateUpdateSteps(state2, A, xs, dts, Bs[0], Cs, ys=ys2, dt_bias=bias, Dskip=Dk, zs=zs)
+    for s in range(6):
+        run2(s)
+        ssm.ssm_state_update(state3, xs[s], dts[s], A, Bs[0], Cs[s], dt_bias=bias, Dskip=Dk, z=zs[s],
+                             y=ys3[s])
+    torch.cuda.synchronize()
+    assert torch.equal(ys2, ys3) and torch.equal(state2, state3)
 
 
 @pytest.mark.parametrize("shape", [(3, 7, 16, 5, "f32"), (2, 70, 4, 9, "bf16"), (1, 1, 1, 3, "f32"),
