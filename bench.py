@@ -753,6 +753,24 @@ def main():
         zfn()
     zms, _ = time_launches(torch, zfn, 10, stream)
     result["zoh_variant"] = {"kernel_ms_mean": zms, "elements_per_s": elems / (zms * 1e-3)}
+    # the same step on (batch, L, dim)-ordered copies of the inputs (ssm_scan_fwd_bld)
+    tb = {k: t[k].transpose(1, 2).contiguous() for k in ("x", "dt", "z", "Bm", "Cm")}
+    yb = torch.empty((wl.batch, wl.seqlen, wl.dim), device="cuda")
+    wsb = torch.empty(ssm.lib().ssm_scan_fwd_bld_workspace_bytes(wl.batch, wl.dim, wl.seqlen,
+                                                                 wl.dstate),
+                      dtype=torch.uint8, device="cuda")
+    bfn = lambda: ssm.ssm_scan_fwd_bld(tb["x"], tb["dt"], t["A"], tb["Bm"], tb["Cm"],
+                                       dt_bias=t["dt_bias"], Dskip=t["Dskip"], z=tb["z"], y=yb,
+                                       hL=hL, workspace=wsb)
+    for _ in range(3):
+        bfn()
+    bms, _ = time_launches(torch, bfn, 20, stream)
+    brf = roofline(wl.batch, wl.dim, wl.seqlen, wl.dstate, in_bytes, bms * 1e-3)
+    result["bld_layout"] = {"kernel_ms_mean": bms, "elements_per_s": elems / (bms * 1e-3),
+                            "over_bdl_time": bms / region_ms, "roofline_frac": brf["frac"],
+                            "note": "x, dt, z, y as [batch, L, dim], Bm, Cm as [batch, L, N]: "
+                                    "aggregate, combine and main launches"}
+    del tb, yb, wsb
     if not args.no_peaks:
         from selective_state_space_64_amd import peaks
         result["peaks"] = peaks.measure(torch)

@@ -98,7 +98,8 @@ const char *ssm_status_string(ssm_status_t status);
  * the workspace argument may then be NULL).  It is non-zero when the
  * sequence is split into segments scanned in parallel, which the library
  * does when batch x ceil(dim / 16) is small (under 256) and seqlen long
- * (segments of at least 1024 steps).  The recurrence is affine in the state,
+ * (segments of at least 1024 steps, a multiple of 256).  The recurrence is
+ * affine in the state,
  * so each segment but the last first runs from a zero state (h0 for the
  * first) to get its end state and Delta sum; the main pass then enters
  * segment s with the earlier segments composed,
@@ -131,7 +132,8 @@ size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
  *            with SSM_FLAG_CHECKPOINTS, the backward pass's workspace (at
  *            least ssm_scan_bwd_workspace_bytes(...) bytes), which receives
  *            the checkpoints and must not overlap any input or output
- * Supported sizes: batch <= 65535, seqlen <= 2^28 - 4096, dstate in {1, 2, 4, 8, 16}.
+ * Supported sizes: batch <= 65535, dim <= 2^30, seqlen <= 2^28 - 4096,
+ * dstate in {1, 2, 4, 8, 16}.
  */
 ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
                           unsigned flags, const void *x, const void *dt, const float *dt_bias,
@@ -213,6 +215,62 @@ ssm_status_t ssm_scan_fwd_noalloc(int batch, int dim, int seqlen, int dstate,
                                   float *hL, const ssm_scan_layout_t *layout, void *stream);
 
 /*
+ * The selective scan on tensors in (batch, L, dim) order: a time step's
+ * channels contiguous, time steps apart.  It is the order of the (B, L, D)
+ * output in the reading guide's "Hardware-aware state expansion" section and
+ * the order in which a model's input projection produces x and z, so those
+ * can be passed without a transpose (x and z as the two halves of one
+ * [batch][L][2 dim] projection output).
+ *   x, dt, z, y  element (b, t, d) at b * *_batch + t * *_step + d
+ *   Bm, Cm       element (b, t, n) at b * *_batch + t * *_step + n
+ *   A, Dskip, dt_bias, h0, hL as in ssm_scan_fwd (dense).
+ * Strides are in ELEMENTS of the tensor's own type; the channel (state)
+ * index is always contiguous.
+ *   x_step .. y_step   distance between time steps of x, dt, z, y; >= dim;
+ *                      0 means dim
+ *   x_batch .. y_batch distance between batch entries; >= seqlen * step;
+ *                      0 means seqlen * step
+ *   B_step, C_step     distance between time steps of Bm, Cm; >= dstate;
+ *                      0 means dstate
+ *   B_batch, C_batch   >= seqlen * step; 0 means seqlen * step
+ * A NULL layout means all zero (dense (batch, L, dim) and (batch, L, dstate)).
+ * A negative stride, one below its minimum, a step stride above 2^40 or a
+ * tensor spanning 2^56 elements or more is SSM_ERR_BAD_SHAPE.
+ */
+typedef struct {
+    long long x_step, dt_step, z_step, y_step;
+    long long x_batch, dt_batch, z_batch, y_batch;
+    long long B_step, C_step, B_batch, C_batch;
+} ssm_bld_layout_t;
+
+/* Device workspace ssm_scan_fwd_bld needs, in bytes (never 0 for valid
+ * sizes; 0 for sizes it refuses).  The kernels run channels along the lanes
+ * of a wave and cut the sequence into pieces walked by separate waves, so
+ * that enough waves run at once; the workspace holds, per piece and
+ * (batch, channel), the piece's map h -> exp(A sum Delta) h + e (dstate + 1
+ * floats), then the state entering it, composed in order with the scan's
+ * associative operator (the "Parallel Associative Scan" glossary entry). */
+size_t ssm_scan_fwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate);
+
+/*
+ * ssm_scan_fwd on (batch, L, dim)-ordered tensors, laid out by `layout`
+ * (host pointer, read during the call only).  Same arguments, results (up to
+ * the association order of the fp32 sums) and errors as ssm_scan_fwd, with:
+ *   workspace, workspace_bytes: at least ssm_scan_fwd_bld_workspace_bytes(...)
+ *            bytes, 4-byte aligned, overlapping no input or output (required)
+ *   flags:   SSM_FLAG_ZOH_B only (SSM_FLAG_CHECKPOINTS, whose checkpoints
+ *            feed the [batch][dim][L] backward pass, is SSM_ERR_UNSUPPORTED)
+ * Overlap is checked on address ranges from the first to the last element.
+ * Supported sizes: as ssm_scan_fwd.
+ */
+ssm_status_t ssm_scan_fwd_bld(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+                              unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                              const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                              const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                              float *hL, void *workspace, size_t workspace_bytes,
+                              const ssm_bld_layout_t *layout, void *stream);
+
+/*
  * One decode step (seqlen = 1) on a persistent state.
  *   state    [batch][dim][dstate]   fp32, read and overwritten in place
  *   x, dt    [batch][dim]           in_dtype
@@ -220,7 +278,7 @@ ssm_status_t ssm_scan_fwd_noalloc(int batch, int dim, int seqlen, int dstate,
  *   Bm, Cm   [batch][dstate]        in_dtype
  *   Dskip    [dim] fp32 or NULL;  z [batch][dim] in_dtype or NULL
  *   y        [batch][dim]           out_dtype; must not overlap any input or state
- * Supported sizes: batch <= 65535, dstate in {1, 2, 4, 8, 16}.
+ * Supported sizes: batch <= 65535, dim <= 2^30, dstate in {1, 2, 4, 8, 16}.
  */
 ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
                               unsigned flags, float *state, const void *x, const void *dt,

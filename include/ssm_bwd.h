@@ -49,7 +49,11 @@ extern "C" {
  * partial copies of dBm and dCm (8 * 2 * batch * dstate * seqlen fp32), or,
  * if larger, the forward's sequence-split workspace
  * (ssm_scan_fwd_workspace_bytes), which a forward with SSM_FLAG_CHECKPOINTS
- * keeps after the checkpoints. */
+ * keeps after the checkpoints; for a split shape, as many bytes again as the
+ * forward's split workspace follow (the backward's own adjoint planes).  A function of the sizes
+ * only; sizes ssm_scan_bwd would refuse (batch, dim or seqlen below 1,
+ * batch above 65535, seqlen above 2^28 - 4096, dstate not in {1, 2, 4, 8,
+ * 16}) give 0. */
 size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
 
 /*

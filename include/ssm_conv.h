@@ -50,7 +50,7 @@ extern "C" {
  *   stateL   [batch][dim][width-1] fp32 final conv state, or NULL (not
  *            returned); may be exactly state0 (each row reads its state0
  *            before writing stateL) but must not otherwise overlap an input or y
- * Supported sizes: batch, dim, seqlen >= 1 with batch * dim * seqlen < 2^62.
+ * Supported sizes: batch, dim, seqlen >= 1, dim <= 2^30, batch * dim * seqlen < 2^62.
  */
 ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype_t in_dtype,
                             unsigned flags, const void *x, const float *weight,

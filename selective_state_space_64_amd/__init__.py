@@ -37,6 +37,7 @@ STATUS = {
 }
 EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes",
            "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_scan_fwd_noalloc",
+           "ssm_scan_fwd_bld_workspace_bytes", "ssm_scan_fwd_bld",
            "ssm_state_update", "ssm_state_update_strided",
            "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided", "ssm_conv1d_update",
            "ssm_conv1d_update_strided",
@@ -47,6 +48,13 @@ class ScanLayout(ctypes.Structure):
     """ssm_scan_layout_t: strides in elements, 0 = dense default."""
     _fields_ = [("seq_row", ctypes.c_longlong), ("seq_batch", ctypes.c_longlong * 4),
                 ("bc_row", ctypes.c_longlong), ("bc_batch", ctypes.c_longlong * 2)]
+
+
+class BldLayout(ctypes.Structure):
+    """ssm_bld_layout_t: step and batch strides in elements, 0 = dense default."""
+    _fields_ = [(n, ctypes.c_longlong) for n in (
+        "x_step", "dt_step", "z_step", "y_step", "x_batch", "dt_batch", "z_batch", "y_batch",
+        "B_step", "C_step", "B_batch", "C_batch")]
 
 
 class BwdLayout(ctypes.Structure):
@@ -100,6 +108,11 @@ def lib():
         L.ssm_scan_fwd_noalloc.restype = i
         L.ssm_scan_fwd_noalloc.argtypes = ([i, i, i, i, i, u] + [vp] * 9 +
                                            [i, vp, vp, ctypes.POINTER(ScanLayout), vp])
+        L.ssm_scan_fwd_bld_workspace_bytes.restype = sz
+        L.ssm_scan_fwd_bld_workspace_bytes.argtypes = [i, i, i, i]
+        L.ssm_scan_fwd_bld.restype = i
+        L.ssm_scan_fwd_bld.argtypes = ([i, i, i, i, i, u] + [vp] * 9 +
+                                       [i, vp, vp, vp, sz, ctypes.POINTER(BldLayout), vp])
         L.ssm_state_update_strided.restype = i
         L.ssm_state_update_strided.argtypes = ([i, i, i, i, u] + [vp] * 9 +
                                                [i, vp, ctypes.POINTER(UpdateLayout), vp])
@@ -300,6 +313,74 @@ def ssm_scan_fwd(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
                                     _dtype_code(y.dtype), yp, hp, wp, wb, ctypes.byref(layout),
                                     _stream(stream, x.device))
     _check(st)
+    return y, hL
+
+
+def _steps(ts, names, shape, dtype):
+    """Pointers, step strides and batch strides (elements; 0 = dense default)
+    of [batch, L, n] tensors whose last index is contiguous."""
+    batch, L, n = shape
+    ptrs, st, sb = [], [], []
+    for t, name in zip(ts, names):
+        if t is None:
+            ptrs.append(None)
+            st.append(0)
+            sb.append(0)
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+        if t.shape != shape:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+        want = dtype[name] if isinstance(dtype, dict) else dtype
+        if t.dtype != want:
+            raise TypeError("%s must be %s, got %s" % (name, want, t.dtype))
+        _no_broadcast(t, name)
+        if n > 1 and t.stride(2) != 1:
+            raise ValueError("%s must have a contiguous last (channel) index" % name)
+        if not t.is_cuda:
+            raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+        ptrs.append(t.data_ptr())
+        st.append(t.stride(1) if L > 1 else 0)
+        sb.append(t.stride(0) if batch > 1 else 0)
+    return ptrs, st, sb
+
+
+@_on_caller_stream
+def ssm_scan_fwd_bld(x, dt, A, Bm, Cm, *, dt_bias=None, Dskip=None, z=None, h0=None,
+                     out_dtype=torch.float32, return_final_state=True, y=None, hL=None, zoh=False,
+                     workspace=None, stream=None):
+    """The selective scan on (batch, L, dim)-ordered tensors: x, dt, z, y are
+    [batch, L, dim] and Bm, Cm [batch, L, N], each with a contiguous last
+    index (views such as x and z as halves of one [batch, L, 2 dim]
+    projection output are taken as they are).  Returns (y, hL); y is
+    [batch, L, dim].  workspace: ssm_scan_fwd_bld_workspace_bytes(...) bytes,
+    allocated here when not given."""
+    _no_broadcast_args(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, dt_bias=dt_bias, Dskip=Dskip, z=z, h0=h0,
+                       y=y, hL=hL)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, L, dim]")
+    batch, L, dim = x.shape
+    N = A.shape[-1]
+    ind, f32 = x.dtype, torch.float32
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=out_dtype, device=x.device)
+    if hL is None and return_final_state:
+        hL = torch.empty((batch, dim, N), dtype=f32, device=x.device)
+    (xp, dtp, zp, yp), st, sb = _steps((x, dt, z, y), ("x", "dt", "z", "y"), (batch, L, dim),
+                                       {"x": ind, "dt": ind, "z": ind, "y": y.dtype})
+    (Bp, Cp), bst, bsb = _steps((Bm, Cm), ("Bm", "Cm"), (batch, L, N), ind)
+    layout = BldLayout(*st, *sb, *bst, *bsb)
+    need = lib().ssm_scan_fwd_bld_workspace_bytes(batch, dim, L, N)
+    if workspace is None:
+        workspace = torch.empty(max(1, need), dtype=torch.uint8, device=x.device)
+    st_ = lib().ssm_scan_fwd_bld(
+        batch, dim, L, N, _dtype_code(ind), SSM_FLAG_ZOH_B if zoh else 0, xp, dtp,
+        _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32), Bp, Cp,
+        _ptr(Dskip, "Dskip", (dim,), f32), zp, _ptr(h0, "h0", (batch, dim, N), f32),
+        _dtype_code(y.dtype), yp, _ptr(hL, "hL", (batch, dim, N), f32), _ptr(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), ctypes.byref(layout),
+        _stream(stream, x.device))
+    _check(st_)
     return y, hL
 
 

@@ -261,6 +261,12 @@ hipError_t launch_conv_typed(const ConvArgs &a, hipStream_t stream)
     const bool vec_out = vec16(a.y, sizeof(Tout), a.y_row, a.y_b);
     const long long blocks = (p.total_runs + kConvThreads - 1) / kConvThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (log_enabled())
+        log_line("conv1d_fwd: conv1d_fwd_kernel<in %s, out %s, W %d>, %lld runs of %d outputs, "
+                 "%lld workgroups x %d threads, %s-bit row index, vector in %d out %d",
+                 type_tag<Tin>(), type_tag<Tout>(), W, (long long)p.total_runs, kRun, blocks,
+                 kConvThreads, p.total_runs + kConvThreads <= (1ll << 32) ? "32" : "64",
+                 int(vec_in), int(vec_out));
     if (p.total_runs + kConvThreads <= (1ll << 32)) {
         const MagicDiv m = magic_div(unsigned(p.runs_per_row));
         p.div_mul = m.mul;
@@ -281,6 +287,9 @@ hipError_t launch_update_typed(const ConvUpdateArgs &a, hipStream_t stream)
     const long long rows = (long long)a.batch * a.dim;
     const long long blocks = (rows + kConvThreads - 1) / kConvThreads;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (log_enabled())
+        log_line("conv1d_update: conv1d_update_kernel<in %s, out %s, W %d>, %lld workgroups x %d "
+                 "threads", type_tag<Tin>(), type_tag<Tout>(), W, blocks, kConvThreads);
     hipLaunchKernelGGL((conv1d_update_kernel<Tin, Tout, W>), dim3(unsigned(blocks)),
                        dim3(kConvThreads), 0, stream, p, a.silu != 0);
     return hipGetLastError();

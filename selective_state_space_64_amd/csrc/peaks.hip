@@ -11,6 +11,8 @@
 //   kind 2  the scan's mix: per step and chain one exp2, one mul and three
 //           fma (the per-element work of the recurrence: Delta*A, exp, B x,
 //           state update, readout), eight chains per lane
+//   kind 3  v_fma_f32 with one wave-uniform (SGPR) operand, eight chains per
+//           lane: the form an operand shared by a whole wave takes
 // Each lane writes one float so that nothing is optimised away.  The grid
 // is sized by the caller; every access stays inside out[0 .. threads).
 #include <hip/hip_runtime.h>
@@ -21,7 +23,8 @@ constexpr int kChains = 8;
 constexpr int kThreads = 256;
 
 template <int kKind>
-__global__ __launch_bounds__(kThreads) void probe_kernel(float *out, int iters, float seed)
+__global__ __launch_bounds__(kThreads) void probe_kernel(float *out, int iters, float seed,
+                                                         float uniform)
 {
     const int tid = blockIdx.x * kThreads + threadIdx.x;
     float a[kChains];
@@ -39,6 +42,8 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(float *out, int iters, 
                 a[k] = __builtin_fmaf(a[k], m0, c0);
             } else if constexpr (kKind == 1) {
                 a[k] = __builtin_amdgcn_exp2f(-a[k]);  // stays in [0.5, 1]
+            } else if constexpr (kKind == 3) {
+                a[k] = __builtin_fmaf(a[k], uniform, c0);  // `uniform` lives in an SGPR
             } else {
                 const float e = __builtin_amdgcn_exp2f(a[k] * m1);  // mul + exp
                 float h = __builtin_fmaf(e, a[k], c1);              // state update
@@ -57,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void probe_kernel(float *out, int iters, 
 
 extern "C" {
 
-// Lane operations per thread of one launch of probe `kind` (0..2) with
+// Lane operations per thread of one launch of probe `kind` (0..3) with
 // `iters` iterations: instructions of the measured form, per lane.
 long long ssm_peaks_ops_per_thread(int kind, int iters)
 {
@@ -73,9 +78,10 @@ int ssm_peaks_launch(int kind, int blocks, int iters, float *out, void *stream)
     if (blocks < 1 || iters < 1 || !out) return -1;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     switch (kind) {
-    case 0: hipLaunchKernelGGL(probe_kernel<0>, dim3(blocks), dim3(kThreads), 0, s, out, iters, 0.5f); break;
-    case 1: hipLaunchKernelGGL(probe_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, out, iters, 0.5f); break;
-    case 2: hipLaunchKernelGGL(probe_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, out, iters, 0.5f); break;
+    case 0: hipLaunchKernelGGL(probe_kernel<0>, dim3(blocks), dim3(kThreads), 0, s, out, iters, 0.5f, 0.9999f); break;
+    case 1: hipLaunchKernelGGL(probe_kernel<1>, dim3(blocks), dim3(kThreads), 0, s, out, iters, 0.5f, 0.9999f); break;
+    case 2: hipLaunchKernelGGL(probe_kernel<2>, dim3(blocks), dim3(kThreads), 0, s, out, iters, 0.5f, 0.9999f); break;
+    case 3: hipLaunchKernelGGL(probe_kernel<3>, dim3(blocks), dim3(kThreads), 0, s, out, iters, 0.5f, 0.9999f); break;
     default: return -1;
     }
     return int(hipGetLastError());

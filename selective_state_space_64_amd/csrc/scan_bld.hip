@@ -1,0 +1,319 @@
+// scan_bld.hip -- the selective-scan forward on tensors in (batch, L, dim)
+// order: time steps apart, channels contiguous, the order in which the
+// reading guide's "Hardware-aware state expansion" section writes the
+// (B, L, D) output back, and in which a model's input projection produces x
+// and z.  Same computation as scan_fwd.hip ("Method" and "The selection
+// mechanism (S6)" sections of the page "Mamba: Linear-Time Sequence Modeling
+// with Selective State Spaces"):
+//     Delta_t = softplus(dt_t + dt_bias[d])
+//     h_t[n]  = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t Bm[b,t,n] x_t
+//     y_t     = (sum_n Cm[b,t,n] h_t[n] + Dskip[d] x_t) * silu(z_t)
+// (kZoh: the exact zero-order-hold input term); only y and the final state
+// reach memory.
+//
+// Work split.  Channels run along the lanes: a workgroup is one wave, 64
+// consecutive channels of one batch row, so that every load of x, dt and z
+// and every store of y at a time step is one contiguous run across the wave,
+// and Bm, Cm at that step (shared by all channels) are wave-uniform.  Each
+// lane keeps its channel's N states in registers and walks its piece of the
+// sequence step by step: no in-chunk scan.  The sequence is cut into pieces
+// (grid z) so that enough waves run at once; a piece acts on the state
+// entering it as the affine map h -> exp(A sum Delta) h + e (e its end state
+// from zero), and composing those maps in order is the scan's associative
+// operator (the glossary's parallel associative scan).  Three launches:
+//   1. bld_agg_kernel: every piece from a zero state: its end state and
+//      Delta sum;
+//   2. bld_combine_kernel: one thread per (batch, channel, state) composes
+//      the pieces in order from h0, overwrites each piece's record with the
+//      state entering it, and writes hL;
+//   3. bld_main_kernel: every piece from its entering state, with the
+//      readout, the gate and the output.
+// No MFMA: the recurrence is not a dense contraction.
+#include <algorithm>
+
+#include "ssm_device.hpp"
+#include "ssm_launch.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kLanes = 64;  // one wave: 64 consecutive channels
+
+struct BldParams {
+    int dim, seqlen, npieces, piece_len;
+    // element strides: time step, batch entry (channel / state stride 1)
+    long long x_t, x_b, dt_t, dt_b, z_t, z_b, y_t, y_b, B_t, B_b, C_t, C_b;
+    const float *dt_bias, *A, *Dskip, *h0;
+    float *hL;
+    float *rec;  // [npieces][batch][dim][N + 1]: piece maps, then entering states
+    int bc_words;  // every Bm and Cm row starts on a 4-byte boundary
+};
+
+template <typename T>
+__device__ inline float load_elem(const T *p)
+{
+    return io<T>::load1(p);
+}
+
+template <typename Tout>
+__device__ inline void store_elem(Tout *p, float v)
+{
+    if constexpr (sizeof(Tout) == 4) {
+        *reinterpret_cast<float *>(p) = v;
+    } else {
+        *reinterpret_cast<uint16_t *>(p) = uint16_t(pack_bf16x2(v, 0.0f) & 0xffffu);
+    }
+}
+
+// The Bm (or Cm) row of one step: N values shared by the whole wave.  The
+// address is made visibly wave-uniform (read from the first lane into
+// scalar registers), so that where the compiler can prove the row unchanged
+// by the kernel's own stores it comes through the scalar data cache into
+// SGPRs once per wave (the aggregate pass) instead of as a 64-lane vector
+// load.  bf16 rows are read as 32-bit words only when `words` says every
+// row starts on a 4-byte boundary: a scalar load ignores the address's two
+// low bits.
+template <typename Tin, int N>
+__device__ inline void load_row(const Tin *p, bool words, float *v)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+    const Tin *__restrict__ q = reinterpret_cast<const Tin *>((uint64_t(hi) << 32) | lo);
+    if (sizeof(Tin) == 2 && N % 2 == 0 && words) {
+        const uint32_t *w = reinterpret_cast<const uint32_t *>(q);
+#pragma unroll
+        for (int n = 0; n < N / 2; ++n) {
+            const uint32_t u = w[n];
+            v[2 * n] = io<bf16_t>::lo(u);
+            v[2 * n + 1] = io<bf16_t>::hi(u);
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) v[n] = load_elem(q + n);
+    }
+}
+
+template <typename Tin, int N, bool kZoh>
+__global__ __launch_bounds__(kLanes) void bld_agg_kernel(BldParams p, const Tin *__restrict__ x,
+                                                         const Tin *__restrict__ dt,
+                                                         const Tin *__restrict__ Bm)
+{
+    const int d = blockIdx.x * kLanes + threadIdx.x;
+    const bool live = d < p.dim;
+    const int dc = live ? d : p.dim - 1;
+    const int b = blockIdx.y, piece = blockIdx.z;
+    const int t0 = piece * p.piece_len, t1 = min(p.seqlen, t0 + p.piece_len);
+    float a[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a[n] = p.A[size_t(dc) * N + n] * kLog2e;
+        h[n] = 0.0f;
+    }
+    [[maybe_unused]] float inva[N];
+    if constexpr (kZoh) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) inva[n] = rcp_hw(a[n]) * kLog2e;
+    }
+    const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    const Tin *xp = x + size_t(b) * size_t(p.x_b) + size_t(t0) * size_t(p.x_t) + dc;
+    const Tin *dp = dt + size_t(b) * size_t(p.dt_b) + size_t(t0) * size_t(p.dt_t) + dc;
+    const Tin *bp = Bm + size_t(b) * size_t(p.B_b) + size_t(t0) * size_t(p.B_t);
+    float sumd = 0.0f;
+    for (int t = t0; t < t1; ++t) {
+        const float xv = load_elem(xp), delta = softplus(load_elem(dp) + bias);
+        float bn[N];
+        load_row<Tin, N>(bp, p.bc_words != 0, bn);
+        const float u = delta * xv;
+        [[maybe_unused]] const float invd = kZoh ? rcp_hw(delta) : 0.0f;
+        sumd += delta;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float s = delta * a[n];
+            const float e = exp2_hw(s);
+            float bb = u * bn[n];
+            if constexpr (kZoh) bb *= phi_zoh(s * kLn2, e, invd * inva[n]);
+            h[n] = __builtin_fmaf(e, h[n], bb);
+        }
+        xp += p.x_t;
+        dp += p.dt_t;
+        bp += p.B_t;
+    }
+    if (live) {
+        float *r = p.rec + ((size_t(piece) * gridDim.y + b) * p.dim + d) * (N + 1);
+#pragma unroll
+        for (int n = 0; n < N; ++n) r[n] = h[n];
+        r[N] = sumd;
+    }
+}
+
+// One thread per (batch, channel, state): the state entering every piece,
+// written over that piece's map (read first, by the same thread), and hL.
+template <int N>
+__global__ __launch_bounds__(256) void bld_combine_kernel(BldParams p, int batch)
+{
+    const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+    const size_t rows = size_t(batch) * p.dim;
+    if (i >= rows * N) return;
+    const int n = int(i % N);
+    const size_t row = i / N;  // b * dim + d
+    const int d = int(row % size_t(p.dim));
+    const float a = p.A[size_t(d) * N + n] * kLog2e;
+    float h = p.h0 ? p.h0[row * N + n] : 0.0f;
+    for (int k = 0; k < p.npieces; ++k) {
+        float *r = p.rec + (size_t(k) * rows + row) * (N + 1);
+        const float sd = r[N], e = r[n];
+        r[n] = h;
+        h = __builtin_fmaf(exp2_hw(a * sd), h, e);
+    }
+    if (p.hL) p.hL[row * N + n] = h;
+}
+
+template <typename Tin, typename Tout, int N, bool kZoh>
+__global__ __launch_bounds__(kLanes) void bld_main_kernel(
+    BldParams p, const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ z,
+    const Tin *__restrict__ Bm, const Tin *__restrict__ Cm, Tout *__restrict__ y)
+{
+    const int d = blockIdx.x * kLanes + threadIdx.x;
+    const bool live = d < p.dim;
+    const int dc = live ? d : p.dim - 1;
+    const int b = blockIdx.y, piece = blockIdx.z;
+    const int t0 = piece * p.piece_len, t1 = min(p.seqlen, t0 + p.piece_len);
+    const float *r = p.rec + ((size_t(piece) * gridDim.y + b) * p.dim + dc) * (N + 1);
+    float a[N], h[N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+        a[n] = p.A[size_t(dc) * N + n] * kLog2e;
+        h[n] = r[n];
+    }
+    [[maybe_unused]] float inva[N];
+    if constexpr (kZoh) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) inva[n] = rcp_hw(a[n]) * kLog2e;
+    }
+    const float bias = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    const float skip = p.Dskip ? p.Dskip[dc] : 0.0f;
+    const Tin *xp = x + size_t(b) * size_t(p.x_b) + size_t(t0) * size_t(p.x_t) + dc;
+    const Tin *dp = dt + size_t(b) * size_t(p.dt_b) + size_t(t0) * size_t(p.dt_t) + dc;
+    const Tin *zp = z ? z + size_t(b) * size_t(p.z_b) + size_t(t0) * size_t(p.z_t) + dc : nullptr;
+    Tout *yp = y + size_t(b) * size_t(p.y_b) + size_t(t0) * size_t(p.y_t) + dc;
+    const Tin *bp = Bm + size_t(b) * size_t(p.B_b) + size_t(t0) * size_t(p.B_t);
+    const Tin *cp = Cm + size_t(b) * size_t(p.C_b) + size_t(t0) * size_t(p.C_t);
+    for (int t = t0; t < t1; ++t) {
+        const float xv = load_elem(xp), delta = softplus(load_elem(dp) + bias);
+        const float zv = zp ? load_elem(zp) : 0.0f;
+        float bn[N], cn[N];
+        load_row<Tin, N>(bp, p.bc_words != 0, bn);
+        load_row<Tin, N>(cp, p.bc_words != 0, cn);
+        const float u = delta * xv;
+        [[maybe_unused]] const float invd = kZoh ? rcp_hw(delta) : 0.0f;
+        float yv = skip * xv;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const float s = delta * a[n];
+            const float e = exp2_hw(s);
+            float bb = u * bn[n];
+            if constexpr (kZoh) bb *= phi_zoh(s * kLn2, e, invd * inva[n]);
+            h[n] = __builtin_fmaf(e, h[n], bb);
+            yv = __builtin_fmaf(cn[n], h[n], yv);
+        }
+        if (zp) {
+            yv *= silu(zv);
+            zp += p.z_t;
+        }
+        if (live) store_elem(yp, yv);
+        xp += p.x_t;
+        dp += p.dt_t;
+        yp += p.y_t;
+        bp += p.B_t;
+        cp += p.C_t;
+    }
+}
+
+// Pieces: enough waves for the whole GPU (about 4096 at once, i.e. four per
+// SIMD), at least 64 steps each.
+BldSplit bld_split_impl(int batch, int dim, int seqlen)
+{
+    const long long waves = (long long)batch * ((dim + kLanes - 1) / kLanes);
+    long long np = (4096 + waves - 1) / waves;
+    np = std::max(1LL, std::min<long long>(np, seqlen / 64));
+    np = std::min<long long>(np, 65535);
+    BldSplit s;
+    s.piece_len = int((seqlen + np - 1) / np);
+    s.npieces = (seqlen + s.piece_len - 1) / s.piece_len;
+    return s;
+}
+
+template <typename Tin, typename Tout, int N, bool kZoh>
+hipError_t launch_typed(const BldArgs &a, hipStream_t stream)
+{
+    const BldSplit sp = bld_split_impl(a.batch, a.dim, a.seqlen);
+    BldParams p{a.dim, a.seqlen, sp.npieces, sp.piece_len,
+                a.x_t, a.x_b, a.dt_t, a.dt_b, a.z_t, a.z_b, a.y_t, a.y_b,
+                a.B_t, a.B_b, a.C_t, a.C_b, a.dt_bias, a.A, a.Dskip, a.h0, a.hL, a.workspace, 0};
+    // bf16 Bm / Cm rows can be read as words when every row is word-aligned
+    auto words = [](const void *base, long long st, long long sb) {
+        return (reinterpret_cast<uintptr_t>(base) & 3) == 0 && (st * 2) % 4 == 0 &&
+               (sb * 2) % 4 == 0;
+    };
+    p.bc_words = words(a.Bm, a.B_t, a.B_b) && words(a.Cm, a.C_t, a.C_b);
+    const dim3 grid((unsigned(a.dim) + kLanes - 1) / kLanes, a.batch, sp.npieces);
+    const size_t threads = size_t(a.batch) * a.dim * N;
+    if (log_enabled())
+        log_line("scan_fwd_bld: %d pieces of %d steps: bld_agg_kernel<in %s, N %d, zoh %d>, "
+                 "bld_combine_kernel, bld_main_kernel<out %s>, grid (%u, %u, %u) x %d threads",
+                 sp.npieces, sp.piece_len, type_tag<Tin>(), N, int(kZoh), type_tag<Tout>(), grid.x,
+                 grid.y, grid.z, kLanes);
+    const Tin *x = static_cast<const Tin *>(a.x), *dt = static_cast<const Tin *>(a.dt);
+    const Tin *Bm = static_cast<const Tin *>(a.Bm), *Cm = static_cast<const Tin *>(a.Cm);
+    hipLaunchKernelGGL((bld_agg_kernel<Tin, N, kZoh>), grid, dim3(kLanes), 0, stream, p, x, dt, Bm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bld_combine_kernel<N>), dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
+                       stream, p, a.batch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bld_main_kernel<Tin, Tout, N, kZoh>), grid, dim3(kLanes), 0, stream, p, x,
+                       dt, static_cast<const Tin *>(a.z), Bm, Cm, static_cast<Tout *>(a.y));
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout, bool kZoh>
+hipError_t launch_n(const BldArgs &a, hipStream_t stream)
+{
+    switch (a.dstate) {
+    case 1: return launch_typed<Tin, Tout, 1, kZoh>(a, stream);
+    case 2: return launch_typed<Tin, Tout, 2, kZoh>(a, stream);
+    case 4: return launch_typed<Tin, Tout, 4, kZoh>(a, stream);
+    case 8: return launch_typed<Tin, Tout, 8, kZoh>(a, stream);
+    case 16: return launch_typed<Tin, Tout, 16, kZoh>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_mode(const BldArgs &a, hipStream_t stream)
+{
+    return a.zoh ? launch_n<Tin, Tout, true>(a, stream) : launch_n<Tin, Tout, false>(a, stream);
+}
+
+}  // namespace
+
+BldSplit bld_split(int batch, int dim, int seqlen) { return bld_split_impl(batch, dim, seqlen); }
+
+size_t scan_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    const BldSplit sp = bld_split_impl(batch, dim, seqlen);
+    return size_t(sp.npieces) * size_t(batch) * size_t(dim) * size_t(dstate + 1) * sizeof(float);
+}
+
+hipError_t launch_scan_bld(const BldArgs &a, hipStream_t stream)
+{
+    if (a.in_bf16) {
+        return a.out_bf16 ? launch_mode<bf16_t, bf16_t>(a, stream)
+                          : launch_mode<bf16_t, float>(a, stream);
+    }
+    return a.out_bf16 ? launch_mode<float, bf16_t>(a, stream) : launch_mode<float, float>(a, stream);
+}
+
+}  // namespace ssm

@@ -215,38 +215,6 @@ __device__ inline float row_total_last(float v)
     return v;
 }
 
-// Two independent forward row scans (see row_scan in scan_common.hpp),
-// interleaved so that each one's DPP read hazard is covered by the other's
-// instructions instead of wait states.
-__device__ inline void row_scan_x2(float &a0, float &b0, float &e0, float &h0,
-                                   float &a1, float &b1, float &e1, float &h1)
-{
-    asm volatile(
-        "s_nop 1\n\t"
-        "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %4 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %4, %4, %4 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %4 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %4, %4, %4 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %4, %4, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mul_f32_dpp %4, %4, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
-        "v_fma_f32 %2, %0, %3, %1\n\t"
-        "v_fma_f32 %6, %4, %7, %5\n\t"
-        "s_nop 0\n\t"
-        "v_mov_b32_dpp %3, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
-        "v_mov_b32_dpp %7, %6 row_shr:1 row_mask:0xf bank_mask:0xf"
-        : "+v"(a0), "+v"(b0), "=&v"(e0), "+v"(h0), "+v"(a1), "+v"(b1), "=&v"(e1), "+v"(h1));
-}
-
 // Two independent reverse row scans (see row_scan_rev), interleaved.
 __device__ inline void row_scan_rev_x2(float &a0, float &b0, float &e0, float &h0,
                                        float &a1, float &b1, float &e1, float &h1)
@@ -826,7 +794,13 @@ hipError_t launch_bwd_typed(const BwdArgs &a, hipStream_t stream)
     hipLaunchKernelGGL(bwd_zero_kernel, dim3(1024), dim3(256), 0, stream, part,
                        size_t(kCopies) * 2 * nbc, a.dA, size_t(a.dim) * N, a.dDskip, size_t(a.dim),
                        a.ddt_bias, size_t(a.dim));
-    const unsigned gx = (a.dim + kChanB - 1) / kChanB;
+    const unsigned gx = (unsigned(a.dim) + kChanB - 1) / kChanB;
+    if (log_enabled())
+        log_line("scan_bwd: checkpoints %s; %s; scan_bwd_kernel<in %s, grad %s, N %d, zoh %d> "
+                 "grid (%u, %d, %d) x %d threads, partial-sum copies %d",
+                 a.ckpt_given ? "from the forward" : "recomputed", sp.nseg > 1 ? "split" : "no split",
+                 type_tag<Tin>(), type_tag<Tg>(), N, int(kZoh), gx, a.batch, sp.nseg, kThreadsB,
+                 kCopies);
     if (sp.nseg > 1)
         hipLaunchKernelGGL((adjoint_agg_kernel<Tin, Tg, N>), dim3(gx, a.batch, sp.nseg - 1),
                            dim3(kThreadsB), 0, stream, p);

@@ -50,6 +50,38 @@ __device__ inline void row_scan(float &a, float &b, float &hend, float &h)
         : "+v"(a), "+v"(b), "=&v"(hend), "+v"(h));
 }
 
+// Two independent row scans (see row_scan), interleaved so that each one's
+// DPP read hazard is covered by the other's instructions instead of wait
+// states.
+__device__ inline void row_scan_x2(float &a0, float &b0, float &e0, float &h0,
+                                   float &a1, float &b1, float &e1, float &h1)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %4, %4, %4 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fma_f32 %2, %0, %3, %1\n\t"
+        "v_fma_f32 %6, %4, %7, %5\n\t"
+        "s_nop 0\n\t"
+        "v_mov_b32_dpp %3, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mov_b32_dpp %7, %6 row_shr:1 row_mask:0xf bank_mask:0xf"
+        : "+v"(a0), "+v"(b0), "=&v"(e0), "+v"(h0), "+v"(a1), "+v"(b1), "=&v"(e1), "+v"(h1));
+}
+
 template <typename Tout, int K>
 __device__ inline void store_y(Tout *dst, bool vec, int count, const float *v)
 {

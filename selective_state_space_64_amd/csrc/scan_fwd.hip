@@ -75,6 +75,21 @@ constexpr int kK = SSM_SCAN_K;              // consecutive timesteps per lane
 #define SSM_SPLIT_MIN_STEPS 1024
 #endif
 constexpr int kMaxSegments = 1024;
+// Steps per lane in the split's aggregate pass (a multiple of kK).
+#ifndef SSM_SCAN_AGG_K
+#define SSM_SCAN_AGG_K 16
+#endif
+constexpr int kAggK = SSM_SCAN_AGG_K;
+static_assert(kAggK % kK == 0, "aggregate chunks are whole main-pass chunks");
+// Steps per lane in the checkpoint-only pass (no readout either, so the
+// longer fold fits); a 64-step checkpoint falls on every (64 / K)-th lane.
+// The exact zero-order-hold form keeps K = 8 in both passes: at 16 its
+// fp32 instantiations would spill.
+#ifndef SSM_SCAN_CKPT_K
+#define SSM_SCAN_CKPT_K 16
+#endif
+constexpr int kCkptK = SSM_SCAN_CKPT_K;
+static_assert(kAggK % kCkptK == 0, "checkpoint-pass segments are whole chunks");
 // Occupancy target (waves per SIMD): 4, which is also what the ~36 KB of LDS
 // per 4-wave workgroup allows (4 workgroups per CU).  More resident waves
 // were measured not to help: the state loop runs near the VALU issue limit.
@@ -128,14 +143,19 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
     // sB has one spare state so the look-ahead load of the last state stays
     // inside the array.
     __shared__ float4 sB[2][(N + 1) * Q * kRow];
-    __shared__ float4 sC[2][N * Q * kRow];
+    __shared__ float4 sC[2][kRead ? N * Q * kRow : 1];
     // Per channel: NP entries of A * log2(e), then NP entries of the state
     // entering the current chunk.
     __shared__ float sAC[kChannels * 2 * NP];
-    // Checkpoints: per channel, the state at the 64-step midpoint of the
-    // chunk (lane 7's end state), gathered so that the row of N states goes
-    // out in 16-byte stores.
-    __shared__ float sMid[kCkpt ? kChannels * NP : 1];
+    // Checkpoints: every 64 steps, kPer per chunk.  The first is the carry
+    // entering the chunk; the others are the end states of every kG-th lane,
+    // gathered per channel (kMid rows of NP) so that a row of N states goes
+    // out in one store instruction.
+    static_assert(!kCkpt || (kCkptSteps % K == 0 && T % kCkptSteps == 0), "whole lanes per checkpoint");
+    constexpr int kG = kCkptSteps / K;         // lanes per 64-step checkpoint
+    constexpr int kPer = T / kCkptSteps;       // checkpoints per chunk
+    constexpr int kMid = kPer - 1;             // ... after the chunk's entry
+    __shared__ float sMid[kCkpt ? kChannels * kMid * NP : 1];
 
     const int tid = threadIdx.x;
     const int j = tid & (kRow - 1);
@@ -315,13 +335,12 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         }
         const bool more = ch + 1 < nchunks;
         // Checkpoints for the backward pass: the state entering each 64-step
-        // half of the chunk, one (b, d, half) row of N states per store
+        // part of the chunk, one (b, d, part) row of N states per store
         // instruction (lane j writes state j), so every row goes out as one
         // contiguous line instead of N scattered words.
-        [[maybe_unused]] auto store_ck = [&](const float *src, int half) {
-            static_assert(kRow * K == 2 * kCkptSteps, "two checkpoints per chunk");
+        [[maybe_unused]] auto store_ck = [&](const float *src, int part) {
             static_assert(N <= kRow, "one lane per state");
-            const int ck = 2 * (ch + lseg / T) + half;  // global 64-step chunk
+            const int ck = kPer * (ch + lseg / T) + part;  // global 64-step chunk
             if (live && j < N && ck < p.nck) ckw[ck_lane + uint32_t(ck) * uint32_t(N)] = src[j];
         };
         if constexpr (kCkpt) store_ck(aptr + NP, 0);  // the carry entering the chunk
@@ -372,7 +391,8 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             row_scan(aa, hl, hend, h);
             if (j == kRow - 1) aptr[NP + n] = hend;
             if constexpr (kCkpt) {
-                if (j == kRow / 2 - 1) sMid[c * NP + n] = hend;  // entering the chunk's second half
+                // entering the next 64-step part of the chunk
+                if ((j + 1) % kG == 0 && j < kRow - 1) sMid[(c * kMid + (j + 1) / kG - 1) * NP + n] = hend;
             }
             bp += Q * kRow;
             load_b(bp, bv);          // next state's B (one past the end on the last state)
@@ -383,6 +403,61 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
                 for (int i = 0; i < K; ++i) {
                     h = __builtin_fmaf(dA[i], h, bb[i]);
                     yv[i] = __builtin_fmaf(cv[i], h, yv[i]);
+                }
+            }
+        };
+
+        // Two states at once (the two-states-per-trip instantiation): both
+        // folds first, then one asm block in which the two DPP scans cover
+        // each other's read hazards (no wait states), then both replays.
+        [[maybe_unused]] auto state_pair = [&](int n) {
+            float bv1[K];
+            load_b(bp + Q * kRow, bv1);
+            const float ap1 = aptr[n + 1], carry1 = aptr[NP + n + 1];
+            float dA0[K], bb0[K], dA1[K], bb1[K];
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                dA0[i] = exp2_hw(delta[i] * ap);
+                bb0[i] = u[i] * bv[i];
+            }
+#pragma unroll
+            for (int i = 0; i < K; ++i) {
+                dA1[i] = exp2_hw(delta[i] * ap1);
+                bb1[i] = u[i] * bv1[i];
+            }
+            float hl0 = bb0[0], hl1 = bb1[0];
+#pragma unroll
+            for (int i = 1; i < K; ++i) {
+                hl0 = __builtin_fmaf(dA0[i], hl0, bb0[i]);
+                hl1 = __builtin_fmaf(dA1[i], hl1, bb1[i]);
+            }
+            float aa0 = exp2_hw(sumd * ap), aa1 = exp2_hw(sumd * ap1);
+            float hend0, hend1, h0 = carry, h1 = carry1;
+            row_scan_x2(aa0, hl0, hend0, h0, aa1, hl1, hend1, h1);
+            if (j == kRow - 1) {
+                aptr[NP + n] = hend0;
+                aptr[NP + n + 1] = hend1;
+            }
+            bp += 2 * Q * kRow;
+            load_b(bp, bv);  // the next pair's first B (one past the end after the last)
+            ap = aptr[n + 2];
+            carry = aptr[NP + n + 2];
+            if constexpr (kRead) {
+                // each state's Cm run is read just before its replay, so that
+                // neither is held across the folds and the scan
+                float cv[K];
+                load_b(cp, cv);
+#pragma unroll
+                for (int i = 0; i < K; ++i) {
+                    h0 = __builtin_fmaf(dA0[i], h0, bb0[i]);
+                    yv[i] = __builtin_fmaf(cv[i], h0, yv[i]);
+                }
+                load_b(cp + Q * kRow, cv);
+                cp += 2 * Q * kRow;
+#pragma unroll
+                for (int i = 0; i < K; ++i) {
+                    h1 = __builtin_fmaf(dA1[i], h1, bb1[i]);
+                    yv[i] = __builtin_fmaf(cv[i], h1, yv[i]);
                 }
             }
         };
@@ -401,18 +476,34 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
                 stage_load(Bb, ch + 1, stB);
                 if constexpr (kRead) stage_load(Cb, ch + 1, stC);
             }
-#pragma unroll kSU
-            for (int n = 0; n < N1; ++n) state_step(n);
-            if (more && stager) {
-                stage_store(sB[buf ^ 1], stB);
-                if constexpr (kRead) stage_store(sC[buf ^ 1], stC);
+            if constexpr (kSU == 2) {
+                static_assert(N1 % 2 == 0 && N2 % 2 == 0 && N % 2 == 0, "whole pairs per third");
+#pragma unroll 1
+                for (int n = 0; n < N1; n += 2) state_pair(n);
+                if (more && stager) {
+                    stage_store(sB[buf ^ 1], stB);
+                    if constexpr (kRead) stage_store(sC[buf ^ 1], stC);
+                }
+#pragma unroll 1
+                for (int n = N1; n < N2; n += 2) state_pair(n);
+                if (kRead && zw) z_load(ch, yoff);
+                if (more) xd_load(ch + 1);
+#pragma unroll 1
+                for (int n = N2; n < N; n += 2) state_pair(n);
+            } else {
+#pragma unroll 1
+                for (int n = 0; n < N1; ++n) state_step(n);
+                if (more && stager) {
+                    stage_store(sB[buf ^ 1], stB);
+                    if constexpr (kRead) stage_store(sC[buf ^ 1], stC);
+                }
+#pragma unroll 1
+                for (int n = N1; n < N2; ++n) state_step(n);
+                if (kRead && zw) z_load(ch, yoff);
+                if (more) xd_load(ch + 1);
+#pragma unroll 1
+                for (int n = N2; n < N; ++n) state_step(n);
             }
-#pragma unroll kSU
-            for (int n = N1; n < N2; ++n) state_step(n);
-            if (kRead && zw) z_load(ch, yoff);
-            if (more) xd_load(ch + 1);
-#pragma unroll kSU
-            for (int n = N2; n < N; ++n) state_step(n);
         } else {
             // few states: everything is fetched up front
             if (more && stager) {
@@ -441,7 +532,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
             else if (cnt > 0)
                 store_y<Tout, K>(yr, cnt == K && aligned16(yr), cnt, yv);
         }
-        if constexpr (kCkpt) store_ck(sMid + c * NP, 1);  // lane 7's end states, same wave
+        if constexpr (kCkpt) {
+            // written by lanes of the same row (same wave) in the state loop
+#pragma unroll
+            for (int m = 0; m < kMid; ++m) store_ck(sMid + (c * kMid + m) * NP, m + 1);
+        }
         lds_barrier();
     }
 
@@ -470,20 +565,33 @@ hipError_t launch_typed(const ScanArgs &a, hipStream_t stream)
                  a.x, a.dt, a.dt_bias, a.A, a.Bm, a.Cm,
                  a.Dskip, a.z, a.h0, a.y, a.hL, a.ck, (a.seqlen + kCkptSteps - 1) / kCkptSteps,
                  sp.seg_len, sp.nseg, a.agg};
-    const unsigned gx = (a.dim + kChannels - 1) / kChannels;
+    const unsigned gx = (unsigned(a.dim) + kChannels - 1) / kChannels;
+    if (log_enabled() && sp.nseg > 1)
+        log_line("scan_fwd: sequence split into %d segments of %d steps; aggregate pass "
+                 "scan_fwd_kernel<in %s, N %d, K %d, zoh %d, aggregate>, grid (%u, %d, %d) x %d threads",
+                 sp.nseg, sp.seg_len, type_tag<Tin>(), N, kZoh ? kK : kAggK, int(kZoh), gx, a.batch,
+                 sp.nseg - 1, kThreads);
     if (sp.nseg > 1) {
         // every segment but the last: its end state and Delta sum
-        hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, false, true, true>),
+        // The aggregate pass has no replay, so each lane's fold streams its
+        // steps and 16 steps per lane fit: half the row scans per element.
+        hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, kZoh ? kK : kAggK, kZoh, false, true, true>),
                            dim3(gx, a.batch, sp.nseg - 1), dim3(kThreads), 0, stream, p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const dim3 grid(gx, a.batch, sp.nseg);
+    if (log_enabled())
+        log_line("scan_fwd: scan_fwd_kernel<in %s, out %s, N %d, K %d, zoh %d, checkpoints %d, "
+                 "output %d>, %s, grid (%u, %u, %u) x %d threads",
+                 type_tag<Tin>(), type_tag<Tout>(), N, (a.ckpt_only && !kZoh) ? kCkptK : K, int(kZoh),
+                 a.ck ? 1 : 0, a.ckpt_only ? 0 : 1, sp.nseg > 1 ? "main pass" : "no split", grid.x, grid.y,
+                 grid.z, kThreads);
     if (a.ckpt_only) {
         // no output: one instantiation (fp32 Tout) serves every caller
         if constexpr (sizeof(Tout) == 4) {
-            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, K, kZoh, true, false, false>), grid,
-                               dim3(kThreads), 0, stream, p);
+            hipLaunchKernelGGL((scan_fwd_kernel<Tin, Tout, N, kZoh ? kK : kCkptK, kZoh, true, false, false>),
+                               grid, dim3(kThreads), 0, stream, p);
             return hipGetLastError();
         }
         return hipErrorInvalidValue;
@@ -521,8 +629,8 @@ hipError_t launch_mode(const ScanArgs &a, hipStream_t stream)
 
 ScanSplit scan_fwd_split(int batch, int dim, int seqlen)
 {
-    constexpr int T = kRow * kK;
-    const long long wgs = (long long)batch * ((dim + kChannels - 1) / kChannels);
+    constexpr int T = kRow * kAggK;  // segments: whole chunks of both passes
+    const long long wgs = (long long)batch * (((long long)dim + kChannels - 1) / kChannels);
     ScanSplit sp{1, seqlen};
     if (wgs >= SSM_SPLIT_BELOW_WGS) return sp;
     long long nseg = SSM_SPLIT_TARGET_WGS / wgs;  // whole waves of workgroups

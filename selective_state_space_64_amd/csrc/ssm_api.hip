@@ -6,6 +6,11 @@
 #include "ssm_conv.h"
 
 #include <stdint.h>
+#include <string.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -34,6 +39,18 @@ bool overlaps(const void *p, size_t pb, const void *q, size_t qb)
     if (!p || !q || pb == 0 || qb == 0) return false;
     const Span a = span(p, pb), b = span(q, qb);
     return a.lo < b.hi && b.lo < a.hi;
+}
+
+// The value of an enum argument as the int a C caller passed: its bits are
+// read without loading the argument as the enum type, so a value outside the
+// enumeration (an error the validation reports) is not undefined behaviour.
+template <typename E>
+int enum_bits(const E &e)
+{
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v = 0;
+    memcpy(&v, &e, sizeof v);
+    return v;
 }
 
 bool valid_dtype(int t) { return t == SSM_F32 || t == SSM_BF16; }
@@ -108,19 +125,37 @@ hipError_t scratch_address(float **out)
     return hipSuccess;
 }
 
+// Step and batch strides (0 = dense) and the span in elements of a
+// (batch, seqlen, rowlen) tensor whose row index is contiguous: false when a
+// stride is negative or below its minimum, or the span reaches 2^56.
+bool bld_span(long long given_step, long long given_batch, int batch, int seqlen, int rowlen,
+              long long &st, long long &sb, size_t &sp)
+{
+    st = given_step ? given_step : rowlen;
+    if (st < rowlen || st > (1ll << 40)) return false;
+    const __int128 min_b = (__int128)seqlen * st;
+    sb = given_batch ? given_batch : (long long)min_b;
+    if ((__int128)sb < min_b) return false;
+    const __int128 n = (__int128)(batch - 1) * sb + (__int128)(seqlen - 1) * st + rowlen;
+    if (n >= ((__int128)1 << 56)) return false;
+    sp = size_t(n);
+    return true;
+}
+
 // ssm_scan_fwd_strided, and with noalloc set ssm_scan_fwd_noalloc: the
 // split's planes then go to the library's own scratch array instead of the
 // caller's workspace (which must be NULL), and checkpoints are refused.
-ssm_status_t scan_fwd_impl(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+ssm_status_t scan_fwd_impl(int batch, int dim, int seqlen, int dstate, int in_dtype,
                            unsigned flags, const void *x, const void *dt, const float *dt_bias,
                            const float *A, const void *Bm, const void *Cm, const float *Dskip,
-                           const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
+                           const void *z, const float *h0, int out_dtype, void *y,
                            float *hL, void *workspace, size_t workspace_bytes,
                            const ssm_scan_layout_t *layout, void *stream, bool noalloc)
 {
     if (!x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
-    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || dim > ssm::kMaxDim ||
+        seqlen > ssm::kMaxSeqlen)
         return SSM_ERR_BAD_SHAPE;
     if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_ZOH_B | SSM_FLAG_CHECKPOINTS)) != 0)
         return SSM_ERR_UNSUPPORTED;
@@ -201,12 +236,68 @@ ssm_status_t scan_fwd_impl(int batch, int dim, int seqlen, int dstate, ssm_dtype
 
 }  // namespace
 
+namespace ssm {
+
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *v = getenv("SSM_LOG");
+        return v && *v && !(v[0] == '0' && v[1] == 0);
+    }();
+    return on;
+}
+
+void log_line(const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "[ssm] %s\n", buf);
+}
+
+}  // namespace ssm
+
 extern "C" {
+
+// Implementations behind the entry points, dtype arguments as int.
+static ssm_status_t ssm_state_update_strided_impl(int batch, int dim, int dstate, int in_dtype,
+                                      unsigned flags, float *state, const void *x,
+                                      const void *dt, const float *dt_bias, const float *A,
+                                      const void *Bm, const void *Cm, const float *Dskip,
+                                      const void *z, int out_dtype, void *y,
+                                      const ssm_update_layout_t *layout, void *stream);
+static ssm_status_t ssm_conv1d_fwd_strided_impl(int batch, int dim, int seqlen, int width,
+                                    int in_dtype, unsigned flags, const void *x,
+                                    const float *weight, const float *bias, const float *state0,
+                                    int out_dtype, void *y, float *stateL,
+                                    const ssm_conv_layout_t *layout, void *stream);
+static ssm_status_t ssm_conv1d_update_strided_impl(int batch, int dim, int width, int in_dtype,
+                                       unsigned flags, float *state, const void *x,
+                                       const float *weight, const float *bias,
+                                       int out_dtype, void *y, long long x_batch,
+                                       long long y_batch, void *stream);
+static ssm_status_t ssm_scan_bwd_strided_impl(int batch, int dim, int seqlen, int dstate,
+                                  int in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, int grad_dtype,
+                                  const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                                  float *dBm, float *dCm, float *dA, float *dDskip,
+                                  float *ddt_bias, float *dh0, void *workspace,
+                                  size_t workspace_bytes, const ssm_scan_bwd_layout_t *layout,
+                                  void *stream);
+
 
 int ssm_abi_version(void) { return SSM_ABI_VERSION; }
 
-const char *ssm_status_string(ssm_status_t s)
+const char *ssm_status_string(ssm_status_t status)
 {
+    // C callers may pass any int; reading the argument's bits as an int keeps
+    // a value outside the enumeration defined behaviour here
+    int s = 0;
+    memcpy(&s, &status, sizeof s);
     switch (s) {
     case SSM_OK: return "ok";
     case SSM_ERR_NULL_ARG: return "a required pointer argument is NULL";
@@ -224,8 +315,8 @@ const char *ssm_status_string(ssm_status_t s)
 
 size_t ssm_scan_fwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 {
-    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen ||
-        !valid_dstate(dstate))
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || dim > ssm::kMaxDim ||
+        seqlen > ssm::kMaxSeqlen || !valid_dstate(dstate))
         return 0;
     return ssm::scan_fwd_split_bytes(batch, dim, seqlen, dstate);
 }
@@ -236,9 +327,9 @@ ssm_status_t ssm_scan_fwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
                           float *hL, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return ssm_scan_fwd_strided(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A,
-                                Bm, Cm, Dskip, z, h0, out_dtype, y, hL, workspace,
-                                workspace_bytes, nullptr, stream);
+    return scan_fwd_impl(batch, dim, seqlen, dstate, enum_bits(in_dtype), flags, x, dt, dt_bias, A,
+                         Bm, Cm, Dskip, z, h0, enum_bits(out_dtype), y, hL, workspace,
+                         workspace_bytes, nullptr, stream, false);
 }
 
 ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
@@ -249,9 +340,9 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
                                   float *hL, void *workspace, size_t workspace_bytes,
                                   const ssm_scan_layout_t *layout, void *stream)
 {
-    return scan_fwd_impl(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A, Bm, Cm,
-                         Dskip, z, h0, out_dtype, y, hL, workspace, workspace_bytes, layout, stream,
-                         false);
+    return scan_fwd_impl(batch, dim, seqlen, dstate, enum_bits(in_dtype), flags, x, dt, dt_bias, A,
+                         Bm, Cm, Dskip, z, h0, enum_bits(out_dtype), y, hL, workspace,
+                         workspace_bytes, layout, stream, false);
 }
 
 ssm_status_t ssm_scan_fwd_noalloc(int batch, int dim, int seqlen, int dstate,
@@ -261,8 +352,84 @@ ssm_status_t ssm_scan_fwd_noalloc(int batch, int dim, int seqlen, int dstate,
                                   const void *z, const float *h0, ssm_dtype_t out_dtype, void *y,
                                   float *hL, const ssm_scan_layout_t *layout, void *stream)
 {
-    return scan_fwd_impl(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A, Bm, Cm,
-                         Dskip, z, h0, out_dtype, y, hL, nullptr, 0, layout, stream, true);
+    return scan_fwd_impl(batch, dim, seqlen, dstate, enum_bits(in_dtype), flags, x, dt, dt_bias, A,
+                         Bm, Cm, Dskip, z, h0, enum_bits(out_dtype), y, hL, nullptr, 0, layout,
+                         stream, true);
+}
+
+size_t ssm_scan_fwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || dim > ssm::kMaxDim ||
+        seqlen > ssm::kMaxSeqlen || !valid_dstate(dstate))
+        return 0;
+    return ssm::scan_bld_workspace_bytes(batch, dim, seqlen, dstate);
+}
+
+ssm_status_t ssm_scan_fwd_bld(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype_e,
+                              unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                              const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                              const void *z, const float *h0, ssm_dtype_t out_dtype_e, void *y,
+                              float *hL, void *workspace, size_t workspace_bytes,
+                              const ssm_bld_layout_t *layout, void *stream)
+{
+    const int in_dtype = enum_bits(in_dtype_e), out_dtype = enum_bits(out_dtype_e);
+    if (!x || !dt || !A || !Bm || !Cm || !y || !workspace) return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || dim > ssm::kMaxDim ||
+        seqlen > ssm::kMaxSeqlen)
+        return SSM_ERR_BAD_SHAPE;
+    if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_ZOH_B) != 0) return SSM_ERR_UNSUPPORTED;
+    const size_t st_elems = mul3(batch, dim, dstate);
+    if (!mul3(batch, dim, seqlen) || !mul3(batch, dstate, seqlen) || !st_elems)
+        return SSM_ERR_BAD_SHAPE;
+    const ssm_bld_layout_t dense{};
+    const ssm_bld_layout_t &lay = layout ? *layout : dense;
+    // x, dt, z, y, then Bm, Cm: strides with defaults filled in, spans
+    const long long gs[6] = {lay.x_step, lay.dt_step, lay.z_step, lay.y_step, lay.B_step,
+                             lay.C_step};
+    const long long gb[6] = {lay.x_batch, lay.dt_batch, lay.z_batch, lay.y_batch, lay.B_batch,
+                             lay.C_batch};
+    long long st[6], sb[6];
+    size_t sp[6];
+    for (int i = 0; i < 6; ++i)
+        if (!bld_span(gs[i], gb[i], batch, seqlen, i < 4 ? dim : dstate, st[i], sb[i], sp[i]))
+            return SSM_ERR_BAD_SHAPE;
+    const size_t ws_bytes = ssm::scan_bld_workspace_bytes(batch, dim, seqlen, dstate);
+
+    const size_t in = dsize(in_dtype);
+    for (const void *p : {x, dt, Bm, Cm, z})
+        if (misaligned(p, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)dt_bias, (const void *)A, (const void *)Dskip,
+                          (const void *)h0, (const void *)hL, (const void *)workspace})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+    if (workspace_bytes < ws_bytes) return SSM_ERR_WORKSPACE;
+
+    const size_t ybytes = sp[3] * dsize(out_dtype);
+    const size_t hbytes = st_elems * sizeof(float);
+    struct In {
+        const void *p;
+        size_t bytes;
+    } inputs[] = {{x, sp[0] * in},     {dt, sp[1] * in},     {dt_bias, dim * sizeof(float)},
+                  {A, size_t(dim) * dstate * sizeof(float)},
+                  {Bm, sp[4] * in},    {Cm, sp[5] * in},     {Dskip, dim * sizeof(float)},
+                  {z, sp[2] * in},     {h0, hbytes}};
+    for (const In &i : inputs) {
+        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        if (hL && !(i.p == h0 && hL == h0) && overlaps(hL, hbytes, i.p, i.bytes))
+            return SSM_ERR_ALIAS;
+        if (overlaps(workspace, ws_bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, ybytes, hL, hbytes)) return SSM_ERR_ALIAS;
+    if (overlaps(workspace, ws_bytes, y, ybytes) || overlaps(workspace, ws_bytes, hL, hbytes))
+        return SSM_ERR_ALIAS;
+
+    ssm::BldArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                   (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, y, hL,
+                   st[0], sb[0], st[1], sb[1], st[2], sb[2], st[3], sb[3], st[4], sb[4], st[5],
+                   sb[5], static_cast<float *>(workspace)};
+    const hipError_t e = ssm::launch_scan_bld(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
@@ -271,24 +438,25 @@ ssm_status_t ssm_state_update(int batch, int dim, int dstate, ssm_dtype_t in_dty
                               const void *Cm, const float *Dskip, const void *z,
                               ssm_dtype_t out_dtype, void *y, void *stream)
 {
-    return ssm_state_update_strided(batch, dim, dstate, in_dtype, flags, state, x, dt, dt_bias, A,
-                                    Bm, Cm, Dskip, z, out_dtype, y, nullptr, stream);
+    return ssm_state_update_strided_impl(batch, dim, dstate, enum_bits(in_dtype), flags, state, x,
+                                         dt, dt_bias, A, Bm, Cm, Dskip, z, enum_bits(out_dtype), y,
+                                         nullptr, stream);
 }
 
-ssm_status_t ssm_state_update_strided(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
+static ssm_status_t ssm_state_update_strided_impl(int batch, int dim, int dstate, int in_dtype,
                                       unsigned flags, float *state, const void *x,
                                       const void *dt, const float *dt_bias, const float *A,
                                       const void *Bm, const void *Cm, const float *Dskip,
-                                      const void *z, ssm_dtype_t out_dtype, void *y,
+                                      const void *z, int out_dtype, void *y,
                                       const ssm_update_layout_t *layout, void *stream)
 {
     if (!state || !x || !dt || !A || !Bm || !Cm || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
-    if (batch < 1 || dim < 1) return SSM_ERR_BAD_SHAPE;
+    if (batch < 1 || dim < 1 || dim > ssm::kMaxDim) return SSM_ERR_BAD_SHAPE;
     if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_ZOH_B) != 0) return SSM_ERR_UNSUPPORTED;
 
     const size_t rows = mul3(batch, dim, 1);
-    if (batch > ssm::kMaxBatch) return SSM_ERR_BAD_SHAPE;
+    if (batch > ssm::kMaxBatch || dim > ssm::kMaxDim) return SSM_ERR_BAD_SHAPE;
     const size_t st_elems = mul3(batch, dim, dstate);
     if (!rows || !st_elems) return SSM_ERR_BAD_SHAPE;
     const ssm_update_layout_t dense{};
@@ -337,24 +505,37 @@ ssm_status_t ssm_state_update_strided(int batch, int dim, int dstate, ssm_dtype_
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+ssm_status_t ssm_state_update_strided(int batch, int dim, int dstate, ssm_dtype_t in_dtype,
+                                      unsigned flags, float *state, const void *x,
+                                      const void *dt, const float *dt_bias, const float *A,
+                                      const void *Bm, const void *Cm, const float *Dskip,
+                                      const void *z, ssm_dtype_t out_dtype, void *y,
+                                      const ssm_update_layout_t *layout, void *stream)
+{
+    return ssm_state_update_strided_impl(batch, dim, dstate, enum_bits(in_dtype), flags, state, x,
+                                         dt, dt_bias, A, Bm, Cm, Dskip, z, enum_bits(out_dtype), y,
+                                         layout, stream);
+}
+
 ssm_status_t ssm_conv1d_fwd(int batch, int dim, int seqlen, int width, ssm_dtype_t in_dtype,
                             unsigned flags, const void *x, const float *weight,
                             const float *bias, const float *state0, ssm_dtype_t out_dtype,
                             void *y, float *stateL, void *stream)
 {
-    return ssm_conv1d_fwd_strided(batch, dim, seqlen, width, in_dtype, flags, x, weight, bias,
-                                  state0, out_dtype, y, stateL, nullptr, stream);
+    return ssm_conv1d_fwd_strided_impl(batch, dim, seqlen, width, enum_bits(in_dtype), flags, x,
+                                       weight, bias, state0, enum_bits(out_dtype), y, stateL,
+                                       nullptr, stream);
 }
 
-ssm_status_t ssm_conv1d_fwd_strided(int batch, int dim, int seqlen, int width,
-                                    ssm_dtype_t in_dtype, unsigned flags, const void *x,
+static ssm_status_t ssm_conv1d_fwd_strided_impl(int batch, int dim, int seqlen, int width,
+                                    int in_dtype, unsigned flags, const void *x,
                                     const float *weight, const float *bias, const float *state0,
-                                    ssm_dtype_t out_dtype, void *y, float *stateL,
+                                    int out_dtype, void *y, float *stateL,
                                     const ssm_conv_layout_t *layout, void *stream)
 {
     if (!x || !weight || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
-    if (batch < 1 || dim < 1 || seqlen < 1) return SSM_ERR_BAD_SHAPE;
+    if (batch < 1 || dim < 1 || seqlen < 1 || dim > ssm::kMaxDim) return SSM_ERR_BAD_SHAPE;
     if (width < 2 || width > 4 || (flags & ~SSM_CONV_SILU) != 0) return SSM_ERR_UNSUPPORTED;
     const size_t st_elems = mul3(batch, dim, width - 1);
     if (!mul3(batch, dim, seqlen) || !st_elems) return SSM_ERR_BAD_SHAPE;
@@ -399,23 +580,34 @@ ssm_status_t ssm_conv1d_fwd_strided(int batch, int dim, int seqlen, int width,
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+ssm_status_t ssm_conv1d_fwd_strided(int batch, int dim, int seqlen, int width,
+                                    ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                    const float *weight, const float *bias, const float *state0,
+                                    ssm_dtype_t out_dtype, void *y, float *stateL,
+                                    const ssm_conv_layout_t *layout, void *stream)
+{
+    return ssm_conv1d_fwd_strided_impl(batch, dim, seqlen, width, enum_bits(in_dtype), flags, x,
+                                       weight, bias, state0, enum_bits(out_dtype), y, stateL,
+                                       layout, stream);
+}
+
 ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dtype,
                                unsigned flags, float *state, const void *x, const float *weight,
                                const float *bias, ssm_dtype_t out_dtype, void *y, void *stream)
 {
-    return ssm_conv1d_update_strided(batch, dim, width, in_dtype, flags, state, x, weight, bias,
-                                     out_dtype, y, 0, 0, stream);
+    return ssm_conv1d_update_strided_impl(batch, dim, width, enum_bits(in_dtype), flags, state, x,
+                                          weight, bias, enum_bits(out_dtype), y, 0, 0, stream);
 }
 
-ssm_status_t ssm_conv1d_update_strided(int batch, int dim, int width, ssm_dtype_t in_dtype,
+static ssm_status_t ssm_conv1d_update_strided_impl(int batch, int dim, int width, int in_dtype,
                                        unsigned flags, float *state, const void *x,
                                        const float *weight, const float *bias,
-                                       ssm_dtype_t out_dtype, void *y, long long x_batch,
+                                       int out_dtype, void *y, long long x_batch,
                                        long long y_batch, void *stream)
 {
     if (!state || !x || !weight || !y) return SSM_ERR_NULL_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
-    if (batch < 1 || dim < 1) return SSM_ERR_BAD_SHAPE;
+    if (batch < 1 || dim < 1 || dim > ssm::kMaxDim) return SSM_ERR_BAD_SHAPE;
     if (width < 2 || width > 4 || (flags & ~SSM_CONV_SILU) != 0) return SSM_ERR_UNSUPPORTED;
     const size_t rows = mul3(batch, dim, 1);
     const size_t st_elems = mul3(batch, dim, width - 1);
@@ -452,9 +644,22 @@ ssm_status_t ssm_conv1d_update_strided(int batch, int dim, int width, ssm_dtype_
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+ssm_status_t ssm_conv1d_update_strided(int batch, int dim, int width, ssm_dtype_t in_dtype,
+                                       unsigned flags, float *state, const void *x,
+                                       const float *weight, const float *bias,
+                                       ssm_dtype_t out_dtype, void *y, long long x_batch,
+                                       long long y_batch, void *stream)
+{
+    return ssm_conv1d_update_strided_impl(batch, dim, width, enum_bits(in_dtype), flags, state, x,
+                                          weight, bias, enum_bits(out_dtype), y, x_batch, y_batch,
+                                          stream);
+}
+
 size_t ssm_scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 {
-    if (batch < 1 || dim < 1 || seqlen < 1 || dstate < 1) return 0;
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || dim > ssm::kMaxDim ||
+        seqlen > ssm::kMaxSeqlen || !valid_dstate(dstate))
+        return 0;
     return ssm::scan_bwd_workspace_bytes(batch, dim, seqlen, dstate);
 }
 
@@ -466,16 +671,17 @@ ssm_status_t ssm_scan_bwd(int batch, int dim, int seqlen, int dstate, ssm_dtype_
                           float *dBm, float *dCm, float *dA, float *dDskip, float *ddt_bias,
                           float *dh0, void *workspace, size_t workspace_bytes, void *stream)
 {
-    return ssm_scan_bwd_strided(batch, dim, seqlen, dstate, in_dtype, flags, x, dt, dt_bias, A, Bm,
-                                Cm, Dskip, z, h0, grad_dtype, dy, dhL, dx, ddt, dz, dBm, dCm, dA,
-                                dDskip, ddt_bias, dh0, workspace, workspace_bytes, nullptr, stream);
+    return ssm_scan_bwd_strided_impl(batch, dim, seqlen, dstate, enum_bits(in_dtype), flags, x, dt,
+                                     dt_bias, A, Bm, Cm, Dskip, z, h0, enum_bits(grad_dtype), dy,
+                                     dhL, dx, ddt, dz, dBm, dCm, dA, dDskip, ddt_bias, dh0,
+                                     workspace, workspace_bytes, nullptr, stream);
 }
 
-ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
-                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+static ssm_status_t ssm_scan_bwd_strided_impl(int batch, int dim, int seqlen, int dstate,
+                                  int in_dtype, unsigned flags, const void *x,
                                   const void *dt, const float *dt_bias, const float *A,
                                   const void *Bm, const void *Cm, const float *Dskip,
-                                  const void *z, const float *h0, ssm_dtype_t grad_dtype,
+                                  const void *z, const float *h0, int grad_dtype,
                                   const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
                                   float *dBm, float *dCm, float *dA, float *dDskip,
                                   float *ddt_bias, float *dh0, void *workspace,
@@ -487,7 +693,8 @@ ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
     if (z && !dz) return SSM_ERR_NULL_ARG;
     if (!z) dz = nullptr;
     if (!valid_dtype(in_dtype) || !valid_dtype(grad_dtype)) return SSM_ERR_BAD_DTYPE;
-    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || seqlen > ssm::kMaxSeqlen)
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || dim > ssm::kMaxDim ||
+        seqlen > ssm::kMaxSeqlen)
         return SSM_ERR_BAD_SHAPE;
     if (!valid_dstate(dstate) || (flags & ~(SSM_FLAG_CHECKPOINTS | SSM_FLAG_ZOH_B)) != 0)
         return SSM_ERR_UNSUPPORTED;
@@ -554,6 +761,23 @@ ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
                    bc_row, bc_b[0], bc_b[1], (flags & SSM_FLAG_ZOH_B) != 0};
     const hipError_t e = ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
+                                  ssm_dtype_t in_dtype, unsigned flags, const void *x,
+                                  const void *dt, const float *dt_bias, const float *A,
+                                  const void *Bm, const void *Cm, const float *Dskip,
+                                  const void *z, const float *h0, ssm_dtype_t grad_dtype,
+                                  const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                                  float *dBm, float *dCm, float *dA, float *dDskip,
+                                  float *ddt_bias, float *dh0, void *workspace,
+                                  size_t workspace_bytes, const ssm_scan_bwd_layout_t *layout,
+                                  void *stream)
+{
+    return ssm_scan_bwd_strided_impl(batch, dim, seqlen, dstate, enum_bits(in_dtype), flags, x, dt,
+                                     dt_bias, A, Bm, Cm, Dskip, z, h0, enum_bits(grad_dtype), dy,
+                                     dhL, dx, ddt, dz, dBm, dCm, dA, dDskip, ddt_bias, dh0,
+                                     workspace, workspace_bytes, layout, stream);
 }
 
 }  // extern "C"

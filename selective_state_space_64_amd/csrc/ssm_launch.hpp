@@ -29,7 +29,7 @@ struct ScanArgs {
 };
 
 // Sequence split of the forward scan: segments of seg_len steps (a multiple
-// of the 128-step chunk) scanned by separate workgroups.  A function of the
+// of the aggregate pass's 256-step chunk) scanned by separate workgroups.  A function of the
 // shape only, so that the workspace size is known before the call.
 struct ScanSplit {
     int nseg, seg_len;
@@ -95,6 +95,32 @@ struct BwdArgs {
     int zoh;  // the exact zero-order-hold form of B-bar
 };
 
+// The forward on (batch, L, dim)-ordered tensors (scan_bld.hip): element
+// strides of a time step and of a batch entry for each tensor; the channel
+// (x, dt, z, y) or state (Bm, Cm) index is contiguous.
+struct BldArgs {
+    int batch, dim, seqlen, dstate;
+    int in_bf16, out_bf16, zoh;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *h0;
+    void *y;
+    float *hL;
+    long long x_t, x_b, dt_t, dt_b, z_t, z_b, y_t, y_b, B_t, B_b, C_t, C_b;
+    float *workspace;  // scan_bld_workspace_bytes
+};
+// Pieces of the sequence scanned by separate waves (a function of the shape).
+struct BldSplit {
+    int npieces, piece_len;
+};
+BldSplit bld_split(int batch, int dim, int seqlen);
+// One record of dstate + 1 floats per piece and (batch, channel).
+size_t scan_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate);
+hipError_t launch_scan_bld(const BldArgs &a, hipStream_t stream);
+
 // The backward pass keeps the state entering every kCkptSteps-step chunk
 // (batch * dim * ceil(seqlen / kCkptSteps) * dstate floats at the start of
 // its workspace); the forward writes the same layout with checkpoints on.
@@ -115,8 +141,22 @@ hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream);
 
+// Dispatch log: with the environment variable SSM_LOG set to a non-zero
+// value when the library is first used, every launch prints one line to
+// stderr (entry point, kernel instantiation, split, grid).  Read once.
+bool log_enabled();
+void log_line(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+template <typename T>
+constexpr const char *type_tag()
+{
+    return sizeof(T) == 2 ? "bf16" : "f32";
+}
+
 // Largest batch the kernels' grids support (grid y dimension).
 constexpr int kMaxBatch = 65535;
+// Largest dim: channel indices are 32-bit ints inside the kernels (workgroup
+// index times channels per workgroup, plus the lane's channel).
+constexpr int kMaxDim = 1 << 30;
 // Longest sequence: the scan addresses the 4 rows of a wave with 32-bit byte
 // offsets, (4 L + 2 chunks) * 4 bytes < 2^32.
 constexpr int kMaxSeqlen = (1 << 28) - (1 << 12);

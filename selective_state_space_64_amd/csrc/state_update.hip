@@ -175,7 +175,11 @@ hipError_t launch_rows(const UpdateArgs &a, const UpdateParams &p, hipStream_t s
 {
     constexpr int R = N < kStatesPerLane ? 1 : N / kStatesPerLane;
     constexpr int per_block = kThreads / R * U;  // channels per workgroup
-    const dim3 grid(unsigned((a.dim + per_block - 1) / per_block), a.batch);
+    const dim3 grid((unsigned(a.dim) + per_block - 1) / per_block, a.batch);
+    if (log_enabled())
+        log_line("state_update: state_update_kernel<in %s, out %s, N %d, zoh %d, rows per lane %d>, "
+                 "grid (%u, %u) x %d threads", type_tag<Tin>(), type_tag<Tout>(), N, int(kZoh), U,
+                 grid.x, grid.y, kThreads);
     hipLaunchKernelGGL((state_update_kernel<Tin, Tout, N, kZoh, U>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssm_peaks.so")
 CUS, CLOCK_HZ = 256, 2.4e9
 NOMINAL_SLOTS = CUS * 128 * CLOCK_HZ
-KINDS = {0: "fma", 1: "exp2", 2: "scan_mix"}
+KINDS = {0: "fma", 1: "exp2", 2: "scan_mix", 3: "fma_sgpr_operand"}
 
 _lib = None
 
@@ -33,7 +33,7 @@ def lib():
     return _lib
 
 
-def measure(torch, blocks=CUS * 8, iters=(4096, 1024, 1024), repeats=5):
+def measure(torch, blocks=CUS * 8, iters=(4096, 1024, 1024, 4096), repeats=5):
     """Median over `repeats` launches of each probe, 2048 workgroups of 256
     threads (8 waves per SIMD) by default."""
     L = lib()
@@ -67,6 +67,7 @@ def measure(torch, blocks=CUS * 8, iters=(4096, 1024, 1024), repeats=5):
         "fma": res["fma"]["lane_ops_per_s"] / NOMINAL_SLOTS,
         "exp2_x4": 4.0 * res["exp2"]["lane_ops_per_s"] / NOMINAL_SLOTS,
         "scan_mix": mix["slots_per_s"] / NOMINAL_SLOTS,
+        "fma_sgpr_operand": res["fma_sgpr_operand"]["lane_ops_per_s"] / NOMINAL_SLOTS,
     }
     res["note"] = ("probe kernels built like the library (no packed fp32); slots count a "
                    "transcendental as 4, as the rooflines do")

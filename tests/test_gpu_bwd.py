@@ -275,7 +275,9 @@ def test_bwd_checkpoints_from_forward(shape):
     """SSM_FLAG_CHECKPOINTS: the forward writes the state entering every
     64-step chunk into the backward's workspace without changing its own
     outputs, and the backward that reads them matches the one that
-    recomputes them (bit for bit where no atomics are involved)."""
+    recomputes them.  Not bit for bit: the recomputation folds 16 steps per
+    lane where the forward folds 8, so the two sets of checkpoints differ in
+    the order of their fp32 roundings."""
     batch, dim, N, L, dt = shape
     inp = synth.make_inputs(workload("ckpt", batch, dim, N, L, dt, seed=13), with_h0=True)
     t = {k: to_dev(inp, k) for k in ("x", "dt", "A", "Bm", "Cm", "dt_bias", "Dskip", "z")}
@@ -293,7 +295,5 @@ def test_bwd_checkpoints_from_forward(shape):
     g1 = ssm.ssm_scan_bwd(t["x"], t["dt"], t["A"], t["Bm"], t["Cm"], dy, workspace=ws,
                           checkpoints_in_workspace=True, **kw)
     torch.cuda.synchronize()
-    for k in ("dx", "ddt", "dz", "dh0"):
-        assert torch.equal(g0[k], g1[k]), k
-    for k in ("dBm", "dCm", "dA", "dDskip", "ddt_bias"):
+    for k in ("dx", "ddt", "dz", "dh0", "dBm", "dCm", "dA", "dDskip", "ddt_bias"):
         assert float((g0[k] - g1[k]).abs().max()) <= 1e-5 * float(g0[k].abs().max()) + 1e-30, k

@@ -241,3 +241,46 @@ def test_explicit_stream_argument():
             assert rel_err(out[k].cpu().numpy()[None], ref[k].cpu().numpy()[None]) <= 1e-6, k
         else:
             assert torch.equal(ref[k], out[k]), k
+
+
+def test_dispatch_log(tmp_path):
+    """SSM_LOG=1 (read once, when the library is first used) prints one line
+    per launch naming the kernel instantiation, the split and the grid; a
+    child process runs a split forward, an unsplit forward, a decode step, a
+    conv and a backward pass with it set."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = """
+import torch, selective_state_space_64_amd as ssm
+d = 'cuda'
+def t(*s, bf=False):
+    x = torch.randn(*s, device=d)
+    return x.to(torch.bfloat16) if bf else x
+A = -torch.rand(32, 16, device=d)
+ssm.ssm_scan_fwd(t(1, 32, 8192), t(1, 32, 8192), A, t(1, 16, 8192), t(1, 16, 8192))
+ssm.ssm_scan_fwd(t(2, 32, 100, bf=True), t(2, 32, 100, bf=True), A, t(2, 16, 100, bf=True),
+                 t(2, 16, 100, bf=True))
+ssm.ssm_state_update(torch.zeros(2, 32, 16, device=d), t(2, 32), t(2, 32), A, t(2, 16), t(2, 16))
+ssm.ssm_conv1d_fwd(t(2, 32, 100), torch.randn(32, 4, device=d))
+ssm.ssm_scan_bwd(t(2, 32, 100), t(2, 32, 100), A, t(2, 16, 100), t(2, 16, 100), t(2, 32, 100))
+torch.cuda.synchronize()
+"""
+    env = dict(os.environ, SSM_LOG="1", PYTHONPATH=root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=300, cwd=root)
+    assert r.returncode == 0, r.stderr[-3000:]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[ssm] ")]
+    text = "\n".join(lines)
+    assert "sequence split into" in text and "scan_fwd_kernel<in f32, N 16, K 16, zoh 0, aggregate>" in text
+    assert "main pass, grid (2, 1, " in text
+    assert "scan_fwd_kernel<in bf16, out f32, N 16, K 8" in text and "no split" in text
+    assert "state_update_kernel<in f32, out f32, N 16" in text
+    assert "conv1d_fwd_kernel<in f32, out f32, W 4>" in text
+    assert "scan_bwd: checkpoints recomputed" in text
+    # without the variable the library prints nothing
+    env.pop("SSM_LOG")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       timeout=300, cwd=root)
+    assert r.returncode == 0 and "[ssm]" not in r.stderr
