@@ -59,10 +59,11 @@ KERNEL_SOURCES = ("selective_state_space_64_amd/csrc/scan_fwd.hip",
 
 def scan_kernel_name(in_dtype, agg=False):
     """The scan kernel's instantiation for a workload (rocprofv3 prints it in
-    the kernel name): Tin, Tout, N, K, kZoh, kCkpt, kAgg, kOut."""
+    the kernel name): Tin, Tout, N, K, kZoh, kCkpt, kAgg, kOut.  The split's
+    aggregate pass folds 16 steps per lane, the main pass 8."""
     tin = "ssm::bf16_t" if in_dtype == "bf16" else "float"
-    return "scan_fwd_kernel<%s, float, 16, 8, false, false, %s, true>" % (
-        tin, "true" if agg else "false")
+    return "scan_fwd_kernel<%s, float, 16, %d, false, false, %s, true>" % (
+        tin, 16 if agg else 8, "true" if agg else "false")
 
 
 SCAN_KERNEL = scan_kernel_name("bf16")
@@ -207,6 +208,8 @@ def parse(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time only ssm_scan_bwd on --workload (for profiler passes)")
     ap.add_argument("--only-workload", action="store_true",
                     help="time only --workload (for profiling one configuration) and exit")
     return ap.parse_args(argv)
@@ -675,6 +678,12 @@ def main():
         res, _ = measure_scan(torch, ssm, synth, wl, args.steps, flusher,
                               warmup_seconds=args.warmup_seconds, warmup=args.warmup)
         print(json.dumps(res), flush=True)
+        return
+    if args.only_backward:
+        inp = synth.make_inputs(wl)
+        t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}
+        del inp
+        print(json.dumps(bench_bwd(torch, ssm, wl, t, launches=args.steps)), flush=True)
         return
     inp = synth.make_inputs(wl)
     t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}

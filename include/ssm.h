@@ -194,10 +194,10 @@ ssm_status_t ssm_scan_fwd_strided(int batch, int dim, int seqlen, int dstate,
  * harnesses that forbid hipMalloc.  The call itself allocates nothing either.
  * Where ssm_scan_fwd_workspace_bytes(...) is non-zero (a sequence split), the
  * split's planes go to a scratch array inside the library: one copy per GPU,
- * 4 456 448 bytes (4096 x 16 x 17 floats), held from the library's first use
- * on that GPU until the process ends.  Every split shape fits in it (the
- * split makes segments x batch x dim at most 4096 x 16); a shape that did not
- * would be SSM_ERR_WORKSPACE.  All calls on one GPU share that GPU's array:
+ * 17 825 792 bytes (16384 x 16 x 17 floats), held from the library's first
+ * use on that GPU until the process ends.  Every split shape fits in it (the
+ * split makes segments x batch x dim at most 16384 x 16); a shape that did
+ * not would be SSM_ERR_WORKSPACE.  All calls on one GPU share that GPU's array:
  * calls that overlap in time on the same GPU (on other streams or from other
  * threads) race on it and must be serialised by the caller.  Nothing in it
  * needs clearing between calls.  `stream` must belong to the current device.

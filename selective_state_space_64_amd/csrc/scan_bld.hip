@@ -38,6 +38,10 @@ namespace ssm {
 namespace {
 
 constexpr int kLanes = 64;  // one wave: 64 consecutive channels
+// Pieces per (batch, channel block): about this many waves in all.
+#ifndef SSM_BLD_TARGET_WAVES
+#define SSM_BLD_TARGET_WAVES 4096
+#endif
 
 struct BldParams {
     int dim, seqlen, npieces, piece_len;
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(kLanes) void bld_main_kernel(
 BldSplit bld_split_impl(int batch, int dim, int seqlen)
 {
     const long long waves = (long long)batch * ((dim + kLanes - 1) / kLanes);
-    long long np = (4096 + waves - 1) / waves;
+    long long np = (SSM_BLD_TARGET_WAVES + waves - 1) / waves;
     np = std::max(1LL, std::min<long long>(np, seqlen / 64));
     np = std::min<long long>(np, 65535);
     BldSplit s;

@@ -46,6 +46,9 @@ namespace {
 #ifndef SSM_SCAN_K
 #define SSM_SCAN_K 8
 #endif
+#ifndef SSM_SCAN_PAIRS
+#define SSM_SCAN_PAIRS 1
+#endif
 #ifndef SSM_SCAN_MINW_BF16
 #define SSM_SCAN_MINW_BF16 4
 #endif
@@ -59,17 +62,17 @@ constexpr int kChannels = kThreads / kRow;  // channels per workgroup
 constexpr int kK = SSM_SCAN_K;              // consecutive timesteps per lane
 // Sequence split (see scan_fwd_split): used when the batch rows and channel
 // blocks give fewer than SSM_SPLIT_BELOW_WGS workgroups; aims at
-// SSM_SPLIT_TARGET_WGS workgroups with segments of at least
-// SSM_SPLIT_MIN_STEPS steps.  The aggregate pass costs about 0.8 of a
-// forward pass, so a split pays where the unsplit launch runs the chip at
-// under about half its rate: measured, fewer than ~300 workgroups (a 2x to 4x
-// gain at 48 to 128 workgroups, a loss at 320 with two segments).  Many
-// segments (~16 workgroups per CU) keep the last wave's tail short.
+// kSplitTargetWgs workgroups (ssm_launch.hpp) with segments of at least
+// SSM_SPLIT_MIN_STEPS steps.  The aggregate pass costs about 0.6 of a main
+// pass, so a split pays where the unsplit launch runs the chip at under
+// about half its rate: measured, fewer than ~300 workgroups (a 2x to 4x gain
+// at 48 to 128 workgroups, a loss at 320 with two segments).  Many segments
+// (~64 workgroups per CU) keep the last wave's tail short: at batch 1, 1536
+// channels and 2^20 steps, targets of 4096 / 16384 / 32768 workgroups
+// measured 14.61 / 14.15 / 15.75 ms per forward call, and the backward call
+// 45.5 ms at 4096 against 44.5 ms at 16384.
 #ifndef SSM_SPLIT_BELOW_WGS
 #define SSM_SPLIT_BELOW_WGS 256
-#endif
-#ifndef SSM_SPLIT_TARGET_WGS
-#define SSM_SPLIT_TARGET_WGS 4096
 #endif
 #ifndef SSM_SPLIT_MIN_STEPS
 #define SSM_SPLIT_MIN_STEPS 1024
@@ -468,10 +471,14 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         // x and dt are fetched during the last third.
         if constexpr (N >= 8) {
             constexpr int N1 = (N + 2) / 3, N2 = N - (N + 2) / 3;
-            // Two states per loop trip share the LDS address updates (3.5
-            // fewer VALU per state, 1-2 % faster at 128 VGPRs); the other
-            // variants would spill at that unroll, so they keep one.
-            constexpr int kSU = (sizeof(Tin) == 2 && N == 16 && !kZoh && !kCkpt && kRead) ? 2 : 1;
+            // Two states per loop trip (state_pair: shared LDS address
+            // updates, the two DPP scans interleaved with no wait states):
+            // measured in interleaved runs against one state per trip
+            // (SSM_SCAN_PAIRS=0), 1.5 % faster at the 130M-layer shape and
+            // equal within noise at the 2.8B layer.  The other variants
+            // would spill at that unroll, so they keep one.
+            constexpr int kSU =
+                (SSM_SCAN_PAIRS && K == 8 && sizeof(Tin) == 2 && N == 16 && !kZoh && !kCkpt && kRead) ? 2 : 1;
             if (more && stager) {
                 stage_load(Bb, ch + 1, stB);
                 if constexpr (kRead) stage_load(Cb, ch + 1, stC);
@@ -633,7 +640,7 @@ ScanSplit scan_fwd_split(int batch, int dim, int seqlen)
     const long long wgs = (long long)batch * (((long long)dim + kChannels - 1) / kChannels);
     ScanSplit sp{1, seqlen};
     if (wgs >= SSM_SPLIT_BELOW_WGS) return sp;
-    long long nseg = SSM_SPLIT_TARGET_WGS / wgs;  // whole waves of workgroups
+    long long nseg = kSplitTargetWgs / wgs;  // whole multiples of the workgroups
     nseg = std::min<long long>(nseg, seqlen / SSM_SPLIT_MIN_STEPS);
     nseg = std::min<long long>(nseg, kMaxSegments);
     if (nseg < 2) return sp;

@@ -91,15 +91,16 @@ bool batch_span(long long given, int batch, int rows, long long rs, int seqlen, 
 // Device scratch of ssm_scan_fwd_noalloc: a file-scope array, one copy per
 // GPU (held from the library's first use on that GPU until the process
 // ends).  It holds the sequence split's planes, at most kScratchBytes: the
-// split gives at most 4096 / (batch * ceil(dim / 16)) segments, so segments x
-// batch x dim <= 4096 * 16, times (dstate + 1) <= 17 floats.  In host code
+// split gives at most kSplitTargetWgs / (batch * ceil(dim / 16)) segments, so
+// segments x batch x dim <= kSplitTargetWgs * 16, times (dstate + 1) <= 17
+// floats (17 825 792 bytes for 16384 workgroups).  In host code
 // the array's name is only a stand-in for the symbol; its device address
 // comes from hipGetSymbolAddress, once per device, and only that address is
 // ever handed to a kernel.  Every call on a GPU shares that GPU's copy, so
 // calls that overlap in time on one GPU (other streams, other threads) race
 // on it.  Nothing in it needs clearing between calls: the aggregate pass
 // writes every plane the main pass reads.
-constexpr size_t kScratchBytes = size_t(4096) * 16 * 17 * sizeof(float);
+constexpr size_t kScratchBytes = size_t(ssm::kSplitTargetWgs) * 16 * 17 * sizeof(float);
 static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 
 constexpr int kMaxDevices = 64;

@@ -125,6 +125,14 @@ hipError_t launch_scan_bld(const BldArgs &a, hipStream_t stream);
 // (batch * dim * ceil(seqlen / kCkptSteps) * dstate floats at the start of
 // its workspace); the forward writes the same layout with checkpoints on.
 constexpr int kCkptSteps = 64;
+
+// The forward's sequence split aims at this many workgroups in all (16
+// channels each); it also bounds the split's planes: segments x batch x dim
+// <= kSplitTargetWgs x 16.
+#ifndef SSM_SPLIT_TARGET_WGS
+#define SSM_SPLIT_TARGET_WGS 16384
+#endif
+constexpr long long kSplitTargetWgs = SSM_SPLIT_TARGET_WGS;
 inline size_t scan_checkpoint_floats(int batch, int dim, int seqlen, int dstate)
 {
     return size_t(batch) * size_t(dim) * ((size_t(seqlen) + kCkptSteps - 1) / kCkptSteps) *

@@ -365,13 +365,13 @@ def test_strided_validation_spans_and_defaults():
 
 def _split_bytes(batch, dim, L, N):
     """The documented split rule, restated: split when batch * ceil(dim / 16)
-    < 256, into whole multiples of that many workgroups up to 4096, segments
+    < 256, into whole multiples of that many workgroups up to 16384, segments
     >= 1024 steps and a multiple of 256 (whole chunks of the aggregate pass's
     16-step lanes), at most 1024 segments."""
     wgs = batch * ((dim + 15) // 16)
     if wgs >= 256:
         return 0
-    nseg = min(4096 // wgs, L // 1024, 1024)
+    nseg = min(16384 // wgs, L // 1024, 1024)
     if nseg < 2:
         return 0
     seg = -(-(-(-L // nseg)) // 256) * 256
@@ -391,8 +391,8 @@ def test_fwd_workspace_bytes_examples():
     L = ssm.lib()
     assert L.ssm_scan_fwd_workspace_bytes(4, 5120, 2048, 16) == 0      # 1280 workgroups
     assert L.ssm_scan_fwd_workspace_bytes(1, 16, 2048, 16) == 2 * 16 * 17 * 4
-    # the long sequence: 96 workgroups -> 42 segments of 25 088 steps
-    assert L.ssm_scan_fwd_workspace_bytes(1, 1536, 1 << 20, 16) == 42 * 1536 * 17 * 4
+    # the long sequence: 96 workgroups -> 164 segments of 6400 steps
+    assert L.ssm_scan_fwd_workspace_bytes(1, 1536, 1 << 20, 16) == 164 * 1536 * 17 * 4
     assert L.ssm_scan_fwd_workspace_bytes(2, 2560, 2048, 16) == 0      # 320 workgroups
     assert L.ssm_scan_fwd_workspace_bytes(0, 16, 4096, 16) == 0
     assert L.ssm_scan_fwd_workspace_bytes(1, 16, 4096, 3) == 0

@@ -62,7 +62,7 @@ def test_split_full_tensor(shape):
 def test_split_segment_count():
     """The shapes above really are split, into the expected segment counts."""
     assert _nseg(1, 16, 4096) == 4           # 1 workgroup, 1024-step segments
-    assert _nseg(1, 1536, 1 << 20) == 42     # 96 workgroups
+    assert _nseg(1, 1536, 1 << 20) == 164    # 96 workgroups, 6400-step segments
     assert _nseg(4, 5120, 2048) == 0         # 1280 workgroups: not split
 
 
