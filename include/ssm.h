@@ -15,7 +15,7 @@
  *                     (batch, L, dim, N) state is never written to memory;
  *                     only the contracted output and the final state are.
  *                     B-bar follows the simplified form dB = Delta * B of the
- *                     dynamic-parameterization section of the soft186.com page
+ *                     dynamic-parameterization section of the page
  *                     "Mamba选择性状态空间机制：效率提升10倍的核心突破", or,
  *                     with SSM_FLAG_ZOH_B, the exact zero-order-hold form.
  *                     Output: y = (C . h + Dskip * x) * silu(z), silu(z) =

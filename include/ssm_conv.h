@@ -5,7 +5,7 @@
  * The Mamba block applies a short 1-D convolution over the sequence before
  * the selective SSM (glossary entry "Mamba Block" of the page "Mamba:
  * Linear-Time Sequence Modeling with Selective State Spaces"; the basic-model
- * example of the soft186.com page "Mamba选择性状态空间机制：效率提升10倍的核心突破"
+ * example of the page "Mamba选择性状态空间机制：效率提升10倍的核心突破"
  * uses d_conv = 4).  The inference cache keeps the convolutional state beside
  * the SSM state ("everything-about-mamba-paper", blogofoto.com), and the fast
  * path pairs the scan kernels with a causal conv1d kernel

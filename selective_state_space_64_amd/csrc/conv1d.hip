@@ -4,7 +4,8 @@
 // The Mamba block runs a short 1-D convolution over the sequence before the
 // selective SSM (glossary entry "Mamba Block" of the page "Mamba: Linear-Time
 // Sequence Modeling with Selective State Spaces"; d_conv = 4 in the
-// basic-model example of the soft186.com page), and the inference cache keeps
+// basic-model example of the page "Mamba选择性状态空间机制：效率提升10倍的核心突破"),
+// and the inference cache keeps
 // its convolutional state beside the SSM state ("everything-about-mamba-paper").
 // Per (batch b, channel d), with the W-1 inputs before t = 0 taken from the
 // conv state (oldest first) or zero:

@@ -22,8 +22,8 @@
 //   1. each lane folds its K steps into one affine map h -> a h + b
 //      (a = exp2(A' sum Delta), b by a K-step fma chain),
 //   2. a 4-level DPP row scan composes the 16 maps (the associative scan of
-//      "Hardware-aware state expansion"; the chunking follows the soft186.com
-//      page's chunked-computation section),
+//      "Hardware-aware state expansion"; the chunking follows the chunked
+//      computation of the page "Mamba选择性状态空间机制：效率提升10倍的核心突破"),
 //   3. each lane applies its prefix to the carry entering the chunk and
 //      replays its K steps, accumulating C_t h_t into y_t,
 //   4. the row's last lane publishes the carry for the next chunk in LDS.
@@ -202,10 +202,11 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         const int dd = min(int(blockIdx.x) * kChannels + cc, dim - 1);
         sAC[cc * 2 * NP + n] = (n < N) ? p.A[size_t(dd) * N + n] * kLog2e : 0.0f;
     }
-    if (j == 0) {
+    {
         // State entering the segment: h0 for the first; otherwise the
         // segments before it composed in order, h <- exp(A sum Delta) h + end
-        // state (each segment's map is affine in its entering state).
+        // state (each segment's map is affine in its entering state), lane j
+        // of the channel's row composing state j.
         // With a split, the aggregate pass copies h0 into the last plane of
         // agg and the main pass reads that copy, so that hL may overwrite h0
         // while other segments of the same channel are still running.
@@ -213,30 +214,27 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         float *h0copy = p.nseg > 1 ? p.agg + ((size_t(p.nseg - 1) * gridDim.y + b) * dim + dc) * NP
                                    : nullptr;
         if (seg == 0 || kAgg) {
-            const bool copy = !kAgg && h0copy;
+            if (j == 0) {
+                const bool copy = !kAgg && h0copy;
 #pragma unroll
-            for (int n = 0; n < N; ++n) {
-                const float v = (p.h0 && seg == 0)
-                                    ? (copy ? h0copy[n] : p.h0[(size_t(b) * dim + dc) * N + n])
-                                    : 0.0f;
-                hin[n] = v;
-                if (kAgg && seg == 0 && p.h0 && live) h0copy[n] = v;
+                for (int n = 0; n < N; ++n) {
+                    const float v = (p.h0 && seg == 0)
+                                        ? (copy ? h0copy[n] : p.h0[(size_t(b) * dim + dc) * N + n])
+                                        : 0.0f;
+                    hin[n] = v;
+                    if (kAgg && seg == 0 && p.h0 && live) h0copy[n] = v;
+                }
             }
-        } else {
-            float h[N];
-#pragma unroll
-            for (int n = 0; n < N; ++n) h[n] = 0.0f;
+        } else if (j < N) {
+            const float a = p.A[size_t(dc) * N + j] * kLog2e;
+            float h = 0.0f;
             for (int s = 0; s < seg; ++s) {
                 const float *ag = p.agg + ((size_t(s) * gridDim.y + b) * dim + dc) * NP;
-                const float sd = ag[N];
-#pragma unroll
-                for (int n = 0; n < N; ++n)
-                    h[n] = __builtin_fmaf(exp2_hw(p.A[size_t(dc) * N + n] * kLog2e * sd), h[n], ag[n]);
+                h = __builtin_fmaf(exp2_hw(a * ag[N]), h, ag[j]);
             }
-#pragma unroll
-            for (int n = 0; n < N; ++n) hin[n] = h[n];
+            hin[j] = h;
         }
-        hin[N] = 0.0f;
+        if (j == 0) hin[N] = 0.0f;
     }
 
     // Staging slot of this thread: state sn, lane block sj (threads < N*16).

@@ -315,7 +315,7 @@ def pin_softplus_silu(o):
 # --------------------------------------------------------------------------
 # Causal depthwise conv in front of the scan (glossary entry "Mamba Block";
 # conv state in the inference cache, "everything-about-mamba-paper";
-# d_conv = 4, soft186.com basic-model example).
+# d_conv = 4, the basic-model example of "Mamba选择性状态空间机制：效率提升10倍的核心突破").
 # --------------------------------------------------------------------------
 def _rand_conv(rng, batch, dim, L, W, state=True):
     return dict(x=rng.standard_normal((batch, dim, L)), weight=rng.standard_normal((dim, W)),
