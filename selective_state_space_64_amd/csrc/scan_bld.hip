@@ -53,10 +53,23 @@ struct BldParams {
     int bc_words;  // every Bm and Cm row starts on a 4-byte boundary
 };
 
+// A step's inputs are fetched as raw bits one step before they are used and
+// decoded where used (the loops below alternate two such buffers), so that
+// the memory latency of step t+1's loads overlaps step t's work.
 template <typename T>
-__device__ inline float load_elem(const T *p)
+__device__ inline uint32_t load_bits(const T *p)
 {
-    return io<T>::load1(p);
+    if constexpr (sizeof(T) == 4) {
+        return __float_as_uint(*reinterpret_cast<const float *>(p));
+    } else {
+        return uint32_t(p->bits);
+    }
+}
+
+template <typename T>
+__device__ inline float decode_bits(uint32_t w)
+{
+    return sizeof(T) == 4 ? __uint_as_float(w) : __uint_as_float(w << 16);
 }
 
 template <typename Tout>
@@ -69,32 +82,56 @@ __device__ inline void store_elem(Tout *p, float v)
     }
 }
 
-// The Bm (or Cm) row of one step: N values shared by the whole wave.  The
-// address is made visibly wave-uniform (read from the first lane into
-// scalar registers), so that where the compiler can prove the row unchanged
-// by the kernel's own stores it comes through the scalar data cache into
-// SGPRs once per wave (the aggregate pass) instead of as a 64-lane vector
-// load.  bf16 rows are read as 32-bit words only when `words` says every
-// row starts on a 4-byte boundary: a scalar load ignores the address's two
-// low bits.
+// The Bm (or Cm) row of one step: N values shared by the whole wave, held as
+// raw words (bf16: two states per word, fp32: one).  The address is made
+// visibly wave-uniform (read from the first lane into scalar registers), so
+// that where the compiler can prove the row unchanged by the kernel's own
+// stores it comes through the scalar data cache into SGPRs once per wave
+// (the aggregate pass) instead of as a 64-lane vector load.  bf16 rows are
+// read as 32-bit words only when `words` says every row starts on a 4-byte
+// boundary (a scalar load ignores the address's two low bits); otherwise
+// two 16-bit loads are packed into each word.
 template <typename Tin, int N>
-__device__ inline void load_row(const Tin *p, bool words, float *v)
+struct Row {
+    static constexpr bool kPacked = sizeof(Tin) == 2 && N % 2 == 0;
+    static constexpr int kWords = kPacked ? N / 2 : N;
+    uint32_t w[kWords];
+};
+
+template <typename Tin, int N>
+__device__ inline void row_fetch(const Tin *p, bool words, Row<Tin, N> &r)
 {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
     const Tin *__restrict__ q = reinterpret_cast<const Tin *>((uint64_t(hi) << 32) | lo);
-    if (sizeof(Tin) == 2 && N % 2 == 0 && words) {
-        const uint32_t *w = reinterpret_cast<const uint32_t *>(q);
+    if constexpr (Row<Tin, N>::kPacked) {
+        if (words) {
+            const uint32_t *u = reinterpret_cast<const uint32_t *>(q);
 #pragma unroll
-        for (int n = 0; n < N / 2; ++n) {
-            const uint32_t u = w[n];
-            v[2 * n] = io<bf16_t>::lo(u);
-            v[2 * n + 1] = io<bf16_t>::hi(u);
+            for (int n = 0; n < N / 2; ++n) r.w[n] = u[n];
+        } else {
+#pragma unroll
+            for (int n = 0; n < N / 2; ++n) r.w[n] = load_bits(q + 2 * n) | (load_bits(q + 2 * n + 1) << 16);
         }
     } else {
 #pragma unroll
-        for (int n = 0; n < N; ++n) v[n] = load_elem(q + n);
+        for (int n = 0; n < N; ++n) r.w[n] = load_bits(q + n);
+    }
+}
+
+template <typename Tin, int N>
+__device__ inline void row_decode(const Row<Tin, N> &r, float *v)
+{
+    if constexpr (Row<Tin, N>::kPacked) {
+#pragma unroll
+        for (int n = 0; n < N / 2; ++n) {
+            v[2 * n] = io<bf16_t>::lo(r.w[n]);
+            v[2 * n + 1] = io<bf16_t>::hi(r.w[n]);
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < N; ++n) v[n] = decode_bits<Tin>(r.w[n]);
     }
 }
 
@@ -123,11 +160,24 @@ __global__ __launch_bounds__(kLanes) void bld_agg_kernel(BldParams p, const Tin 
     const Tin *xp = x + size_t(b) * size_t(p.x_b) + size_t(t0) * size_t(p.x_t) + dc;
     const Tin *dp = dt + size_t(b) * size_t(p.dt_b) + size_t(t0) * size_t(p.dt_t) + dc;
     const Tin *bp = Bm + size_t(b) * size_t(p.B_b) + size_t(t0) * size_t(p.B_t);
+    const bool words = p.bc_words != 0;
     float sumd = 0.0f;
-    for (int t = t0; t < t1; ++t) {
-        const float xv = load_elem(xp), delta = softplus(load_elem(dp) + bias);
+    struct In {
+        uint32_t x, dt;
+        Row<Tin, N> b;
+    };
+    auto fetch = [&](In &in) {  // the next step's inputs; advances the pointers
+        in.x = load_bits(xp);
+        in.dt = load_bits(dp);
+        row_fetch<Tin, N>(bp, words, in.b);
+        xp += p.x_t;
+        dp += p.dt_t;
+        bp += p.B_t;
+    };
+    auto step = [&](const In &in) {
+        const float xv = decode_bits<Tin>(in.x), delta = softplus(decode_bits<Tin>(in.dt) + bias);
         float bn[N];
-        load_row<Tin, N>(bp, p.bc_words != 0, bn);
+        row_decode<Tin, N>(in.b, bn);
         const float u = delta * xv;
         [[maybe_unused]] const float invd = kZoh ? rcp_hw(delta) : 0.0f;
         sumd += delta;
@@ -139,10 +189,17 @@ __global__ __launch_bounds__(kLanes) void bld_agg_kernel(BldParams p, const Tin 
             if constexpr (kZoh) bb *= phi_zoh(s * kLn2, e, invd * inva[n]);
             h[n] = __builtin_fmaf(e, h[n], bb);
         }
-        xp += p.x_t;
-        dp += p.dt_t;
-        bp += p.B_t;
+    };
+    In i0, i1;
+    int t = t0;
+    if (t < t1) fetch(i0);
+    for (; t + 1 < t1; t += 2) {
+        fetch(i1);
+        step(i0);
+        if (t + 2 < t1) fetch(i0);
+        step(i1);
     }
+    if (t < t1) step(i0);
     if (live) {
         float *r = p.rec + ((size_t(piece) * gridDim.y + b) * p.dim + d) * (N + 1);
 #pragma unroll
@@ -203,12 +260,28 @@ __global__ __launch_bounds__(kLanes) void bld_main_kernel(
     Tout *yp = y + size_t(b) * size_t(p.y_b) + size_t(t0) * size_t(p.y_t) + dc;
     const Tin *bp = Bm + size_t(b) * size_t(p.B_b) + size_t(t0) * size_t(p.B_t);
     const Tin *cp = Cm + size_t(b) * size_t(p.C_b) + size_t(t0) * size_t(p.C_t);
-    for (int t = t0; t < t1; ++t) {
-        const float xv = load_elem(xp), delta = softplus(load_elem(dp) + bias);
-        const float zv = zp ? load_elem(zp) : 0.0f;
+    const bool words = p.bc_words != 0;
+    struct In {
+        uint32_t x, dt, z;
+        Row<Tin, N> b, c;
+    };
+    auto fetch = [&](In &in) {  // the next step's inputs; advances the pointers
+        in.x = load_bits(xp);
+        in.dt = load_bits(dp);
+        in.z = zp ? load_bits(zp) : 0u;
+        row_fetch<Tin, N>(bp, words, in.b);
+        row_fetch<Tin, N>(cp, words, in.c);
+        xp += p.x_t;
+        dp += p.dt_t;
+        if (zp) zp += p.z_t;
+        bp += p.B_t;
+        cp += p.C_t;
+    };
+    auto step = [&](const In &in) {
+        const float xv = decode_bits<Tin>(in.x), delta = softplus(decode_bits<Tin>(in.dt) + bias);
         float bn[N], cn[N];
-        load_row<Tin, N>(bp, p.bc_words != 0, bn);
-        load_row<Tin, N>(cp, p.bc_words != 0, cn);
+        row_decode<Tin, N>(in.b, bn);
+        row_decode<Tin, N>(in.c, cn);
         const float u = delta * xv;
         [[maybe_unused]] const float invd = kZoh ? rcp_hw(delta) : 0.0f;
         float yv = skip * xv;
@@ -221,17 +294,20 @@ __global__ __launch_bounds__(kLanes) void bld_main_kernel(
             h[n] = __builtin_fmaf(e, h[n], bb);
             yv = __builtin_fmaf(cn[n], h[n], yv);
         }
-        if (zp) {
-            yv *= silu(zv);
-            zp += p.z_t;
-        }
+        if (z) yv *= silu(decode_bits<Tin>(in.z));
         if (live) store_elem(yp, yv);
-        xp += p.x_t;
-        dp += p.dt_t;
         yp += p.y_t;
-        bp += p.B_t;
-        cp += p.C_t;
+    };
+    In i0, i1;
+    int t = t0;
+    if (t < t1) fetch(i0);
+    for (; t + 1 < t1; t += 2) {
+        fetch(i1);
+        step(i0);
+        if (t + 2 < t1) fetch(i0);
+        step(i1);
     }
+    if (t < t1) step(i0);
 }
 
 // Pieces: enough waves for the whole GPU (about 4096 at once, i.e. four per
