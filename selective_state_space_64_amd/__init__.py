@@ -519,9 +519,10 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
                  grad_dtype=torch.float32, workspace=None, checkpoints_in_workspace=False,
                  dx=None, ddt=None, dz=None, zoh=False, stream=None):
     """Gradients of sum(dy * y) + sum(dhL * hL) through ssm_scan_fwd (Delta*B
-    form, or the exact zero-order-hold form with zoh=True).  Returns a dict: dx, ddt, dz (None without z) in grad_dtype; dBm,
-    dCm, dA, dDskip, ddt_bias, dh0 in fp32 (dDskip / ddt_bias / dh0 are
-    computed for every call).  checkpoints_in_workspace=True: `workspace`
+    form, or the exact zero-order-hold form with zoh=True).  Returns a dict:
+    dx, ddt, dz (None without z) in grad_dtype; dBm, dCm, dA, dDskip,
+    ddt_bias, dh0 in fp32 (dDskip / ddt_bias / dh0 are computed for every
+    call).  checkpoints_in_workspace=True: `workspace`
     holds the checkpoints a forward call wrote (SSM_FLAG_CHECKPOINTS).
     x, dt, z, dy and the outputs dx, ddt, dz (given here, else allocated
     dense) may be strided views with a contiguous time index and one shared
