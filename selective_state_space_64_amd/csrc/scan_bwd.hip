@@ -99,16 +99,20 @@ __device__ inline bool run_aligned(const T *q)
     return (reinterpret_cast<uintptr_t>(q) & (4 * sizeof(T) - 1)) == 0;
 }
 
-template <typename T>
+// kShared: ordinary cached loads for Bm and Cm, which every channel of the
+// batch row reads at about the same time; streamed tensors load nontemporal.
+template <typename T, bool kShared = false>
 __device__ inline void load4(const T *q, int count, float *out)
 {
     if (count == 4 && run_aligned(q)) {
         if constexpr (sizeof(T) == 4) {
-            const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(q));
+            const f32x4 *p = reinterpret_cast<const f32x4 *>(q);
+            const f32x4 v = kShared ? *p : __builtin_nontemporal_load(p);
             out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
         } else {
             typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(q));
+            const u32x2 *p = reinterpret_cast<const u32x2 *>(q);
+            const u32x2 v = kShared ? *p : __builtin_nontemporal_load(p);
             out[0] = io<bf16_t>::lo(v.x); out[1] = io<bf16_t>::hi(v.x);
             out[2] = io<bf16_t>::lo(v.y); out[3] = io<bf16_t>::hi(v.y);
         }
@@ -148,16 +152,18 @@ struct Run4 {
     uint32_t w[sizeof(T)];
 };
 
-template <typename T>
+template <typename T, bool kShared = false>
 __device__ inline void load4_raw(const T *q, int count, Run4<T> &r)
 {
     if (count == 4 && run_aligned(q)) {
         if constexpr (sizeof(T) == 4) {
-            const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(q));
+            const u32x4 *p = reinterpret_cast<const u32x4 *>(q);
+            const u32x4 v = kShared ? *p : __builtin_nontemporal_load(p);
             r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
         } else {
             typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-            const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(q));
+            const u32x2 *p = reinterpret_cast<const u32x2 *>(q);
+            const u32x2 v = kShared ? *p : __builtin_nontemporal_load(p);
             r.w[0] = v.x; r.w[1] = v.y;
         }
     } else if constexpr (sizeof(T) == 4) {
@@ -275,7 +281,7 @@ __device__ inline void stage_chunk(float4 *dst, const Tin *src, int L, long long
     const int cnt = max(0, min(K, L - l));
     const Tin *q = src + size_t(sn) * size_t(srow) + l;
     float v[K];
-    load4<Tin>(q, cnt, v);
+    load4<Tin, true>(q, cnt, v);
 #pragma unroll
     for (int i = 0; i < Q; ++i)
         dst[(sn * Q + i) * kRowB + sj] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
@@ -503,8 +509,8 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
         if (kPfBC && stager) {
             const int l = ch * T + sj * K;
             const int c2 = max(0, min(K, L - l));
-            load4_raw<Tin>(Bb + size_t(sn) * size_t(p.bc_row) + l, c2, pB);
-            load4_raw<Tin>(Cb + size_t(sn) * size_t(p.bc_row) + l, c2, pC);
+            load4_raw<Tin, true>(Bb + size_t(sn) * size_t(p.bc_row) + l, c2, pB);
+            load4_raw<Tin, true>(Cb + size_t(sn) * size_t(p.bc_row) + l, c2, pC);
         }
         if (ck_thread) pck = ck_row[size_t(ch) * N];
     };

@@ -245,10 +245,10 @@ __global__ __launch_bounds__(kThreads, kMinWavesPerSimd<Tin>) void scan_fwd_kern
         const int l = chunk * T + sj * K;
         const Tin *q = src + size_t(sn) * size_t(p.bc_row) + l;
         if (chunk_full(chunk)) {
-            load_raw<Tin, K>(q, true, K, st);
+            load_raw<Tin, K, true>(q, true, K, st);
         } else {
             const int cnt = max(0, min(K, L - l));
-            load_raw<Tin, K>(q, cnt == K && aligned16(q), cnt, st);
+            load_raw<Tin, K, true>(q, cnt == K && aligned16(q), cnt, st);
         }
     };
     auto stage_store = [&](float4 *dst, const raw_run<Tin, K> &st) {

@@ -93,7 +93,10 @@ template <typename T, int n> struct raw_run {
     uint32_t w[kWords];
 };
 
-template <typename T, int n>
+// Streamed data (read once) takes nontemporal loads; kShared = true takes
+// ordinary cached loads, for data that other workgroups read at about the
+// same time (Bm and Cm, shared by every channel of a batch row).
+template <typename T, int n, bool kShared = false>
 __device__ inline void load_raw(const T *p, bool vec, int count, raw_run<T, n> &r)
 {
     static_assert(n % io<T>::kVec == 0, "a run must be whole 16-byte vectors");
@@ -101,7 +104,7 @@ __device__ inline void load_raw(const T *p, bool vec, int count, raw_run<T, n> &
         const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
 #pragma unroll
         for (int v = 0; v < raw_run<T, n>::kWords / 4; ++v) {
-            u32x4 x = __builtin_nontemporal_load(q + v);
+            u32x4 x = kShared ? q[v] : __builtin_nontemporal_load(q + v);
             r.w[4 * v + 0] = x.x; r.w[4 * v + 1] = x.y;
             r.w[4 * v + 2] = x.z; r.w[4 * v + 3] = x.w;
         }
