@@ -30,6 +30,7 @@
 //      readout, the gate and the output.
 // No MFMA: the recurrence is not a dense contraction.
 #include <algorithm>
+#include <type_traits>
 
 #include "ssm_device.hpp"
 #include "ssm_launch.hpp"
@@ -40,7 +41,7 @@ namespace {
 constexpr int kLanes = 64;  // one wave: 64 consecutive channels
 // Pieces per (batch, channel block): about this many waves in all.
 #ifndef SSM_BLD_TARGET_WAVES
-#define SSM_BLD_TARGET_WAVES 4096
+#define SSM_BLD_TARGET_WAVES 16384
 #endif
 
 struct BldParams {
@@ -84,11 +85,10 @@ __device__ inline void store_elem(Tout *p, float v)
 
 // The Bm (or Cm) row of one step: N values shared by the whole wave, held as
 // raw words (bf16: two states per word, fp32: one).  The address is made
-// visibly wave-uniform (read from the first lane into scalar registers), so
-// that where the compiler can prove the row unchanged by the kernel's own
-// stores it comes through the scalar data cache into SGPRs once per wave
-// (the aggregate pass) instead of as a 64-lane vector load.  bf16 rows are
-// read as 32-bit words only when `words` says every row starts on a 4-byte
+// visibly wave-uniform (read from the first lane into scalar registers), and
+// whole words are read as scalar loads into SGPRs once per wave instead of
+// as 64-lane vector loads.  bf16 rows are read as 32-bit words only in the
+// kWords instantiations, launched when every row starts on a 4-byte
 // boundary (a scalar load ignores the address's two low bits); otherwise
 // two 16-bit loads are packed into each word.
 template <typename Tin, int N>
@@ -98,22 +98,32 @@ struct Row {
     uint32_t w[kWords];
 };
 
-template <typename Tin, int N>
-__device__ inline void row_fetch(const Tin *p, bool words, Row<Tin, N> &r)
+template <typename Tin, int N, bool kWords>
+__device__ inline void row_fetch(const Tin *p, Row<Tin, N> &r)
 {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
     const Tin *__restrict__ q = reinterpret_cast<const Tin *>((uint64_t(hi) << 32) | lo);
+    // Whole 32-bit words are read through the constant address space: Bm and
+    // Cm are never written by these kernels, and there the compiler takes
+    // uniform loads as scalar loads even in a kernel that stores (the main
+    // pass), so that the row and its widening stay in scalar registers
+    // instead of being loaded and decoded in all 64 lanes.
+    typedef const __attribute__((address_space(4))) uint32_t cword;
     if constexpr (Row<Tin, N>::kPacked) {
-        if (words) {
-            const uint32_t *u = reinterpret_cast<const uint32_t *>(q);
+        if constexpr (kWords) {
+            cword *u = (cword *)(reinterpret_cast<const uint32_t *>(q));
 #pragma unroll
             for (int n = 0; n < N / 2; ++n) r.w[n] = u[n];
         } else {
 #pragma unroll
             for (int n = 0; n < N / 2; ++n) r.w[n] = load_bits(q + 2 * n) | (load_bits(q + 2 * n + 1) << 16);
         }
+    } else if constexpr (sizeof(Tin) == 4) {
+        cword *u = (cword *)(reinterpret_cast<const uint32_t *>(q));
+#pragma unroll
+        for (int n = 0; n < N; ++n) r.w[n] = u[n];
     } else {
 #pragma unroll
         for (int n = 0; n < N; ++n) r.w[n] = load_bits(q + n);
@@ -135,7 +145,7 @@ __device__ inline void row_decode(const Row<Tin, N> &r, float *v)
     }
 }
 
-template <typename Tin, int N, bool kZoh>
+template <typename Tin, int N, bool kZoh, bool kWords>
 __global__ __launch_bounds__(kLanes) void bld_agg_kernel(BldParams p, const Tin *__restrict__ x,
                                                          const Tin *__restrict__ dt,
                                                          const Tin *__restrict__ Bm)
@@ -160,7 +170,6 @@ __global__ __launch_bounds__(kLanes) void bld_agg_kernel(BldParams p, const Tin 
     const Tin *xp = x + size_t(b) * size_t(p.x_b) + size_t(t0) * size_t(p.x_t) + dc;
     const Tin *dp = dt + size_t(b) * size_t(p.dt_b) + size_t(t0) * size_t(p.dt_t) + dc;
     const Tin *bp = Bm + size_t(b) * size_t(p.B_b) + size_t(t0) * size_t(p.B_t);
-    const bool words = p.bc_words != 0;
     float sumd = 0.0f;
     struct In {
         uint32_t x, dt;
@@ -169,7 +178,7 @@ __global__ __launch_bounds__(kLanes) void bld_agg_kernel(BldParams p, const Tin 
     auto fetch = [&](In &in) {  // the next step's inputs; advances the pointers
         in.x = load_bits(xp);
         in.dt = load_bits(dp);
-        row_fetch<Tin, N>(bp, words, in.b);
+        row_fetch<Tin, N, kWords>(bp, in.b);
         xp += p.x_t;
         dp += p.dt_t;
         bp += p.B_t;
@@ -230,7 +239,7 @@ __global__ __launch_bounds__(256) void bld_combine_kernel(BldParams p, int batch
     if (p.hL) p.hL[row * N + n] = h;
 }
 
-template <typename Tin, typename Tout, int N, bool kZoh>
+template <typename Tin, typename Tout, int N, bool kZoh, bool kWords>
 __global__ __launch_bounds__(kLanes) void bld_main_kernel(
     BldParams p, const Tin *__restrict__ x, const Tin *__restrict__ dt, const Tin *__restrict__ z,
     const Tin *__restrict__ Bm, const Tin *__restrict__ Cm, Tout *__restrict__ y)
@@ -260,7 +269,6 @@ __global__ __launch_bounds__(kLanes) void bld_main_kernel(
     Tout *yp = y + size_t(b) * size_t(p.y_b) + size_t(t0) * size_t(p.y_t) + dc;
     const Tin *bp = Bm + size_t(b) * size_t(p.B_b) + size_t(t0) * size_t(p.B_t);
     const Tin *cp = Cm + size_t(b) * size_t(p.C_b) + size_t(t0) * size_t(p.C_t);
-    const bool words = p.bc_words != 0;
     struct In {
         uint32_t x, dt, z;
         Row<Tin, N> b, c;
@@ -269,8 +277,8 @@ __global__ __launch_bounds__(kLanes) void bld_main_kernel(
         in.x = load_bits(xp);
         in.dt = load_bits(dp);
         in.z = zp ? load_bits(zp) : 0u;
-        row_fetch<Tin, N>(bp, words, in.b);
-        row_fetch<Tin, N>(cp, words, in.c);
+        row_fetch<Tin, N, kWords>(bp, in.b);
+        row_fetch<Tin, N, kWords>(cp, in.c);
         xp += p.x_t;
         dp += p.dt_t;
         if (zp) zp += p.z_t;
@@ -310,8 +318,9 @@ __global__ __launch_bounds__(kLanes) void bld_main_kernel(
     if (t < t1) step(i0);
 }
 
-// Pieces: enough waves for the whole GPU (about 4096 at once, i.e. four per
-// SIMD), at least 64 steps each.
+// Pieces: about 16384 waves in all (four rounds at four per SIMD: the more
+// waves in flight, the better the per-step loads' latency is hidden, and
+// extra pieces cost only their composition), at least 64 steps each.
 BldSplit bld_split_impl(int batch, int dim, int seqlen)
 {
     const long long waves = (long long)batch * ((dim + kLanes - 1) / kLanes);
@@ -346,16 +355,24 @@ hipError_t launch_typed(const BldArgs &a, hipStream_t stream)
                  grid.y, grid.z, kLanes);
     const Tin *x = static_cast<const Tin *>(a.x), *dt = static_cast<const Tin *>(a.dt);
     const Tin *Bm = static_cast<const Tin *>(a.Bm), *Cm = static_cast<const Tin *>(a.Cm);
-    hipLaunchKernelGGL((bld_agg_kernel<Tin, N, kZoh>), grid, dim3(kLanes), 0, stream, p, x, dt, Bm);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bld_combine_kernel<N>), dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
-                       stream, p, a.batch);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bld_main_kernel<Tin, Tout, N, kZoh>), grid, dim3(kLanes), 0, stream, p, x,
-                       dt, static_cast<const Tin *>(a.z), Bm, Cm, static_cast<Tout *>(a.y));
-    return hipGetLastError();
+    // bf16 rows of two states per word: a separate instantiation for word-aligned rows, so
+    // that the row loads are scalar loads with no per-lane alternative in the loop
+    auto launch = [&](auto words) -> hipError_t {
+        constexpr bool kW = decltype(words)::value;
+        hipLaunchKernelGGL((bld_agg_kernel<Tin, N, kZoh, kW>), grid, dim3(kLanes), 0, stream, p, x, dt,
+                           Bm);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bld_combine_kernel<N>), dim3(unsigned((threads + 255) / 256)), dim3(256), 0,
+                           stream, p, a.batch);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((bld_main_kernel<Tin, Tout, N, kZoh, kW>), grid, dim3(kLanes), 0, stream, p,
+                           x, dt, static_cast<const Tin *>(a.z), Bm, Cm, static_cast<Tout *>(a.y));
+        return hipGetLastError();
+    };
+    if (Row<Tin, N>::kPacked && p.bc_words) return launch(std::true_type{});
+    return launch(std::false_type{});
 }
 
 template <typename Tin, typename Tout, bool kZoh>
