@@ -230,8 +230,30 @@ __global__ __launch_bounds__(256) void bld_combine_kernel(BldParams p, int batch
     const int d = int(row % size_t(p.dim));
     const float a = p.A[size_t(d) * N + n] * kLog2e;
     float h = p.h0 ? p.h0[row * N + n] : 0.0f;
-    for (int k = 0; k < p.npieces; ++k) {
-        float *r = p.rec + (size_t(k) * rows + row) * (N + 1);
+    // Pieces in groups of kG: the group's records are all loaded before the
+    // first is composed, so that the loads' latency is paid once per group
+    // rather than once per piece (each piece's entering state overwrites its
+    // own record's e, already in registers).
+    constexpr int kG = 8;
+    const size_t pstride = rows * (N + 1);
+    float *r0 = p.rec + row * (N + 1);
+    int k = 0;
+    for (; k + kG <= p.npieces; k += kG) {
+        float sd[kG], e[kG];
+#pragma unroll
+        for (int j = 0; j < kG; ++j) {
+            const float *r = r0 + size_t(k + j) * pstride;
+            sd[j] = r[N];
+            e[j] = r[n];
+        }
+#pragma unroll
+        for (int j = 0; j < kG; ++j) {
+            r0[size_t(k + j) * pstride + n] = h;
+            h = __builtin_fmaf(exp2_hw(a * sd[j]), h, e[j]);
+        }
+    }
+    for (; k < p.npieces; ++k) {
+        float *r = r0 + size_t(k) * pstride;
         const float sd = r[N], e = r[n];
         r[n] = h;
         h = __builtin_fmaf(exp2_hw(a * sd), h, e);
