@@ -6,10 +6,11 @@
 // "Mamba: Linear-Time Sequence Modeling with Selective State Spaces": the
 // backward pass recomputes the intermediate states).  Per (b, d) the adjoint
 //     lambda_t = ds_t C_t + A-bar_{t+1} lambda_{t+1},   ds_t = dy_t silu(z_t)
-// runs backwards in time; with hp_t = A-bar_t h_{t-1}, formed as the product
-// of A-bar_t with the previous state (kept from the forward replay), not as
-// the difference h_t - Delta_t B_t x_t, which cancels for channels that reset
-// (A-bar ~ 0: h_t is then almost all input term),
+// runs backwards in time; with hp_t = A-bar_t h_{t-1}, whose products with
+// lambda_t are formed as (lambda_t A-bar_t) h_{t-1} from the previous state
+// (kept from the forward replay) and the adjoint carried to step t-1, not
+// through the difference h_t - Delta_t B_t x_t, which cancels for channels
+// that reset (A-bar ~ 0: h_t is then almost all input term),
 //     dx_t      = Dskip ds_t + sum_n lambda_t Delta_t B_t
 //     dDelta_t  = sum_n lambda_t (A hp_t + B_t x_t),   ddt_t = dDelta_t sigmoid(u_t)
 //     dA[d,n]  += lambda_t Delta_t hp_t                 dBm[b,n,t] += lambda_t Delta_t x_t
@@ -529,7 +530,8 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
             stage_chunk<Tin, K>(sC, Cb, L, p.bc_row, ch, sn, sj);
         }
         if (ck_thread) sH[ck_c * NP + ck_n] = pck;
-        // per step: sb = sum_n lambda B, sah = sum_n lambda A A-bar h_{t-1}
+        // per step: sb = sum_n lambda B, sah = sum_n lambda A' A-bar h_{t-1}
+        // with A' = A log2(e) (times ln 2 once per step below)
         float xv[K], delta[K], w[K], ds[K], sacc[K], sb[K], sah[K], sgu[K], gzf[K];
         [[maybe_unused]] float invd[K], sba[K];  // exact ZOH: 1/Delta, sum_n lambda A-bar B
         float dv[K], gy[K], zv[K];
@@ -583,7 +585,8 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 #pragma unroll 1
         for (int n = 0; n < N; n += G) {
             const int pb = (n / G) & 1;  // sP buffer of this pair
-            float a1[G], An[G], bv[G][K], cv[G][K], da[G][K], hh[G][K], ptot[G], hl[G];
+            float a1[G], bv[G][K], cv[G][K], da[G][K], hh[G][K], ptot[G], hl[G];
+            [[maybe_unused]] float An[G];  // A (natural units), exact ZOH only
             // bg: B times the input factor's Delta-free part (phi(Delta A) for
             // the exact ZOH form, 1 otherwise), so B-bar x = w bg, w = Delta x
             [[maybe_unused]] float ph[G][K], inva[G];
@@ -591,7 +594,7 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 #pragma unroll
             for (int g = 0; g < G; ++g) {
                 a1[g] = ap[n + g];
-                An[g] = a1[g] * kLn2;
+                if constexpr (kZoh) An[g] = a1[g] * kLn2;
                 lds_run<K>(bp + (n + g) * Q * kRowB, bv[g]);
                 lds_run<K>(cp + (n + g) * Q * kRowB, cv[g]);
 #pragma unroll
@@ -624,9 +627,9 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
             } else {
                 row_scan(aa[0], hl[0], hend[0], h[0]);
             }
-            // hin: the state entering the lane's first step (A-bar h_{t-1} is
-            // formed below as a product, not as h_t - B-bar x, which cancels
-            // when A-bar ~ 0)
+            // hin: the state entering the lane's first step (lambda A-bar h_{t-1}
+            // is formed below as a product with it, not from h_t - B-bar x,
+            // which cancels when A-bar ~ 0)
             float hin[G];
 #pragma unroll
             for (int g = 0; g < G; ++g) {
@@ -671,16 +674,11 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
 #pragma unroll
                 for (int i = K - 1; i >= 0; --i) {
                     lam = __builtin_fmaf(ds[i], cv[g][i], lam);
-                    const float hpa = da[g][i] * (i > 0 ? hh[g][i - 1] : hin[g]);  // A-bar h_{t-1}
-                    const float lh = lam * hpa;
-                    sah[i] = __builtin_fmaf(An[g], lh, sah[i]);
-                    dap[g] = __builtin_fmaf(delta[i], lh, dap[g]);
                     sb[i] = __builtin_fmaf(lam, bg[g][i], sb[i]);
                     if constexpr (kZoh) {
                         // dg/dDelta = A-bar (the Delta gradient), dg/dA = Delta^2 psi
                         const float ps =
                             psi_zoh(delta[i] * An[g], da[g][i], invd[i] * inva[g]);
-                        sba[i] = __builtin_fmaf(lam * da[g][i], bv[g][i], sba[i]);
                         dap[g] = __builtin_fmaf(lam * bv[g][i] * xv[i], delta[i] * delta[i] * ps,
                                                 dap[g]);
                         gbv[i] = lam * w[i] * ph[g][i];
@@ -688,7 +686,14 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
                         gbv[i] = lam * w[i];
                     }
                     gcv[i] = ds[i] * hh[g][i];
+                    // lambda_t A-bar_t: the adjoint carried to the step before,
+                    // and, times h_{t-1}, the A-bar h_{t-1} term of dA and dDelta
+                    // (one product per step instead of forming A-bar h_{t-1} first)
                     lam *= da[g][i];
+                    if constexpr (kZoh) sba[i] = __builtin_fmaf(lam, bv[g][i], sba[i]);
+                    const float lh = lam * (i > 0 ? hh[g][i - 1] : hin[g]);
+                    sah[i] = __builtin_fmaf(a1[g], lh, sah[i]);
+                    dap[g] = __builtin_fmaf(delta[i], lh, dap[g]);
                 }
                 sP[pb][g][0][c][j] = make_float4(gbv[0], gbv[1], gbv[2], gbv[3]);
                 sP[pb][g][1][c][j] = make_float4(gcv[0], gcv[1], gcv[2], gcv[3]);
@@ -734,9 +739,9 @@ __global__ __launch_bounds__(kThreadsB, 3) void scan_bwd_kernel(BwdParams p)
             for (int i = 0; i < K; ++i) {
                 gx[i] = __builtin_fmaf(delta[i], sb[i], skip * ds[i]);
                 if constexpr (kZoh) {
-                    gdt[i] = __builtin_fmaf(xv[i], sba[i], sah[i]) * sgu[i];
+                    gdt[i] = __builtin_fmaf(xv[i], sba[i], sah[i] * kLn2) * sgu[i];
                 } else {
-                    gdt[i] = __builtin_fmaf(xv[i], sb[i], sah[i]) * sgu[i];
+                    gdt[i] = __builtin_fmaf(xv[i], sb[i], sah[i] * kLn2) * sgu[i];
                 }
                 dbias_acc += i < cnt ? gdt[i] : 0.0f;
                 gz[i] = gzf[i] * sacc[i];
