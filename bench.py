@@ -499,6 +499,23 @@ def bench_decode(torch, ssm, synth, steps_cap=256, layers=16):
         flusher()
 
     rot_ms = replay(g_rot, reset_rot)
+
+    # measured ceiling for a pass over the same rotating states: one torch
+    # in-place add per token on the layer's state (read + write of the state,
+    # no inputs), captured and replayed the same way
+    g_add = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        states[0].add_(1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g_add):
+        for s in range(steps):
+            states[s % layers].add_(1.0)
+    add_ms = replay(g_add, reset_rot)
+    add_bytes = 2 * wl.batch * wl.dim * wl.dstate * 4
+    del g_add
     per_call_bytes = (2 * wl.batch * wl.dim * wl.dstate * 4 + 3 * wl.batch * wl.dim * 2
                       + 2 * wl.batch * wl.dstate * 2 + wl.dim * wl.dstate * 4 + 2 * wl.dim * 4
                       + wl.batch * wl.dim * 4)
@@ -519,7 +536,13 @@ def bench_decode(torch, ssm, synth, steps_cap=256, layers=16):
                          "timing": "per step of a graph replay, state rotating over %d "
                                    "buffers (launch gaps included)" % layers,
                          "cached_state": {"achieved": gbps(graph_ms),
-                                          "frac": gbps(graph_ms) * 1e9 / PEAK_HBM}},
+                                          "frac": gbps(graph_ms) * 1e9 / PEAK_HBM},
+                         "measured_ceiling": {
+                             "what": "torch in-place add over the same 16 rotating states, "
+                                     "one per token in a graph replay",
+                             "us_per_step": add_ms * 1e3,
+                             "achieved": add_bytes / (add_ms * 1e-3) / 1e9,
+                             "decode_frac_of_ceiling": gbps(rot_ms) / (add_bytes / (add_ms * 1e-3) / 1e9)}},
             "note": "one launch per token, state fp32 in place; eager: StateUpdateSteps loop"}
 
 

@@ -22,7 +22,11 @@
 // states and one row per lane, and 9.8 us for four states and two rows;
 // eight rows per lane (155 VGPRs) took 11.1 us.  The per-(b, d) scalars
 // (Delta, x, z) are computed by each of the R lanes.  A, Bm and Cm come from
-// cache.
+// cache.  The state is read with nontemporal loads and written with ordinary
+// stores: with 16 layers' states rotating past the 256 MB MALL (a multi-layer
+// decode) a step took 10.45 us against 11.5 us with ordinary loads, and the
+// same with one state that stays in the MALL (8.9 us); nontemporal stores as
+// well cost 10.6 us with the resident state, and alone 12.1 us rotating.
 #include "ssm_device.hpp"
 #include "ssm_launch.hpp"
 
@@ -46,14 +50,15 @@ struct UpdateParams {
     long long x_b, dt_b, z_b, y_b, B_b, C_b;
 };
 
-template <int N>
+// kStream: nontemporal loads (the state, read once per token)
+template <int N, bool kStream = false>
 __device__ inline void load_f32(const float *p, float *v)
 {
     if constexpr (N % 4 == 0) {
         const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
 #pragma unroll
         for (int i = 0; i < N / 4; ++i) {
-            const f32x4 w = q[i];
+            const f32x4 w = kStream ? __builtin_nontemporal_load(q + i) : q[i];
             v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
         }
     } else {
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void state_update_kernel(UpdateParams p)
         live[k] = dk < p.dim;
         const int d = live[k] ? dk : p.dim - 1;  // dead lanes still join the DPP sum
         dd[k] = d;
-        load_f32<S>(p.state + (size_t(b) * p.dim + d) * N + n0, h[k]);
+        load_f32<S, true>(p.state + (size_t(b) * p.dim + d) * N + n0, h[k]);
         const float *Ap = p.A + size_t(d) * N + n0;
         if (a_vec) {
             load_f32<S>(Ap, a[k]);
