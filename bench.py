@@ -566,6 +566,17 @@ def bench_conv(torch, ssm, synth, wl, x, launches=20):
                         "unit": "GB/s", "frac": achieved / PEAK_HBM, "traffic": None,
                         "algorithmic_bytes": nbytes,
                         "model": "x read once (2 B) + y written once (2 B) per output, plus taps"}}
+    # the same conv on (batch, L, dim)-ordered tensors (ssm_conv1d_fwd_bld)
+    xt = x.transpose(1, 2).contiguous()
+    yt = torch.empty_like(xt)
+    fb = lambda: ssm.ssm_conv1d_fwd_bld(xt, wt, bias=bt, y=yt, return_final_state=False)
+    for _ in range(3):
+        fb()
+    ms_b, _ = time_launches(torch, fb, launches, stream)
+    out["bld_layout"] = {"kernel_ms_mean": ms_b, "achieved": nbytes / (ms_b * 1e-3) / 1e9,
+                         "frac": nbytes / (ms_b * 1e-3) / PEAK_HBM,
+                         "note": "x, y as [batch, L, dim]; same algorithmic bytes"}
+    del xt, yt
     dwl = synth.WORKLOADS[4]
     state = torch.zeros((dwl.batch, dwl.dim, 3), device="cuda")
     xs = torch.randn((64, dwl.batch, dwl.dim), device="cuda").to(torch.bfloat16)

@@ -85,6 +85,40 @@ ssm_status_t ssm_conv1d_fwd_strided(int batch, int dim, int seqlen, int width,
                                     const ssm_conv_layout_t *layout, void *stream);
 
 /*
+ * The conv on (batch, L, dim)-ordered x and y: a time step's channels
+ * contiguous, time steps apart.  It is the order of the (B, L, D) tensors in
+ * the reading guide's "Hardware-aware state expansion" section and the order
+ * in which the input projection produces the block's x, so the conv can read
+ * x as one half of a [batch][L][2 dim] projection output and feed
+ * ssm_scan_fwd_bld without a transpose.
+ *   x   element (b, t, d) at b * x_batch + t * x_step + d   (in_dtype)
+ *   y   element (b, t, d) at b * y_batch + t * y_step + d   (out_dtype)
+ *   x_step, y_step    distance between time steps; >= dim; 0 means dim
+ *   x_batch, y_batch  distance between batch entries; >= seqlen * step;
+ *                     0 means seqlen * step
+ * Strides are in ELEMENTS of the tensor's own type.  A negative stride, one
+ * below its minimum, a step stride above 2^40 or a tensor spanning 2^56
+ * elements or more is SSM_ERR_BAD_SHAPE.
+ */
+typedef struct {
+    long long x_step, x_batch;
+    long long y_step, y_batch;
+} ssm_conv_bld_layout_t;
+
+/* ssm_conv1d_fwd on (batch, L, dim)-ordered x and y laid out by `layout`
+ * (host pointer, read during the call only; NULL means dense): the same
+ * arguments, results (bit for bit) and errors, with weight, bias and the conv
+ * states dense as in ssm_conv1d_fwd ([batch][dim][width-1]); stateL may be
+ * exactly state0.  Overlap is checked on address ranges from the first to
+ * the last element.  Supported sizes: batch, dim, seqlen >= 1, dim <= 2^30,
+ * batch * dim * seqlen < 2^62. */
+ssm_status_t ssm_conv1d_fwd_bld(int batch, int dim, int seqlen, int width, ssm_dtype_t in_dtype,
+                                unsigned flags, const void *x, const float *weight,
+                                const float *bias, const float *state0, ssm_dtype_t out_dtype,
+                                void *y, float *stateL, const ssm_conv_bld_layout_t *layout,
+                                void *stream);
+
+/*
  * One decode step: the same operation at seqlen = 1 on a persistent state.
  *   state    [batch][dim][width-1] fp32, read and overwritten in place with
  *            the window shifted by one (the new input last)

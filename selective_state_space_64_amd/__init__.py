@@ -39,7 +39,7 @@ EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes
            "ssm_scan_fwd", "ssm_scan_fwd_strided", "ssm_scan_fwd_noalloc",
            "ssm_scan_fwd_bld_workspace_bytes", "ssm_scan_fwd_bld",
            "ssm_state_update", "ssm_state_update_strided",
-           "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided", "ssm_conv1d_update",
+           "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided", "ssm_conv1d_fwd_bld", "ssm_conv1d_update",
            "ssm_conv1d_update_strided",
            "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_strided"]
 
@@ -67,6 +67,11 @@ class ConvLayout(ctypes.Structure):
     """ssm_conv_layout_t: strides in elements, 0 = dense default."""
     _fields_ = [("x_row", ctypes.c_longlong), ("x_batch", ctypes.c_longlong),
                 ("y_row", ctypes.c_longlong), ("y_batch", ctypes.c_longlong)]
+
+
+class ConvBldLayout(ctypes.Structure):
+    """ssm_conv_bld_layout_t: step and batch strides in elements, 0 = dense default."""
+    _fields_ = [(n, ctypes.c_longlong) for n in ("x_step", "x_batch", "y_step", "y_batch")]
 
 
 class UpdateLayout(ctypes.Structure):
@@ -133,6 +138,9 @@ def lib():
         L.ssm_conv1d_fwd_strided.restype = i
         L.ssm_conv1d_fwd_strided.argtypes = ([i, i, i, i, i, u] + [vp] * 4 +
                                              [i, vp, vp, ctypes.POINTER(ConvLayout), vp])
+        L.ssm_conv1d_fwd_bld.restype = i
+        L.ssm_conv1d_fwd_bld.argtypes = ([i, i, i, i, i, u] + [vp] * 4 +
+                                         [i, vp, vp, ctypes.POINTER(ConvBldLayout), vp])
         L.ssm_conv1d_update.restype = i
         L.ssm_conv1d_update.argtypes = [i, i, i, i, u] + [vp] * 4 + [i, vp, vp]
         _lib = L
@@ -613,6 +621,37 @@ def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=No
 
 
 @_on_caller_stream
+def ssm_conv1d_fwd_bld(x, weight, *, bias=None, state0=None, silu=True, out_dtype=None,
+                       return_final_state=True, y=None, stateL=None, stream=None):
+    """The causal depthwise conv on [batch, L, dim] tensors (channels
+    contiguous; x may be the first half of a [batch, L, 2 dim] projection
+    output); returns (y [batch, L, dim], stateL [batch, dim, W-1]).  The conv
+    states are [batch, dim, W-1] as in ssm_conv1d_fwd."""
+    _no_broadcast_args(x=x, weight=weight, bias=bias, state0=state0, y=y, stateL=stateL)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, L, dim]")
+    batch, L, dim = x.shape
+    W = weight.shape[-1]
+    out_dtype = out_dtype or x.dtype
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=out_dtype, device=x.device)
+    if stateL is None and return_final_state:
+        stateL = torch.empty((batch, dim, W - 1), dtype=torch.float32, device=x.device)
+    f32 = torch.float32
+    (xp,), (x_t,), (x_b,) = _steps((x,), ("x",), (batch, L, dim), x.dtype)
+    (yp,), (y_t,), (y_b,) = _steps((y,), ("y",), (batch, L, dim), out_dtype)
+    layout = ConvBldLayout(x_t, x_b, y_t, y_b)
+    args = [xp, _ptr(weight, "weight", (dim, W), f32),
+            _ptr(bias, "bias", (dim,), f32), _ptr(state0, "state0", (batch, dim, W - 1), f32)]
+    sp = _ptr(stateL, "stateL", (batch, dim, W - 1), f32)
+    st = lib().ssm_conv1d_fwd_bld(batch, dim, L, W, _dtype_code(x.dtype),
+                                  SSM_CONV_SILU if silu else 0, *args, _dtype_code(y.dtype), yp,
+                                  sp, ctypes.byref(layout), _stream(stream, x.device))
+    _check(st)
+    return y, stateL
+
+
+@_on_caller_stream
 def ssm_conv1d_update(state, x, weight, *, bias=None, silu=True, out_dtype=None, y=None,
                       stream=None):
     """One decode step of the conv; shifts `state` [batch, dim, W-1] in place
@@ -639,4 +678,5 @@ scan_fwd = ssm_scan_fwd
 scan_bwd = ssm_scan_bwd
 state_update = ssm_state_update
 conv1d_fwd = ssm_conv1d_fwd
+conv1d_fwd_bld = ssm_conv1d_fwd_bld
 conv1d_update = ssm_conv1d_update

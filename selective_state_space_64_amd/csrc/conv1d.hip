@@ -318,6 +318,215 @@ hipError_t update_width(const ConvUpdateArgs &a, hipStream_t s)
     return hipErrorInvalidValue;
 }
 
+
+// ---------------------------------------------------------------- (batch, L, dim) order
+// The same convolution on x and y whose channels are contiguous and whose time
+// steps are `*_t` elements apart (the order a model's input projection
+// produces).  A lane owns V consecutive channels (V = 4 when every access of
+// the call can be one 4-element vector, else 1) and walks a piece of
+// consecutive steps, keeping the W-1 previous inputs of its channels in
+// registers; a wave reads and writes 64 V consecutive channels of one step per
+// access.  Pieces are walked by separate workgroups: each re-reads the W-1
+// inputs before its first step (the first piece takes them from the conv
+// state).  The first piece's lanes also write the final conv state, after
+// reading the initial one, so the two may be the same buffer.
+struct ConvBldParams {
+    int dim, seqlen, piece, cblocks;
+    long long x_t, x_b, y_t, y_b;
+    const void *x;
+    const float *weight, *bias, *state0;
+    void *y;
+    float *stateL;
+};
+
+template <typename T, int V>
+__device__ inline void bld_load(const T *p, float *v)
+{
+    if constexpr (V == 1) {
+        v[0] = io<T>::load1(p);
+    } else if constexpr (sizeof(T) == 4) {
+        const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
+    } else {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+        v[0] = io<bf16_t>::lo(w.x); v[1] = io<bf16_t>::hi(w.x);
+        v[2] = io<bf16_t>::lo(w.y); v[3] = io<bf16_t>::hi(w.y);
+    }
+}
+
+template <typename T, int V>
+__device__ inline void bld_store(T *p, const float *v)
+{
+    if constexpr (sizeof(T) == 4) {
+        if constexpr (V == 1) {
+            *reinterpret_cast<float *>(p) = v[0];
+        } else {
+            *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+    } else {
+        if constexpr (V == 1) {
+            reinterpret_cast<bf16_t *>(p)->bits = uint16_t(pack_bf16x2(v[0], 0.0f) & 0xffffu);
+        } else {
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2 *>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+    }
+}
+
+template <typename Tin, typename Tout, int W, int V>
+__global__ void __launch_bounds__(kConvThreads)
+conv1d_bld_kernel(ConvBldParams p, bool act)
+{
+    constexpr int H = W - 1;
+    constexpr int U = 8;  // steps whose loads are issued before the first is used
+    const int cb = int(blockIdx.x % unsigned(p.cblocks));
+    const int b = int(blockIdx.x / unsigned(p.cblocks));
+    const int d0 = (cb * kConvThreads + int(threadIdx.x)) * V;  // first channel of the lane
+    if (d0 >= p.dim) return;  // dim is a multiple of V: the lane's channels are all live
+    const int t0 = int(blockIdx.y) * p.piece;
+    const int t1 = min(p.seqlen, t0 + p.piece);
+    const Tin *xb = static_cast<const Tin *>(p.x) + size_t(b) * size_t(p.x_b) + d0;
+    Tout *yb = static_cast<Tout *>(p.y) + size_t(b) * size_t(p.y_b) + d0;
+    const size_t row = size_t(b) * size_t(p.dim) + size_t(d0);  // conv-state row of channel d0
+
+    float w[W][V], bias[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+#pragma unroll
+        for (int k = 0; k < W; ++k) w[k][v] = p.weight[size_t(d0 + v) * W + k];
+        bias[v] = p.bias ? p.bias[d0 + v] : 0.0f;
+    }
+    // h[k]: the input at step t - H + k before the step t being computed
+    float h[H > 0 ? H : 1][V];
+    if (t0 == 0) {
+#pragma unroll
+        for (int k = 0; k < H; ++k)
+#pragma unroll
+            for (int v = 0; v < V; ++v) h[k][v] = p.state0 ? p.state0[(row + v) * H + k] : 0.0f;
+        if (p.stateL) {
+            // final state: the last H entries of (state0, x)
+            float fin[H > 0 ? H : 1][V];
+#pragma unroll
+            for (int k = 0; k < H; ++k) {
+                const int idx = p.seqlen - H + k;  // < 0: inside state0
+                if (idx >= 0) {
+                    bld_load<Tin, V>(xb + size_t(idx) * size_t(p.x_t), fin[k]);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) fin[k][v] = h[idx + H][v];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < H; ++k)
+#pragma unroll
+                for (int v = 0; v < V; ++v) p.stateL[(row + v) * H + k] = fin[k][v];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < H; ++k) bld_load<Tin, V>(xb + size_t(t0 - H + k) * size_t(p.x_t), h[k]);
+    }
+
+    const Tin *xp = xb + size_t(t0) * size_t(p.x_t);
+    Tout *yp = yb + size_t(t0) * size_t(p.y_t);
+    for (int t = t0; t < t1; t += U) {
+        float xv[U][V];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (t + u < t1) {
+                bld_load<Tin, V>(xp + size_t(u) * size_t(p.x_t), xv[u]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) xv[u][v] = 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (t + u >= t1) break;
+            float out[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                // the [batch][dim][L] kernel's order: bias, then the oldest input first
+                float s = bias[v];
+#pragma unroll
+                for (int k = 0; k < H; ++k) s = __builtin_fmaf(w[k][v], h[k][v], s);
+                s = __builtin_fmaf(w[H][v], xv[u][v], s);
+                out[v] = act ? silu(s) : s;
+            }
+            bld_store<Tout, V>(yp + size_t(u) * size_t(p.y_t), out);
+#pragma unroll
+            for (int k = 0; k + 1 < H; ++k)
+#pragma unroll
+                for (int v = 0; v < V; ++v) h[k][v] = h[k + 1][v];
+#pragma unroll
+            for (int v = 0; v < V; ++v) h[H - 1][v] = xv[u][v];
+        }
+        xp += size_t(U) * size_t(p.x_t);
+        yp += size_t(U) * size_t(p.y_t);
+    }
+}
+
+template <typename Tin, typename Tout, int W>
+hipError_t launch_bld_typed(const ConvBldArgs &a, hipStream_t stream)
+{
+    // 4-channel vectors when every lane's every access starts on a multiple
+    // of 4 elements of an aligned base
+    auto vec4 = [](const void *base, size_t esize, long long st, long long bs) {
+        return (reinterpret_cast<uintptr_t>(base) % (4 * esize)) == 0 && st % 4 == 0 && bs % 4 == 0;
+    };
+    const bool v4 = a.dim % 4 == 0 && vec4(a.x, sizeof(Tin), a.x_t, a.x_b) &&
+                    vec4(a.y, sizeof(Tout), a.y_t, a.y_b);
+    const int V = v4 ? 4 : 1;
+    ConvBldParams p;
+    p.dim = a.dim;
+    p.seqlen = a.seqlen;
+    p.cblocks = int((a.dim + kConvThreads * V - 1) / (kConvThreads * V));
+    p.x_t = a.x_t;
+    p.x_b = a.x_b;
+    p.y_t = a.y_t;
+    p.y_b = a.y_b;
+    p.x = a.x;
+    p.weight = a.weight;
+    p.bias = a.bias;
+    p.state0 = a.state0;
+    p.y = a.y;
+    p.stateL = a.stateL;
+    // Pieces of 64 steps, halved (to 16 at least) while the launch has fewer
+    // than ~4 waves per SIMD; at most 65535 pieces.
+    const long long waves_per_piece = (long long)a.batch * p.cblocks * (kConvThreads / 64);
+    long long piece = 64;
+    while (piece > 16 && waves_per_piece * ((a.seqlen + piece - 1) / piece) < 4096) piece /= 2;
+    if ((a.seqlen + piece - 1) / piece > 65535) piece = (a.seqlen + 65534) / 65535;
+    p.piece = int(piece);
+    const long long npieces = (a.seqlen + piece - 1) / piece;
+    const long long gx = (long long)a.batch * p.cblocks;
+    if (gx > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (log_enabled())
+        log_line("conv1d_fwd_bld: conv1d_bld_kernel<in %s, out %s, W %d, channels per lane %d>, "
+                 "grid (%lld, %lld) x %d threads, pieces of %lld steps",
+                 type_tag<Tin>(), type_tag<Tout>(), W, V, gx, npieces, kConvThreads, piece);
+    const dim3 grid{unsigned(gx), unsigned(npieces), 1u};
+    if (v4) {
+        hipLaunchKernelGGL((conv1d_bld_kernel<Tin, Tout, W, 4>), grid, dim3(kConvThreads), 0,
+                           stream, p, a.silu != 0);
+    } else {
+        hipLaunchKernelGGL((conv1d_bld_kernel<Tin, Tout, W, 1>), grid, dim3(kConvThreads), 0,
+                           stream, p, a.silu != 0);
+    }
+    return hipGetLastError();
+}
+
+template <typename Tin, typename Tout>
+hipError_t bld_width(const ConvBldArgs &a, hipStream_t s)
+{
+    switch (a.width) {
+    case 2: return launch_bld_typed<Tin, Tout, 2>(a, s);
+    case 3: return launch_bld_typed<Tin, Tout, 3>(a, s);
+    case 4: return launch_bld_typed<Tin, Tout, 4>(a, s);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream)
@@ -335,6 +544,14 @@ hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t stream)
                           : update_width<bf16_t, float>(a, stream);
     }
     return a.out_bf16 ? update_width<float, bf16_t>(a, stream) : update_width<float, float>(a, stream);
+}
+
+hipError_t launch_conv1d_bld(const ConvBldArgs &a, hipStream_t stream)
+{
+    if (a.in_bf16) {
+        return a.out_bf16 ? bld_width<bf16_t, bf16_t>(a, stream) : bld_width<bf16_t, float>(a, stream);
+    }
+    return a.out_bf16 ? bld_width<float, bf16_t>(a, stream) : bld_width<float, float>(a, stream);
 }
 
 }  // namespace ssm

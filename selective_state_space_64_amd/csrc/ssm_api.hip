@@ -592,6 +592,58 @@ ssm_status_t ssm_conv1d_fwd_strided(int batch, int dim, int seqlen, int width,
                                        layout, stream);
 }
 
+ssm_status_t ssm_conv1d_fwd_bld(int batch, int dim, int seqlen, int width, ssm_dtype_t in_dtype_e,
+                                unsigned flags, const void *x, const float *weight,
+                                const float *bias, const float *state0, ssm_dtype_t out_dtype_e,
+                                void *y, float *stateL, const ssm_conv_bld_layout_t *layout,
+                                void *stream)
+{
+    const int in_dtype = enum_bits(in_dtype_e), out_dtype = enum_bits(out_dtype_e);
+    if (!x || !weight || !y) return SSM_ERR_NULL_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1 || seqlen < 1 || dim > ssm::kMaxDim) return SSM_ERR_BAD_SHAPE;
+    if (width < 2 || width > 4 || (flags & ~SSM_CONV_SILU) != 0) return SSM_ERR_UNSUPPORTED;
+    const size_t st_elems = mul3(batch, dim, width - 1);
+    if (!mul3(batch, dim, seqlen) || !st_elems) return SSM_ERR_BAD_SHAPE;
+    const ssm_conv_bld_layout_t dense{};
+    const ssm_conv_bld_layout_t &lay = layout ? *layout : dense;
+    long long x_t, x_b, y_t, y_b;
+    size_t x_span, y_span;
+    if (!bld_span(lay.x_step, lay.x_batch, batch, seqlen, dim, x_t, x_b, x_span) ||
+        !bld_span(lay.y_step, lay.y_batch, batch, seqlen, dim, y_t, y_b, y_span))
+        return SSM_ERR_BAD_SHAPE;
+
+    const size_t in = dsize(in_dtype);
+    if (misaligned(x, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)weight, (const void *)bias, (const void *)state0,
+                          (const void *)stateL})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (misaligned(y, dsize(out_dtype))) return SSM_ERR_MISALIGNED;
+
+    const size_t ybytes = y_span * dsize(out_dtype);
+    const size_t sbytes = st_elems * sizeof(float);
+    struct In {
+        const void *p;
+        size_t bytes;
+    } inputs[] = {{x, x_span * in},
+                  {weight, size_t(dim) * width * sizeof(float)},
+                  {bias, dim * sizeof(float)},
+                  {state0, sbytes}};
+    for (const In &i : inputs) {
+        if (overlaps(y, ybytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        // stateL may be exactly state0 (read before written per row), nothing else
+        if (stateL && !(i.p == state0 && stateL == state0) && overlaps(stateL, sbytes, i.p, i.bytes))
+            return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, ybytes, stateL, sbytes)) return SSM_ERR_ALIAS;
+
+    ssm::ConvBldArgs a{batch, dim, seqlen, width, in_dtype == SSM_BF16, out_dtype == SSM_BF16,
+                       (flags & SSM_CONV_SILU) != 0, x, weight, bias, state0, y, stateL,
+                       x_t, x_b, y_t, y_b};
+    const hipError_t e = ssm::launch_conv1d_bld(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 ssm_status_t ssm_conv1d_update(int batch, int dim, int width, ssm_dtype_t in_dtype,
                                unsigned flags, float *state, const void *x, const float *weight,
                                const float *bias, ssm_dtype_t out_dtype, void *y, void *stream)

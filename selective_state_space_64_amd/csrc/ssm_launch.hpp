@@ -64,6 +64,18 @@ struct ConvArgs {
     long long x_row, x_b, y_row, y_b;
 };
 
+// The conv on (batch, L, dim)-ordered x and y: element (b, t, d) at
+// b * *_b + t * *_t + d (element strides).
+struct ConvBldArgs {
+    int batch, dim, seqlen, width;
+    int in_bf16, out_bf16, silu;
+    const void *x;
+    const float *weight, *bias, *state0;
+    void *y;
+    float *stateL;
+    long long x_t, x_b, y_t, y_b;
+};
+
 struct ConvUpdateArgs {
     int batch, dim, width;
     int in_bf16, out_bf16, silu;
@@ -146,6 +158,7 @@ size_t scan_bwd_workspace_bytes(int batch, int dim, int seqlen, int dstate);
 hipError_t launch_scan_fwd(const ScanArgs &a, hipStream_t stream);
 hipError_t launch_state_update(const UpdateArgs &a, hipStream_t stream);
 hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream);
+hipError_t launch_conv1d_bld(const ConvBldArgs &a, hipStream_t stream);
 hipError_t launch_conv1d_update(const ConvUpdateArgs &a, hipStream_t stream);
 hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream);
 

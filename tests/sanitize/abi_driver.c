@@ -108,6 +108,13 @@ int main(void)
     cl.y_row = 0;
     cl.x_batch = 1ll << 62;
     REFUSED(ssm_conv1d_fwd_strided(4, 5120, 2048, 4, bf, 0, x, w, bias, s0, bf, y, hL, &cl, 0));
+    ssm_conv_bld_layout_t cb = {0};
+    cb.x_step = 5119;
+    REFUSED(ssm_conv1d_fwd_bld(4, 5120, 2048, 4, bf, 0, x, w, bias, s0, bf, y, hL, &cb, 0));
+    cb.x_step = 0;
+    cb.y_batch = 1ll << 62;
+    REFUSED(ssm_conv1d_fwd_bld(4, 5120, 2048, 4, bf, 0, x, w, bias, s0, bf, y, hL, &cb, 0));
+    REFUSED(ssm_conv1d_fwd_bld(4, 5120, 2048, 4, bf, 0, x, w, bias, s0, bf, x, hL, 0, 0));
     REFUSED(ssm_conv1d_update(64, 5120, 1, bf, 0, s0, x, w, bias, bf, y, 0));
     REFUSED(ssm_conv1d_update_strided(64, 5120, 4, bf, 0, s0, x, w, bias, bf, y, -1, 0, 0));
     REFUSED(ssm_conv1d_update_strided(64, 5120, 4, bf, 0, s0, x, w, bias, bf, y, 0, 1ll << 62, 0));

@@ -63,6 +63,8 @@ def test_binding_argtypes_match_prototypes():
                 assert at == ctypes.POINTER(ssm.BwdLayout), (name, decl, at)
             elif "ssm_conv_layout_t" in decl:
                 assert at == ctypes.POINTER(ssm.ConvLayout), (name, decl, at)
+            elif "ssm_conv_bld_layout_t" in decl:
+                assert at == ctypes.POINTER(ssm.ConvBldLayout), (name, decl, at)
             elif "ssm_update_layout_t" in decl:
                 assert at == ctypes.POINTER(ssm.UpdateLayout), (name, decl, at)
             elif "ssm_bld_layout_t" in decl:
@@ -577,6 +579,40 @@ def test_conv_strided_validation():
     # y strided: stateL must avoid y's span
     assert _conv_strided_call((0, 0, 50, 1000), sL=_CFAKE["y"] + (1000 + 7 * 50 + 40) * 2 - 4) == 5
     assert _conv_strided_call((0, 0, 50, 1000), sL=_CFAKE["y"] + (1000 + 7 * 50 + 40) * 2) == 8
+
+
+def _conv_bld_call(layout, **over):
+    a = dict(batch=2, dim=8, seqlen=40, width=4, ind=1, flags=1, outd=1, **_CFAKE)
+    a.update(over)
+    lay = None if layout is None else ssm.ConvBldLayout(*layout)
+    return ssm.lib().ssm_conv1d_fwd_bld(
+        a["batch"], a["dim"], a["seqlen"], a["width"], a["ind"], a["flags"], a["x"], a["w"],
+        a["bias"], a["s0"], a["outd"], a["y"], a["sL"],
+        ctypes.byref(lay) if lay is not None else None, None)
+
+
+@no_gpu
+def test_conv_bld_validation():
+    """ssm_conv1d_fwd_bld: x, y as [batch][L][dim] with step and batch strides."""
+    assert _conv_bld_call(None) == 8
+    assert _conv_bld_call((0, 0, 0, 0)) == 8
+    assert _conv_bld_call((8, 320, 8, 320)) == 8          # the dense strides, explicit
+    assert _conv_bld_call((7, 0, 0, 0)) == 2              # step below dim
+    assert _conv_bld_call((0, 0, -8, 0)) == 2
+    assert _conv_bld_call((0, 319, 0, 0)) == 2            # batch stride below seqlen * step
+    assert _conv_bld_call(((1 << 40) + 8, 0, 0, 0)) == 2  # step stride above 2^40
+    assert _conv_bld_call((0, 1 << 56, 0, 0)) == 2
+    for over, status in [(dict(x=None), 1), (dict(batch=0), 2), (dict(seqlen=0), 2),
+                         (dict(ind=2), 3), (dict(width=1), 6), (dict(flags=2), 6),
+                         (dict(x=_CFAKE["x"] + 1), 4), (dict(sL=_CFAKE["sL"] + 2), 4),
+                         (dict(sL=_CFAKE["s0"]), 8), (dict(sL=_CFAKE["s0"] + 4), 5)]:
+        assert _conv_bld_call(None, **over) == status, over
+    # x as the first half of a [2, 40, 16] bf16 projection output: its span is
+    # 640 + 39 * 16 + 8 elements, so y (bf16) may start right after it, not before
+    xz = (16, 640, 0, 0)
+    span = 640 + 39 * 16 + 8
+    assert _conv_bld_call(xz, y=_CFAKE["x"] + (span - 1) * 2) == 5
+    assert _conv_bld_call(xz, y=_CFAKE["x"] + span * 2) == 8
 
 
 def _conv_update_call(L, **over):
