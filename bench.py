@@ -655,6 +655,20 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
     fwd_ckpt()
     bwd_ckpt_ms = timed(lambda: call(2))
     zoh_ms = timed(lambda: call(1))  # SSM_FLAG_ZOH_B, checkpoints recomputed
+    # the same backward on (batch, L, dim) tensors (ssm_scan_bwd_bld): inputs
+    # transposed into its workspace, outputs transposed back
+    del ws
+    tb = lambda k: t[k].transpose(1, 2).contiguous()
+    bt = {k: tb(k) for k in ("x", "dt", "z", "Bm", "Cm")}
+    dyb = dy.transpose(1, 2).contiguous()
+    gb = {k: torch.empty((wl.batch, wl.seqlen, wl.dim), device="cuda") for k in ("dx", "ddt", "dz")}
+    wsb = torch.empty(ssm.lib().ssm_scan_bwd_bld_workspace_bytes(wl.batch, wl.dim, wl.seqlen,
+                                                                 wl.dstate),
+                      dtype=torch.uint8, device="cuda")
+    bld_ms = timed(lambda: ssm.ssm_scan_bwd_bld(
+        bt["x"], bt["dt"], t["A"], bt["Bm"], bt["Cm"], dyb, dt_bias=t["dt_bias"],
+        Dskip=t["Dskip"], z=bt["z"], workspace=wsb, dx=gb["dx"], ddt=gb["ddt"], dz=gb["dz"]))
+    del bt, dyb, gb, wsb
     elems = wl.batch * wl.dim * wl.seqlen * wl.dstate
     slots = elems * BWD_SLOTS_PER_ELEM + wl.batch * wl.dim * wl.seqlen * BWD_SLOTS_PER_ROW_STEP
     achieved = slots / (ms * 1e-3) / 1e12
@@ -665,8 +679,10 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
                          "model": "fp32 VALU issue slots (transcendental = 4), %.2f slots/element"
                                   % (slots / elems)},
             "with_forward_checkpoints": {"forward_ms": fwd_ckpt_ms, "backward_ms": bwd_ckpt_ms},
-            "zoh_ms_mean": zoh_ms,
+            "zoh_ms_mean": zoh_ms, "bld_layout_ms_mean": bld_ms,
             "note": "checkpoint recompute + zero-fill + reverse pass + partial-copy sum; "
+                    "bld_layout: ssm_scan_bwd_bld on (batch, L, dim) tensors, transposes "
+                    "included; "
                     "with_forward_checkpoints: the forward writes the checkpoints and the "
                     "backward skips its recomputation pass; zoh: the exact zero-order-hold "
                     "form of B-bar"}

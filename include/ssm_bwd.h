@@ -120,6 +120,55 @@ ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
                                   size_t workspace_bytes, const ssm_scan_bwd_layout_t *layout,
                                   void *stream);
 
+/*
+ * The backward pass on (batch, L, dim)-ordered tensors, the layout of
+ * ssm_scan_fwd_bld (ssm.h): a time step's channels (states) contiguous, time
+ * steps apart.  Strides in ELEMENTS of each tensor's own type:
+ *   x, dt, z, dy, dx, ddt, dz (index i = 0..6 in that order): element
+ *            (b, t, d) at b * batch_stride[i] + t * step[i] + d;
+ *            step[i] >= dim (0 means dim), batch_stride[i] >= seqlen * step
+ *            (0 means seqlen * step)
+ *   Bm, Cm   element (b, t, n) at b * *_batch + t * *_step + n, limits as
+ *            in ssm_bld_layout_t (B_step, C_step >= dstate)
+ * A negative stride, one below its minimum, a step stride above 2^40 or a
+ * tensor spanning 2^56 elements or more is SSM_ERR_BAD_SHAPE.  A NULL
+ * layout means all zero (dense).
+ */
+typedef struct {
+    long long step[7];
+    long long batch_stride[7];
+    long long B_step, C_step, B_batch, C_batch;
+} ssm_scan_bwd_bld_layout_t;
+
+/* Device workspace ssm_scan_bwd_bld needs, in bytes: seven
+ * [batch][dim][seqlen] and four [batch][dstate][seqlen] planes sized for fp32
+ * (each rounded up to 256 bytes), then ssm_scan_bwd_workspace_bytes(...).
+ * 0 for sizes it refuses (as ssm_scan_bwd_workspace_bytes). */
+size_t ssm_scan_bwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate);
+
+/*
+ * ssm_scan_bwd on (batch, L, dim)-ordered tensors laid out by `layout` (host
+ * pointer, read during the call only).  The same arguments, gradients (up to
+ * the rounding of the atomic sums) and errors as ssm_scan_bwd, with:
+ *   dBm, dCm  [batch][seqlen][dstate] fp32, dense
+ *   workspace, workspace_bytes: at least ssm_scan_bwd_bld_workspace_bytes(...)
+ *   flags     SSM_FLAG_ZOH_B only (ssm_scan_fwd_bld writes no checkpoints:
+ *             SSM_FLAG_CHECKPOINTS is SSM_ERR_UNSUPPORTED)
+ * The call copies x, dt, z, dy, Bm and Cm into [batch][dim][seqlen] (and
+ * [batch][dstate][seqlen]) order in the workspace with tiled transposes
+ * (exact copies), runs the backward kernels there, and copies dx, ddt, dz,
+ * dBm and dCm back.  Overlap is checked on address ranges from the first to
+ * the last element.  Supported sizes: as ssm_scan_fwd.
+ */
+ssm_status_t ssm_scan_bwd_bld(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype,
+                              unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                              const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                              const void *z, const float *h0, ssm_dtype_t grad_dtype,
+                              const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                              float *dBm, float *dCm, float *dA, float *dDskip, float *ddt_bias,
+                              float *dh0, void *workspace, size_t workspace_bytes,
+                              const ssm_scan_bwd_bld_layout_t *layout, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,7 +41,8 @@ EXPORTS = ["ssm_abi_version", "ssm_status_string", "ssm_scan_fwd_workspace_bytes
            "ssm_state_update", "ssm_state_update_strided",
            "ssm_conv1d_fwd", "ssm_conv1d_fwd_strided", "ssm_conv1d_fwd_bld", "ssm_conv1d_update",
            "ssm_conv1d_update_strided",
-           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_strided"]
+           "ssm_scan_bwd_workspace_bytes", "ssm_scan_bwd", "ssm_scan_bwd_strided",
+           "ssm_scan_bwd_bld_workspace_bytes", "ssm_scan_bwd_bld"]
 
 
 class ScanLayout(ctypes.Structure):
@@ -61,6 +62,14 @@ class BwdLayout(ctypes.Structure):
     """ssm_scan_bwd_layout_t: strides in elements, 0 = dense default."""
     _fields_ = [("seq_row", ctypes.c_longlong), ("seq_batch", ctypes.c_longlong * 7),
                 ("bc_row", ctypes.c_longlong), ("bc_batch", ctypes.c_longlong * 2)]
+
+
+class BwdBldLayout(ctypes.Structure):
+    """ssm_scan_bwd_bld_layout_t: step and batch strides in elements (x, dt, z,
+    dy, dx, ddt, dz; then Bm, Cm), 0 = dense default."""
+    _fields_ = [("step", ctypes.c_longlong * 7), ("batch_stride", ctypes.c_longlong * 7),
+                ("B_step", ctypes.c_longlong), ("C_step", ctypes.c_longlong),
+                ("B_batch", ctypes.c_longlong), ("C_batch", ctypes.c_longlong)]
 
 
 class ConvLayout(ctypes.Structure):
@@ -133,6 +142,11 @@ def lib():
         L.ssm_scan_bwd_strided.restype = i
         L.ssm_scan_bwd_strided.argtypes = ([i, i, i, i, i, u] + [vp] * 9 + [i] + [vp] * 12 +
                                            [sz, ctypes.POINTER(BwdLayout), vp])
+        L.ssm_scan_bwd_bld_workspace_bytes.restype = sz
+        L.ssm_scan_bwd_bld_workspace_bytes.argtypes = [i, i, i, i]
+        L.ssm_scan_bwd_bld.restype = i
+        L.ssm_scan_bwd_bld.argtypes = ([i, i, i, i, i, u] + [vp] * 9 + [i] + [vp] * 12 +
+                                       [sz, ctypes.POINTER(BwdBldLayout), vp])
         L.ssm_conv1d_fwd.restype = i
         L.ssm_conv1d_fwd.argtypes = [i, i, i, i, i, u] + [vp] * 4 + [i, vp, vp, vp]
         L.ssm_conv1d_fwd_strided.restype = i
@@ -590,6 +604,65 @@ def ssm_scan_bwd(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=N
 
 
 @_on_caller_stream
+def ssm_scan_bwd_bld(x, dt, A, Bm, Cm, dy, *, dt_bias=None, Dskip=None, z=None, h0=None,
+                     dhL=None, grad_dtype=torch.float32, workspace=None, dx=None, ddt=None,
+                     dz=None, zoh=False, stream=None):
+    """ssm_scan_bwd on (batch, L, dim) tensors: x, dt, z, dy and the outputs
+    dx, ddt, dz as [batch, L, dim], Bm, Cm as [batch, L, N] (the layout of
+    ssm_scan_fwd_bld; channel index contiguous, e.g. z and dz as halves of
+    [batch, L, 2 dim] buffers).  Returns a dict as ssm_scan_bwd, with dBm and
+    dCm as [batch, L, N].  workspace: ssm_scan_bwd_bld_workspace_bytes(...)
+    bytes (allocated here when not given)."""
+    _no_broadcast_args(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, dy=dy, dt_bias=dt_bias, Dskip=Dskip, z=z,
+                       h0=h0, dhL=dhL, dx=dx, ddt=ddt, dz=dz)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, L, dim]")
+    batch, L, dim = x.shape
+    N = A.shape[-1]
+    ind, dev, f32 = x.dtype, x.device, torch.float32
+    shape = (batch, L, dim)
+    g = {
+        "dx": dx if dx is not None else torch.empty(shape, dtype=grad_dtype, device=dev),
+        "ddt": ddt if ddt is not None else torch.empty(shape, dtype=grad_dtype, device=dev),
+        "dz": (dz if dz is not None else torch.empty(shape, dtype=grad_dtype, device=dev))
+              if z is not None else None,
+        "dBm": torch.empty((batch, L, N), dtype=f32, device=dev),
+        "dCm": torch.empty((batch, L, N), dtype=f32, device=dev),
+        "dA": torch.empty((dim, N), dtype=f32, device=dev),
+        "dDskip": torch.empty((dim,), dtype=f32, device=dev),
+        "ddt_bias": torch.empty((dim,), dtype=f32, device=dev),
+        "dh0": torch.empty((batch, dim, N), dtype=f32, device=dev),
+    }
+    need = lib().ssm_scan_bwd_bld_workspace_bytes(batch, dim, L, N)
+    if workspace is None:
+        workspace = torch.empty((max(1, need),), dtype=torch.uint8, device=dev)
+    names = ("x", "dt", "z", "dy", "dx", "ddt", "dz")
+    (xp, dtp, zp, dyp, dxp, ddtp, dzp), st, sb = _steps(
+        (x, dt, z, dy, g["dx"], g["ddt"], g["dz"]), names, shape,
+        {"x": ind, "dt": ind, "z": ind, "dy": grad_dtype, "dx": grad_dtype, "ddt": grad_dtype,
+         "dz": grad_dtype})
+    (Bp, Cp), bst, bsb = _steps((Bm, Cm), ("Bm", "Cm"), (batch, L, N), ind)
+    layout = BwdBldLayout((ctypes.c_longlong * 7)(*st), (ctypes.c_longlong * 7)(*sb),
+                          bst[0], bst[1], bsb[0], bsb[1])
+    args = [
+        xp, dtp, _ptr(dt_bias, "dt_bias", (dim,), f32), _ptr(A, "A", (dim, N), f32),
+        Bp, Cp, _ptr(Dskip, "Dskip", (dim,), f32), zp, _ptr(h0, "h0", (batch, dim, N), f32),
+    ]
+    gargs = [
+        dyp, _ptr(dhL, "dhL", (batch, dim, N), f32), dxp, ddtp, dzp, _ptr(g["dBm"], "dBm"),
+        _ptr(g["dCm"], "dCm"), _ptr(g["dA"], "dA"), _ptr(g["dDskip"], "dDskip"),
+        _ptr(g["ddt_bias"], "ddt_bias"), _ptr(g["dh0"], "dh0"),
+    ]
+    st_ = lib().ssm_scan_bwd_bld(batch, dim, L, N, _dtype_code(ind), SSM_FLAG_ZOH_B if zoh else 0,
+                                 *args, _dtype_code(grad_dtype), *gargs,
+                                 _ptr(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(),
+                                 ctypes.byref(layout), _stream(stream, dev))
+    _check(st_)
+    return g
+
+
+@_on_caller_stream
 def ssm_conv1d_fwd(x, weight, *, bias=None, state0=None, silu=True, out_dtype=None,
                    return_final_state=True, y=None, stateL=None, stream=None):
     """Causal depthwise conv over [batch, dim, L]; returns (y, stateL).
@@ -676,6 +749,7 @@ def ssm_conv1d_update(state, x, weight, *, bias=None, silu=True, out_dtype=None,
 
 scan_fwd = ssm_scan_fwd
 scan_bwd = ssm_scan_bwd
+scan_bwd_bld = ssm_scan_bwd_bld
 state_update = ssm_state_update
 conv1d_fwd = ssm_conv1d_fwd
 conv1d_fwd_bld = ssm_conv1d_fwd_bld

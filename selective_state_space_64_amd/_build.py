@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libssm.so")
 PEAKS_LIB = os.path.join(HERE, "libssm_peaks.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 SOURCES = ["ssm_api.hip", "scan_fwd.hip", "scan_bld.hip", "state_update.hip", "conv1d.hip",
-           "scan_bwd.hip"]
+           "scan_bwd.hip", "transpose.hip"]
 ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of the generated code on purpose.
 HIPFLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

@@ -862,4 +862,75 @@ hipError_t launch_scan_bwd(const BwdArgs &a, hipStream_t stream)
                        : launch_bwd_mode<float, float>(a, stream);
 }
 
+// The backward pass on (batch, L, dim)-ordered tensors: x, dt, z, dy, Bm and
+// Cm are moved into [batch][dim][L] / [batch][N][L] copies in the workspace
+// by tiled transposes (exact word copies), scan_bwd runs on the copies, and
+// dx, ddt, dz, dBm, dCm are moved back.  Workspace: seven [batch][dim][L]
+// and four [batch][N][L] planes sized for fp32 (whatever the dtypes), then
+// the backward pass's own workspace; each plane starts on a 256-byte
+// boundary.
+namespace {
+size_t plane_bytes(size_t elems) { return (elems * sizeof(float) + 255) / 256 * 256; }
+}  // namespace
+
+size_t scan_bwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    return 7 * plane_bytes(size_t(batch) * size_t(dim) * size_t(seqlen)) +
+           4 * plane_bytes(size_t(batch) * size_t(dstate) * size_t(seqlen)) +
+           scan_bwd_workspace_bytes(batch, dim, seqlen, dstate);
+}
+
+hipError_t launch_scan_bwd_bld(const BwdBldArgs &a, hipStream_t stream)
+{
+    const size_t seq = plane_bytes(size_t(a.batch) * size_t(a.dim) * size_t(a.seqlen));
+    const size_t bc = plane_bytes(size_t(a.batch) * size_t(a.dstate) * size_t(a.seqlen));
+    char *w = static_cast<char *>(a.workspace);
+    void *pl[7];  // x, dt, z, dy, dx, ddt, dz in [batch][dim][L]
+    for (int i = 0; i < 7; ++i) pl[i] = w + i * seq;
+    char *bcw = w + 7 * seq;
+    void *Bt = bcw, *Ct = bcw + bc;
+    float *dBt = reinterpret_cast<float *>(bcw + 2 * bc), *dCt = reinterpret_cast<float *>(bcw + 3 * bc);
+    void *bws = bcw + 4 * bc;
+    const int in = a.in_bf16 ? 2 : 4, gs = a.grad_bf16 ? 2 : 4;
+    const long long L = a.seqlen, DL = (long long)a.dim * L, NL = (long long)a.dstate * L;
+    if (log_enabled())
+        log_line("scan_bwd_bld: transposes into [batch][dim][L] (%d-byte inputs, %d-byte "
+                 "gradients), scan_bwd, transposes back", in, gs);
+    // inputs: (b, t, c) -> [b][c][t]
+    const void *ins[4] = {a.x, a.dt, a.z, a.dy};
+    const int isz[4] = {in, in, in, gs};
+    for (int i = 0; i < 4; ++i) {
+        if (!ins[i]) continue;
+        const hipError_t e = launch_transpose(isz[i], ins[i], a.b[i], a.t[i], pl[i], DL, L, a.batch,
+                                              a.seqlen, a.dim, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = launch_transpose(in, a.Bm, a.B_b, a.B_t, Bt, NL, L, a.batch, a.seqlen, a.dstate,
+                                    stream);
+    if (e != hipSuccess) return e;
+    e = launch_transpose(in, a.Cm, a.C_b, a.C_t, Ct, NL, L, a.batch, a.seqlen, a.dstate, stream);
+    if (e != hipSuccess) return e;
+
+    BwdArgs b{a.batch, a.dim, a.seqlen, a.dstate, a.in_bf16, a.grad_bf16,
+              pl[0], pl[1], a.dt_bias, a.A, Bt, Ct, a.Dskip, a.z ? pl[2] : nullptr, a.h0,
+              pl[3], a.dhL, pl[4], pl[5], a.z ? pl[6] : nullptr, dBt, dCt, a.dA, a.dDskip,
+              a.ddt_bias, a.dh0, bws, 0,
+              L, DL, DL, DL, DL, DL, DL, DL, L, NL, NL, a.zoh};
+    e = launch_scan_bwd(b, stream);
+    if (e != hipSuccess) return e;
+
+    // per-step gradients: [b][c][t] -> (b, t, c)
+    void *outs[3] = {a.dx, a.ddt, a.dz};
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i]) continue;
+        e = launch_transpose(gs, pl[4 + i], DL, L, outs[i], a.b[4 + i], a.t[4 + i], a.batch, a.dim,
+                             a.seqlen, stream);
+        if (e != hipSuccess) return e;
+    }
+    // dBm, dCm: [b][n][t] -> dense [b][t][n]
+    e = launch_transpose(4, dBt, NL, L, a.dBm, NL, a.dstate, a.batch, a.dstate, a.seqlen, stream);
+    if (e != hipSuccess) return e;
+    return launch_transpose(4, dCt, NL, L, a.dCm, NL, a.dstate, a.batch, a.dstate, a.seqlen, stream);
+}
+
 }  // namespace ssm

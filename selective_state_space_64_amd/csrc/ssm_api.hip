@@ -833,4 +833,90 @@ ssm_status_t ssm_scan_bwd_strided(int batch, int dim, int seqlen, int dstate,
                                      workspace, workspace_bytes, layout, stream);
 }
 
+size_t ssm_scan_bwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate)
+{
+    if (!ssm_scan_bwd_workspace_bytes(batch, dim, seqlen, dstate)) return 0;
+    return ssm::scan_bwd_bld_workspace_bytes(batch, dim, seqlen, dstate);
+}
+
+ssm_status_t ssm_scan_bwd_bld(int batch, int dim, int seqlen, int dstate, ssm_dtype_t in_dtype_e,
+                              unsigned flags, const void *x, const void *dt, const float *dt_bias,
+                              const float *A, const void *Bm, const void *Cm, const float *Dskip,
+                              const void *z, const float *h0, ssm_dtype_t grad_dtype_e,
+                              const void *dy, const float *dhL, void *dx, void *ddt, void *dz,
+                              float *dBm, float *dCm, float *dA, float *dDskip, float *ddt_bias,
+                              float *dh0, void *workspace, size_t workspace_bytes,
+                              const ssm_scan_bwd_bld_layout_t *layout, void *stream)
+{
+    const int in_dtype = enum_bits(in_dtype_e), grad_dtype = enum_bits(grad_dtype_e);
+    if (!x || !dt || !A || !Bm || !Cm || !dy || !dx || !ddt || !dBm || !dCm || !dA || !workspace)
+        return SSM_ERR_NULL_ARG;
+    if (z && !dz) return SSM_ERR_NULL_ARG;
+    if (!z) dz = nullptr;
+    if (!valid_dtype(in_dtype) || !valid_dtype(grad_dtype)) return SSM_ERR_BAD_DTYPE;
+    if (batch < 1 || dim < 1 || seqlen < 1 || batch > ssm::kMaxBatch || dim > ssm::kMaxDim ||
+        seqlen > ssm::kMaxSeqlen)
+        return SSM_ERR_BAD_SHAPE;
+    if (!valid_dstate(dstate) || (flags & ~SSM_FLAG_ZOH_B) != 0) return SSM_ERR_UNSUPPORTED;
+    const size_t bc_elems = mul3(batch, dstate, seqlen);
+    const size_t st_elems = mul3(batch, dim, dstate);
+    if (!mul3(batch, dim, seqlen) || !bc_elems || !st_elems) return SSM_ERR_BAD_SHAPE;
+    const ssm_scan_bwd_bld_layout_t dense{};
+    const ssm_scan_bwd_bld_layout_t &lay = layout ? *layout : dense;
+    // x, dt, z, dy, dx, ddt, dz, then Bm, Cm: strides with defaults filled in, spans
+    long long st[9], sb[9];
+    size_t sp[9];
+    for (int i = 0; i < 7; ++i)
+        if (!bld_span(lay.step[i], lay.batch_stride[i], batch, seqlen, dim, st[i], sb[i], sp[i]))
+            return SSM_ERR_BAD_SHAPE;
+    if (!bld_span(lay.B_step, lay.B_batch, batch, seqlen, dstate, st[7], sb[7], sp[7]) ||
+        !bld_span(lay.C_step, lay.C_batch, batch, seqlen, dstate, st[8], sb[8], sp[8]))
+        return SSM_ERR_BAD_SHAPE;
+    const size_t ws_need = ssm::scan_bwd_bld_workspace_bytes(batch, dim, seqlen, dstate);
+
+    const size_t in = dsize(in_dtype), gs = dsize(grad_dtype);
+    for (const void *p : {x, dt, Bm, Cm, z})
+        if (misaligned(p, in)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {dy, (const void *)dx, (const void *)ddt, (const void *)dz})
+        if (misaligned(p, gs)) return SSM_ERR_MISALIGNED;
+    for (const void *p : {(const void *)dt_bias, (const void *)A, (const void *)Dskip,
+                          (const void *)h0, (const void *)dhL, (const void *)dBm, (const void *)dCm,
+                          (const void *)dA, (const void *)dDskip, (const void *)ddt_bias,
+                          (const void *)dh0, (const void *)workspace})
+        if (misaligned(p, 4)) return SSM_ERR_MISALIGNED;
+    if (workspace_bytes < ws_need) return SSM_ERR_WORKSPACE;
+
+    struct Buf {
+        const void *p;
+        size_t bytes;
+    };
+    const size_t fb = sizeof(float);
+    const Buf inputs[] = {{x, sp[0] * in},  {dt, sp[1] * in},  {dt_bias, dim * fb},
+                          {A, size_t(dim) * dstate * fb},
+                          {Bm, sp[7] * in},  {Cm, sp[8] * in},  {Dskip, dim * fb},
+                          {z, sp[2] * in},  {h0, st_elems * fb},  {dy, sp[3] * gs},
+                          {dhL, st_elems * fb}};
+    const Buf outputs[] = {{dx, sp[4] * gs},         {ddt, sp[5] * gs},       {dz, sp[6] * gs},
+                           {dBm, bc_elems * fb},     {dCm, bc_elems * fb},
+                           {dA, size_t(dim) * dstate * fb},
+                           {dDskip, dim * fb},       {ddt_bias, dim * fb},    {dh0, st_elems * fb},
+                           {workspace, ws_need}};
+    const int nout = int(sizeof(outputs) / sizeof(outputs[0]));
+    for (int o = 0; o < nout; ++o) {
+        for (const Buf &i : inputs)
+            if (overlaps(outputs[o].p, outputs[o].bytes, i.p, i.bytes)) return SSM_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < nout; ++o2)
+            if (overlaps(outputs[o].p, outputs[o].bytes, outputs[o2].p, outputs[o2].bytes))
+                return SSM_ERR_ALIAS;
+    }
+    ssm::BwdBldArgs a{batch, dim, seqlen, dstate, in_dtype == SSM_BF16, grad_dtype == SSM_BF16,
+                      (flags & SSM_FLAG_ZOH_B) != 0, x, dt, dt_bias, A, Bm, Cm, Dskip, z, h0, dy,
+                      dhL, dx, ddt, dz, dBm, dCm, dA, dDskip, ddt_bias, dh0, workspace,
+                      {st[0], st[1], st[2], st[3], st[4], st[5], st[6]},
+                      {sb[0], sb[1], sb[2], sb[3], sb[4], sb[5], sb[6]},
+                      st[7], sb[7], st[8], sb[8]};
+    const hipError_t e = ssm::launch_scan_bwd_bld(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
 }  // extern "C"

@@ -107,6 +107,35 @@ struct BwdArgs {
     int zoh;  // the exact zero-order-hold form of B-bar
 };
 
+// The backward pass on (batch, L, dim)-ordered tensors: element (b, t, c) of
+// x, dt, z, dy, dx, ddt, dz (c < dim) and of Bm, Cm (c < dstate) at
+// b * *_b + t * *_t + c (element strides, index i of t[] / b[] in the order
+// x, dt, z, dy, dx, ddt, dz); dBm, dCm dense [batch][seqlen][dstate].
+struct BwdBldArgs {
+    int batch, dim, seqlen, dstate;
+    int in_bf16, grad_bf16, zoh;
+    const void *x, *dt;
+    const float *dt_bias, *A;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *h0;
+    const void *dy;
+    const float *dhL;
+    void *dx, *ddt, *dz;
+    float *dBm, *dCm, *dA, *dDskip, *ddt_bias, *dh0;
+    void *workspace;  // scan_bwd_bld_workspace_bytes
+    long long t[7], b[7];
+    long long B_t, B_b, C_t, C_b;
+};
+size_t scan_bwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate);
+hipError_t launch_scan_bwd_bld(const BwdBldArgs &a, hipStream_t stream);
+// Batched transpose of esize-byte elements (2 or 4): src (b, r, c) at
+// src + b s_b + r s_r + c to dst (b, c, r) at dst + b d_b + c d_c + r.
+hipError_t launch_transpose(int esize, const void *src, long long s_b, long long s_r, void *dst,
+                            long long d_b, long long d_c, int batch, int rows, int cols,
+                            hipStream_t stream);
+
 // The forward on (batch, L, dim)-ordered tensors (scan_bld.hip): element
 // strides of a time step and of a batch entry for each tensor; the channel
 // (x, dt, z, y) or state (Bm, Cm) index is contiguous.

@@ -11,6 +11,7 @@
  */
 #include <stdint.h>
 #include <stdio.h>
+#include <string.h>
 
 #include "ssm.h"
 #include "ssm_bwd.h"
@@ -133,6 +134,16 @@ int main(void)
     bl.seq_batch[6] = 0;
     bl.bc_row = 1ll << 62;
     REFUSED(ssm_scan_bwd_strided(2, 8, 40, 16, bf, 0, x, dt, bias, A, Bm, Cm, Dk, z, h0, f32, dy, NULL, dx, ddt, dz, dB, dC, dA, dD, dbias, dh0, ws, 1 << 20, &bl, 0));
+    // backward on (batch, L, dim) tensors
+    sum += ssm_scan_bwd_bld_workspace_bytes(4, 5120, 2048, 16) + ssm_scan_bwd_bld_workspace_bytes(4, 5120, 2048, 3);
+    ssm_scan_bwd_bld_layout_t bb;
+    memset(&bb, 0, sizeof bb);
+    bb.step[3] = 7;
+    REFUSED(ssm_scan_bwd_bld(2, 8, 40, 16, bf, 0, x, dt, bias, A, Bm, Cm, Dk, z, h0, f32, dy, NULL, dx, ddt, dz, dB, dC, dA, dD, dbias, dh0, ws, 1 << 26, &bb, 0));
+    bb.step[3] = 0;
+    bb.C_batch = 1ll << 62;
+    REFUSED(ssm_scan_bwd_bld(2, 8, 40, 16, bf, 0, x, dt, bias, A, Bm, Cm, Dk, z, h0, f32, dy, NULL, dx, ddt, dz, dB, dC, dA, dD, dbias, dh0, ws, 1 << 26, &bb, 0));
+    REFUSED(ssm_scan_bwd_bld(2, 8, 40, 16, bf, SSM_FLAG_CHECKPOINTS, x, dt, bias, A, Bm, Cm, Dk, z, h0, f32, dy, NULL, dx, ddt, dz, dB, dC, dA, dD, dbias, dh0, ws, 1 << 26, NULL, 0));
 
     printf("abi sanitizer run: %s (workspace checksum %zu)\n", failures ? "FAILED" : "ok", sum);
     return failures ? 1 : 0;

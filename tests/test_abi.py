@@ -57,7 +57,9 @@ def test_binding_argtypes_match_prototypes():
         argtypes = getattr(L, name).argtypes
         assert len(argtypes) == len(params), (name, len(argtypes), len(params))
         for decl, at in zip(params, argtypes):
-            if "ssm_scan_layout_t" in decl:
+            if "ssm_scan_bwd_bld_layout_t" in decl:
+                assert at == ctypes.POINTER(ssm.BwdBldLayout), (name, decl, at)
+            elif "ssm_scan_layout_t" in decl:
                 assert at == ctypes.POINTER(ssm.ScanLayout), (name, decl, at)
             elif "ssm_scan_bwd_layout_t" in decl:
                 assert at == ctypes.POINTER(ssm.BwdLayout), (name, decl, at)
@@ -613,6 +615,45 @@ def test_conv_bld_validation():
     span = 640 + 39 * 16 + 8
     assert _conv_bld_call(xz, y=_CFAKE["x"] + (span - 1) * 2) == 5
     assert _conv_bld_call(xz, y=_CFAKE["x"] + span * 2) == 8
+
+
+@no_gpu
+def test_scan_bwd_bld_validation():
+    """ssm_scan_bwd_bld: (batch, L, dim) strides checked before any launch."""
+    L = ssm.lib()
+    f = {k: 0x10000000 * (i + 1) for i, k in enumerate(
+        ["x", "dt", "A", "Bm", "Cm", "z", "dy", "dx", "ddt", "dz", "dBm", "dCm", "dA", "ws"])}
+    need = L.ssm_scan_bwd_bld_workspace_bytes(2, 8, 40, 4)
+    assert need >= 7 * 2560 + 4 * 1280 + L.ssm_scan_bwd_workspace_bytes(2, 8, 40, 4)
+    assert L.ssm_scan_bwd_bld_workspace_bytes(2, 8, 40, 3) == 0
+    seven = ctypes.c_longlong * 7
+
+    def call(layout=None, flags=0, wsb=need, **over):
+        a = dict(f, ind=1, gd=0)
+        a.update(over)
+        lay = ssm.BwdBldLayout(*layout) if layout else None
+        return L.ssm_scan_bwd_bld(2, 8, 40, 4, a["ind"], flags, a["x"], a["dt"], None, a["A"],
+                                  a["Bm"], a["Cm"], None, a["z"], None, a["gd"], a["dy"], None,
+                                  a["dx"], a["ddt"], a["dz"], a["dBm"], a["dCm"], a["dA"], None,
+                                  None, None, a["ws"], wsb,
+                                  ctypes.byref(lay) if lay is not None else None, None)
+
+    assert call() == 8
+    assert call(layout=(seven(), seven(), 0, 0, 0, 0)) == 8
+    assert call(flags=1) == 8                                   # exact ZOH accepted
+    assert call(flags=2) == 6                                   # checkpoints refused
+    assert call(ws=None) == 1
+    assert call(layout=(seven(0, 7, 0, 0, 0, 0, 0), seven(), 0, 0, 0, 0)) == 2
+    assert call(layout=(seven(), seven(0, 0, 0, 0, 0, 0, 319), 0, 0, 0, 0)) == 2
+    assert call(layout=(seven(), seven(), 0, 3, 0, 0)) == 2
+    assert call(layout=(seven(), seven(), 0, 0, 0, 159)) == 2
+    assert call(wsb=need - 1) == 7
+    assert call(x=f["x"] + 1) == 4
+    # dz as the second half of a [2, 40, 16] fp32 gradient buffer whose first
+    # half is dx: interleaved halves of one buffer overlap by address range
+    assert call(layout=(seven(0, 0, 0, 0, 16, 0, 16), seven(0, 0, 0, 0, 640, 0, 640), 0, 0, 0, 0),
+                dz=f["dx"] + 8 * 4) == 5
+    assert call(layout=(seven(0, 0, 0, 0, 0, 0, 16), seven(0, 0, 0, 0, 0, 0, 640), 0, 0, 0, 0)) == 8
 
 
 def _conv_update_call(L, **over):
