@@ -11,8 +11,9 @@
 // A workgroup of 256 threads moves 64 x 64 tiles through LDS (one padding
 // column, so that the column reads of the second half fall in different
 // banks): every global read and write of a wave covers 64 consecutive
-// elements of one row.  Row tiles beyond the grid's y extent (65535) are
-// walked by a grid-stride loop.
+// elements of one row, or, where every row is 4-element aligned, 4 rows of 64
+// elements in 4-element vectors.  Row tiles beyond the grid's y extent
+// (65535) are walked by a grid-stride loop.
 #include "ssm_device.hpp"
 #include "ssm_launch.hpp"
 
@@ -37,15 +38,68 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T *src, long long 
         const int r0 = rt * kTile;
         __syncthreads();  // the previous tile has been written out
 #pragma unroll
-        for (int i = ty; i < kTile; i += 256 / kTile) {
-            const int r = r0 + i, c = c0 + tx;
+        for (int k = 0; k < kTile / 4; ++k) {
+            const int i = ty + 4 * k, r = r0 + i, c = c0 + tx;
             if (r < rows && c < cols) tile[i][tx] = s[(long long)r * s_r + c];
         }
         __syncthreads();
 #pragma unroll
-        for (int i = ty; i < kTile; i += 256 / kTile) {
-            const int c = c0 + i, r = r0 + tx;
+        for (int k = 0; k < kTile / 4; ++k) {
+            const int i = ty + 4 * k, c = c0 + i, r = r0 + tx;
             if (r < rows && c < cols) d[(long long)c * d_c + r] = tile[tx][i];
+        }
+    }
+}
+
+// The same move with 4-element vectors on both sides, for calls whose every
+// row of src and dst starts on a multiple of 4 elements of a base aligned to
+// 4 elements: a thread reads 4 consecutive elements of a src row (8 or 16
+// bytes) and writes 4 consecutive elements of a dst row, gathered from 4 rows
+// of the tile.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose4_kernel(const T *src, long long s_b, long long s_r,
+                                                         T *dst, long long d_b, long long d_c,
+                                                         int rows, int cols)
+{
+    typedef T v4 __attribute__((ext_vector_type(4)));
+    __shared__ T tile[kTile][kTile + 1];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // 16 x 16 threads
+    const int c0 = int(blockIdx.x) * kTile;
+    const T *s = src + (long long)blockIdx.z * s_b;
+    T *d = dst + (long long)blockIdx.z * d_b;
+    for (int rt = blockIdx.y; (long long)rt * kTile < rows; rt += gridDim.y) {
+        const int r0 = rt * kTile;
+        __syncthreads();  // the previous tile has been written out
+#pragma unroll
+        for (int k = 0; k < kTile / 16; ++k) {
+            const int i = ty + 16 * k, r = r0 + i, c = c0 + 4 * tx;
+            if (r < rows) {
+                if (c + 3 < cols) {
+                    const v4 w = *reinterpret_cast<const v4 *>(s + (long long)r * s_r + c);
+                    tile[i][4 * tx] = w.x; tile[i][4 * tx + 1] = w.y;
+                    tile[i][4 * tx + 2] = w.z; tile[i][4 * tx + 3] = w.w;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (c + q < cols) tile[i][4 * tx + q] = s[(long long)r * s_r + c + q];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kTile / 16; ++k) {
+            const int i = ty + 16 * k, c = c0 + i, r = r0 + 4 * tx;
+            if (c < cols) {
+                if (r + 3 < rows) {
+                    const v4 w = {tile[4 * tx][i], tile[4 * tx + 1][i], tile[4 * tx + 2][i],
+                                  tile[4 * tx + 3][i]};
+                    *reinterpret_cast<v4 *>(d + (long long)c * d_c + r) = w;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (r + q < rows) d[(long long)c * d_c + r + q] = tile[4 * tx + q][i];
+                }
+            }
         }
     }
 }
@@ -59,7 +113,18 @@ hipError_t launch_transpose(int esize, const void *src, long long s_b, long long
     const long long rt = (rows + kTile - 1) / kTile, ct = (cols + kTile - 1) / kTile;
     if (ct > 0x7fffffffLL || batch > 65535) return hipErrorInvalidConfiguration;
     const dim3 grid{unsigned(ct), unsigned(rt < 65535 ? rt : 65535), unsigned(batch)};
-    if (esize == 2) {
+    const bool vec = (reinterpret_cast<uintptr_t>(src) % (4 * esize)) == 0 &&
+                     (reinterpret_cast<uintptr_t>(dst) % (4 * esize)) == 0 && s_b % 4 == 0 &&
+                     s_r % 4 == 0 && d_b % 4 == 0 && d_c % 4 == 0;
+    if (vec && esize == 2) {
+        hipLaunchKernelGGL(transpose4_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint16_t *>(src), s_b, s_r, static_cast<uint16_t *>(dst),
+                           d_b, d_c, rows, cols);
+    } else if (vec) {
+        hipLaunchKernelGGL(transpose4_kernel<uint32_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint32_t *>(src), s_b, s_r, static_cast<uint32_t *>(dst),
+                           d_b, d_c, rows, cols);
+    } else if (esize == 2) {
         hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, stream,
                            static_cast<const uint16_t *>(src), s_b, s_r, static_cast<uint16_t *>(dst),
                            d_b, d_c, rows, cols);
