@@ -379,7 +379,9 @@ __global__ void __launch_bounds__(kConvThreads)
 conv1d_bld_kernel(ConvBldParams p, bool act)
 {
     constexpr int H = W - 1;
-    constexpr int U = 8;  // steps whose loads are issued before the first is used
+    // steps whose loads are issued before the first is used: at the 2.8B layer
+    // (bf16 in and out) 1 / 2 / 4 / 8 steps took 40.3 / 34.5 / 36.7 / 38.5 us
+    constexpr int U = 2;
     const int cb = int(blockIdx.x % unsigned(p.cblocks));
     const int b = int(blockIdx.x / unsigned(p.cblocks));
     const int d0 = (cb * kConvThreads + int(threadIdx.x)) * V;  // first channel of the lane
