@@ -601,7 +601,7 @@ BWD_SLOTS_PER_ELEM = 17      # recompute 8 + adjoint 2 + dBm, dCm 2 + dA 3 + dx/
 BWD_SLOTS_PER_ROW_STEP = 40  # softplus 9, sigmoid(u) 9, silu + silu' 14, gradient assembly 8
 
 
-def bench_bwd(torch, ssm, wl, t, launches=10):
+def bench_bwd(torch, ssm, wl, t, launches=10, warmup_seconds=1.0):
     """Backward pass (all launches of one ssm_scan_bwd call: checkpoint
     recompute, zero-fill, reverse pass, sum of partial copies) on the layer,
     dy ~ N(0, 1) fp32, gradients fp32, outputs and workspace preallocated;
@@ -632,13 +632,19 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
         if st != 0:
             raise RuntimeError("ssm_scan_bwd failed with status %d" % st)
 
-    def timed(fn):
+    def timed(fn, seconds=0.0):
+        # the clock ramps up under sustained load: the first timing of the
+        # call runs it untimed for `seconds` first, as the forward's does
+        t_end = time.perf_counter() + seconds
         for _ in range(2):
             fn()
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
         ms, _ = time_launches(torch, fn, launches, stream)
         return ms
 
-    ms = timed(call)
+    ms = timed(call, warmup_seconds)
     # training order: the forward writes the checkpoints (SSM_FLAG_CHECKPOINTS)
     # into the backward's workspace, the backward reads them
     y = torch.empty((wl.batch, wl.dim, wl.seqlen), device="cuda")
@@ -680,7 +686,8 @@ def bench_bwd(torch, ssm, wl, t, launches=10):
                                   % (slots / elems)},
             "with_forward_checkpoints": {"forward_ms": fwd_ckpt_ms, "backward_ms": bwd_ckpt_ms},
             "zoh_ms_mean": zoh_ms, "bld_layout_ms_mean": bld_ms,
-            "note": "checkpoint recompute + zero-fill + reverse pass + partial-copy sum; "
+            "note": "checkpoint recompute + zero-fill + reverse pass + partial-copy sum, "
+                    "timed after %.1f s of untimed calls; " % warmup_seconds +
                     "bld_layout: ssm_scan_bwd_bld on (batch, L, dim) tensors, transposes "
                     "included; "
                     "with_forward_checkpoints: the forward writes the checkpoints and the "
@@ -733,7 +740,8 @@ def main():
         inp = synth.make_inputs(wl)
         t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}
         del inp
-        print(json.dumps(bench_bwd(torch, ssm, wl, t, launches=args.steps)), flush=True)
+        print(json.dumps(bench_bwd(torch, ssm, wl, t, launches=args.steps,
+                                   warmup_seconds=args.warmup_seconds)), flush=True)
         return
     inp = synth.make_inputs(wl)
     t = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm", "A", "Dskip", "dt_bias")}
@@ -836,7 +844,7 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(torch, ssm, synth)
         result["conv1d"] = bench_conv(torch, ssm, synth, wl, t["x"])
-        result["backward"] = bench_bwd(torch, ssm, wl, t)
+        result["backward"] = bench_bwd(torch, ssm, wl, t, warmup_seconds=args.warmup_seconds)
     del t, y, hL, ws
     torch.cuda.empty_cache()
     if not args.no_configs:
