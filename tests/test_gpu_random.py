@@ -1,6 +1,7 @@
 """Randomised parity sweep (seeded): forward scan, backward pass, decode step
 and conv over random shapes, dtypes, state sizes, optional inputs, strided
-views and split lengths, each against the fp64 oracle in full.
+views and split lengths, each against the fp64 oracle in full; the same
+cases in (batch, L, dim) order.
 
 The configurations are drawn once from a fixed seed, so a failure names a
 reproducible case (its id carries every parameter)."""
@@ -130,3 +131,53 @@ def test_random_decode_and_conv(c):
     assert rel_err(yc.cpu().numpy(), rc) <= TOL_F32
     assert np.array_equal(sc.cpu().numpy(), rs.astype(np.float32))
     del xb
+
+
+@pytest.mark.parametrize("c", CASES, ids=_id)
+def test_random_bld_layout(c):
+    """The (batch, L, dim) entry points on the same random cases: the forward
+    scan against the oracle; the backward's per-step gradients bit for bit
+    against the [batch][dim][L] call on the same values (the same kernels on
+    exact copies) and its sums over channels, batch and time within fp32
+    rounding; the conv (width 4) bit for bit against the [batch][dim][L] conv."""
+    print("random bld", _id(c), flush=True)
+    inp = synth.make_inputs(workload("random", c["batch"], c["dim"], c["N"], c["L"], c["dtype"],
+                                     seed=100 + c["i"]), with_h0=True)
+    dev = {k: to_dev(inp, k) for k in ("x", "dt", "z", "Bm", "Cm")}
+    bl = {k: v.transpose(1, 2).contiguous() for k, v in dev.items()}
+    A = to_dev(inp, "A")
+    opt = dict(dt_bias=to_dev(inp, "dt_bias") if c["bias"] else None,
+               Dskip=to_dev(inp, "Dskip") if c["skip"] else None,
+               h0=torch.from_numpy(inp.h0.astype(np.float32)).cuda() if c["h0"] else None,
+               zoh=c["zoh"])
+    y, hL = ssm.ssm_scan_fwd_bld(bl["x"], bl["dt"], A, bl["Bm"], bl["Cm"],
+                                 z=bl["z"] if c["gate"] else None, **opt)
+    rng = np.random.default_rng(c["i"])
+    dy = torch.from_numpy(rng.standard_normal((c["batch"], c["dim"], c["L"])).astype(np.float32)).cuda()
+    g = ssm.ssm_scan_bwd_bld(bl["x"], bl["dt"], A, bl["Bm"], bl["Cm"], dy.transpose(1, 2).contiguous(),
+                             z=bl["z"] if c["gate"] else None, **opt)
+    r = ssm.ssm_scan_bwd(dev["x"], dev["dt"], A, dev["Bm"], dev["Cm"], dy,
+                         z=dev["z"] if c["gate"] else None, **opt)
+    wt = torch.from_numpy(synth.conv_parameters(workload("random_conv", c["batch"], c["dim"], c["N"],
+                                                         c["L"], c["dtype"], seed=400 + c["i"]), 4)[0]).cuda()
+    yc, sc = ssm.ssm_conv1d_fwd_bld(bl["x"], wt, silu=c["gate"])
+    yr, sr = ssm.ssm_conv1d_fwd(dev["x"], wt, silu=c["gate"])
+    torch.cuda.synchronize()
+    ry, rh = oracle_full(inp, c["gate"], c["skip"], c["bias"], inp.h0 if c["h0"] else None,
+                         zoh=c["zoh"])
+    tol = tol_for(c["dtype"])
+    assert rel_err(y.cpu().numpy().transpose(0, 2, 1), ry) <= tol
+    assert rel_err(hL.cpu().numpy(), rh) <= tol
+    for k in ("dx", "ddt", "dz"):
+        if r[k] is None:
+            assert g[k] is None
+            continue
+        assert torch.equal(g[k], r[k].transpose(1, 2)), k
+    for k in ("dBm", "dCm", "dA", "dDskip", "ddt_bias", "dh0"):
+        gv, rv = g[k].cpu().numpy(), r[k].cpu().numpy()
+        if k in ("dBm", "dCm"):
+            rv = rv.transpose(0, 2, 1)
+        if gv.ndim == 1:
+            gv, rv = gv[None], rv[None]
+        assert rel_err(gv, rv) <= 1e-5, (k, rel_err(gv, rv))
+    assert torch.equal(yc, yr.transpose(1, 2)) and torch.equal(sc, sr)
