@@ -143,7 +143,9 @@ typedef struct {
 /* Device workspace ssm_scan_bwd_bld needs, in bytes: seven
  * [batch][dim][seqlen] and four [batch][dstate][seqlen] planes sized for fp32
  * (each rounded up to 256 bytes), then ssm_scan_bwd_workspace_bytes(...).
- * 0 for sizes it refuses (as ssm_scan_bwd_workspace_bytes). */
+ * 0 for sizes it refuses (as ssm_scan_bwd_workspace_bytes, and sizes whose
+ * workspace would reach 2^62 bytes, which ssm_scan_bwd_bld refuses with
+ * SSM_ERR_BAD_SHAPE). */
 size_t ssm_scan_bwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate);
 
 /*

@@ -873,11 +873,18 @@ namespace {
 size_t plane_bytes(size_t elems) { return (elems * sizeof(float) + 255) / 256 * 256; }
 }  // namespace
 
+// 0 when the total would reach 2^62 bytes (sizes no device holds; the call
+// refuses them).
 size_t scan_bwd_bld_workspace_bytes(int batch, int dim, int seqlen, int dstate)
 {
-    return 7 * plane_bytes(size_t(batch) * size_t(dim) * size_t(seqlen)) +
-           4 * plane_bytes(size_t(batch) * size_t(dstate) * size_t(seqlen)) +
-           scan_bwd_workspace_bytes(batch, dim, seqlen, dstate);
+    const unsigned __int128 seq = (unsigned __int128)batch * unsigned(dim) * unsigned(seqlen);
+    const unsigned __int128 bc = (unsigned __int128)batch * unsigned(dstate) * unsigned(seqlen);
+    const unsigned __int128 lim = (unsigned __int128)1 << 62;
+    if (seq * 4 * 7 + bc * 4 * 4 >= lim) return 0;
+    const unsigned __int128 total = 7 * (unsigned __int128)plane_bytes(size_t(seq)) +
+                                    4 * (unsigned __int128)plane_bytes(size_t(bc)) +
+                                    scan_bwd_workspace_bytes(batch, dim, seqlen, dstate);
+    return total >= lim ? 0 : size_t(total);
 }
 
 hipError_t launch_scan_bwd_bld(const BwdBldArgs &a, hipStream_t stream)

@@ -873,6 +873,7 @@ ssm_status_t ssm_scan_bwd_bld(int batch, int dim, int seqlen, int dstate, ssm_dt
         !bld_span(lay.C_step, lay.C_batch, batch, seqlen, dstate, st[8], sb[8], sp[8]))
         return SSM_ERR_BAD_SHAPE;
     const size_t ws_need = ssm::scan_bwd_bld_workspace_bytes(batch, dim, seqlen, dstate);
+    if (!ws_need) return SSM_ERR_BAD_SHAPE;  // a workspace of 2^62 bytes or more
 
     const size_t in = dsize(in_dtype), gs = dsize(grad_dtype);
     for (const void *p : {x, dt, Bm, Cm, z})

@@ -626,6 +626,9 @@ def test_scan_bwd_bld_validation():
     need = L.ssm_scan_bwd_bld_workspace_bytes(2, 8, 40, 4)
     assert need >= 7 * 2560 + 4 * 1280 + L.ssm_scan_bwd_workspace_bytes(2, 8, 40, 4)
     assert L.ssm_scan_bwd_bld_workspace_bytes(2, 8, 40, 3) == 0
+    # 65535 x 2^30 x 4096 elements: within the product limit of the other
+    # entry points, but the transposed planes would take 2^62 bytes or more
+    assert L.ssm_scan_bwd_bld_workspace_bytes(65535, 1 << 30, 4096, 16) == 0
     seven = ctypes.c_longlong * 7
 
     def call(layout=None, flags=0, wsb=need, **over):
@@ -648,6 +651,10 @@ def test_scan_bwd_bld_validation():
     assert call(layout=(seven(), seven(), 0, 3, 0, 0)) == 2
     assert call(layout=(seven(), seven(), 0, 0, 0, 159)) == 2
     assert call(wsb=need - 1) == 7
+    assert L.ssm_scan_bwd_bld(65535, 1 << 30, 4096, 4, 1, 0, f["x"], f["dt"], None, f["A"], f["Bm"],
+                              f["Cm"], None, f["z"], None, 0, f["dy"], None, f["dx"], f["ddt"],
+                              f["dz"], f["dBm"], f["dCm"], f["dA"], None, None, None, f["ws"],
+                              1 << 62, None, None) == 2
     assert call(x=f["x"] + 1) == 4
     # dz as the second half of a [2, 40, 16] fp32 gradient buffer whose first
     # half is dx: interleaved halves of one buffer overlap by address range
