@@ -152,5 +152,14 @@ def test_bwd_max_seqlen():
     del inp
     for k in ("dx", "ddt", "dz"):
         assert rel_err(got[k][None], r[k][0]) <= TOL_F32, k
+    # dA, dDskip and ddt_bias are sums over the 2.7e8 steps, accumulated in
+    # fp32 (per lane over its chunks, a 16-lane butterfly, then one atomic add
+    # per segment in whatever order the 1024 segments finish).  They cancel:
+    # ddt_bias here is 18.84, 3e-6 of the sum of its terms' magnitudes (5.9e6).
+    # Summing the oracle's own per-step ddt, rounded to fp32, in that order
+    # gives 2.1e-5 to 6.4e-5 relative error over 20 segment orders (CPU), and
+    # the per-step fp32 errors of the kernel add to it; observed on the GPU up
+    # to 1.15e-4 for ddt_bias.  Gate: three times the fp32 bar for these sums.
     for k in ("dA", "dDskip", "ddt_bias"):
-        assert rel_err(np.atleast_1d(got[k])[None], np.atleast_1d(r[k][0])[None]) <= TOL_F32, k
+        e = rel_err(np.atleast_1d(got[k])[None], np.atleast_1d(r[k][0])[None])
+        assert e <= 3 * TOL_F32, (k, e)
